@@ -1,0 +1,159 @@
+"""Pins of the oracle's block decoders (CPU only).
+
+* hand-built blocks with hand-derived values (tests/golden/blocks.txt):
+  every field, nibble half, bit position and sign convention of each layout,
+  subnormal and zero scales, and the single fp32 rounding (ties to even) of
+  the Q4_K and A4G64 add/subtract;
+* round trips through the synthetic-data encoders, with the error bound each
+  encoder guarantees (a misplaced nibble or scale breaks the bound by orders
+  of magnitude);
+* structural invariants on random bytes.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from qmm_synth import quantize
+from tests.golden_io import read_blocks
+
+CASES = read_blocks()
+
+
+def test_golden_covers_every_format():
+    assert {c["fmt"] for c in CASES} == set(oracle.FORMATS)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_golden_block(case):
+    fmt = case["fmt"]
+    assert len(case["data"]) == oracle.block_bytes(fmt)
+    assert len(case["expect"]) == oracle.block_weights(fmt)
+    got = oracle.dequantize_blocks(fmt, np.frombuffer(case["data"], dtype=np.uint8))[0]
+    assert got.dtype == np.float32
+    for i, (g, e) in enumerate(zip(got.tolist(), case["expect"])):
+        # every expected value is an exact dyadic rational representable in fp32;
+        # compare by value so +0 == -0
+        assert Fraction(g) == e, f"{case['name']}: weight {i}: got {g}, expected {float(e)}"
+
+
+def test_block_geometry():
+    assert oracle.FORMATS == {
+        "q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210), "a4g64": (64, 36)}
+    assert oracle.row_bytes("q4_0", 512) == 288
+    assert oracle.row_bytes("q4_k", 2560) == 1440
+    assert oracle.row_bytes("q6_k", 9728) == 7980
+    assert oracle.row_bytes("a4g64", 1024) == 576
+    assert oracle.row_bytes("q8_0", 768) == 816
+    for fmt in oracle.FORMATS:
+        assert oracle.row_bytes(fmt, 0) == 0
+        assert oracle.row_bytes(fmt, oracle.block_weights(fmt) + 16) == 0
+
+
+def test_dequantize_matrix_row_order():
+    # Two rows with different scales: row r must start at byte r*row_bytes.
+    b0 = bytes.fromhex("003c" + "88" * 16)   # d=1, code 8 everywhere -> 0
+    b1 = bytes.fromhex("0040" + "99" * 16)   # d=2, code 9 everywhere -> 2
+    blob = np.frombuffer(b0 + b0 + b1 + b1, dtype=np.uint8)
+    w = oracle.dequantize("q4_0", blob, 2, 64)
+    assert w.shape == (2, 64)
+    assert np.all(w[0] == 0) and np.all(w[1] == 2)
+
+
+def _bound(fmt, blocks_u8, w_true, w_hat):
+    """Per-weight error bound the encoder guarantees (see qmm_synth.quantize)."""
+    bw, bb = oracle.FORMATS[fmt]
+    nb = blocks_u8.size // bb
+    blk = blocks_u8.reshape(nb, bb)
+    f16 = lambda off: (blk[:, off].astype(np.uint16) | (blk[:, off + 1].astype(np.uint16) << 8)).view(np.float16).astype(np.float64)
+    rel = 1 + 2.0 ** -20
+    if fmt == "q4_0":
+        d = np.abs(f16(0))[:, None]
+        qs = blk[:, 2:18]
+        q = np.concatenate([qs & 15, qs >> 4], axis=1)
+        return np.where(q == 15, d * (1 + 2.0 ** -7), d / 2 * rel)
+    if fmt == "q8_0":
+        return np.repeat(np.abs(f16(0))[:, None] / 2 * rel, 32, axis=1)
+    if fmt == "a4g64":
+        return np.repeat(f16(0)[:, None] / 2 * rel, 64, axis=1) + 2.0 ** -24 * np.abs(w_hat.reshape(nb, 64))
+    if fmt == "q4_k":
+        raw = blk[:, 4:16].astype(np.int64)
+        bits = sum(raw[:, i] << (8 * i) for i in range(12))
+        sc = np.stack([(bits >> (6 * j)) & 63 for j in range(8)], axis=1).astype(np.float64)
+        step = f16(0)[:, None] * sc
+        return np.repeat(step / 2 * rel, 32, axis=1) + 2.0 ** -24 * np.abs(w_hat.reshape(nb, 256))
+    if fmt == "q6_k":
+        sc = np.abs(blk[:, 2:18].view(np.int8).astype(np.float64))
+        return np.repeat(f16(0)[:, None] * sc / 2 * rel, 16, axis=1)
+    raise AssertionError(fmt)
+
+
+@pytest.mark.parametrize("fmt", list(oracle.FORMATS))
+@pytest.mark.parametrize("dist", ["normal", "uniform_pos", "all_negative", "spiky", "constant", "zeros"])
+def test_round_trip_bound(fmt, dist):
+    g = np.random.default_rng([7, list(oracle.FORMATS).index(fmt), len(dist)])
+    M, K = 6, 512
+    if dist == "normal":
+        w = g.normal(0, 0.02, (M, K))
+    elif dist == "uniform_pos":
+        w = g.uniform(0.001, 3.0, (M, K))
+    elif dist == "all_negative":
+        w = -g.uniform(0.5, 2.0, (M, K))
+    elif dist == "spiky":
+        w = g.normal(0, 1e-3, (M, K))
+        w[:, ::37] = 5.0
+    elif dist == "constant":
+        w = np.full((M, K), 0.3125)
+    else:
+        w = np.zeros((M, K))
+    w = w.astype(np.float32)
+    blob = quantize(fmt, w)
+    assert blob.size == M * oracle.row_bytes(fmt, K)
+    w_hat = oracle.dequantize(fmt, blob, M, K)
+    err = np.abs(w.astype(np.float64) - w_hat.astype(np.float64)).reshape(-1, oracle.block_weights(fmt))
+    bound = _bound(fmt, blob, w, w_hat)
+    assert np.all(err <= bound + 1e-30), f"max excess {np.max(err - bound)}"
+
+
+def test_q4_0_extreme_maps_to_code_zero():
+    # d = w*/-8 sends the largest-magnitude element to code 0 exactly (d*(0-8) = w*).
+    w = np.zeros((1, 32), np.float32)
+    w[0, 5] = -1.0
+    w[0, 7] = 0.5
+    blob = quantize("q4_0", w)
+    w_hat = oracle.dequantize("q4_0", blob, 1, 32)
+    assert w_hat[0, 5] == -1.0 and w_hat[0, 7] == 0.5
+
+
+def test_quantizer_deterministic():
+    w = np.random.default_rng(3).normal(0, 0.02, (8, 768)).astype(np.float32)
+    for fmt in ("q4_0", "q8_0", "q4_k", "q6_k", "a4g64"):
+        K = 768
+        assert np.array_equal(quantize(fmt, w[:, :K]), quantize(fmt, w[:, :K].copy()))
+
+
+@pytest.mark.parametrize("fmt", list(oracle.FORMATS))
+def test_random_bytes_structure(fmt):
+    """On arbitrary bytes the decoded weight divided by its block scale is an integer
+    of the format's code range (Q4_0, Q8_0, Q6_K), and results are finite."""
+    bw, bb = oracle.FORMATS[fmt]
+    g = np.random.default_rng([11, bb])
+    blk = g.integers(0, 256, size=(64, bb), dtype=np.uint8)
+    # keep fp16 scale fields finite and normal-sized
+    for off in {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2]}[fmt]:
+        blk[:, off + 1] &= 0x3B
+    w = oracle.dequantize_blocks(fmt, blk).astype(np.float64)
+    assert np.all(np.isfinite(w))
+    d = (blk[:, 0].astype(np.uint16) | (blk[:, 1].astype(np.uint16) << 8)).view(np.float16).astype(np.float64)[:, None]
+    nz = d[:, 0] != 0
+    if fmt == "q4_0":
+        r = w[nz] / d[nz]
+        assert np.all(r == np.round(r)) and r.min() >= -8 and r.max() <= 7
+    elif fmt == "q8_0":
+        r = w[nz] / d[nz]
+        assert np.all(r == np.round(r)) and r.min() >= -128 and r.max() <= 127
+    elif fmt == "q6_k":
+        r = w[nz] / d[nz]
+        assert np.all(r == np.round(r)) and np.abs(r).max() <= 4096
