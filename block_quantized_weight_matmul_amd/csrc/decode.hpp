@@ -1,0 +1,239 @@
+// decode.hpp -- per-format block decoders for gfx950 (device code).
+//
+// Every kernel of the library works on "units": 32 consecutive weights of one
+// row (K positions 32u .. 32u+31).  A unit is one Q4_0 or Q8_0 block, half an
+// A4G64 group, one 32-weight sub-block of a Q4_K super-block, or two 16-weight
+// sub-blocks of a Q6_K super-block.  Decoding a unit is three steps:
+//
+//   1. load   -- fetch the unit's bytes (scale fields and code bytes) from the
+//                block stream into registers.  Blocks of 18, 34 and 210 bytes
+//                are only 2-byte aligned, so those loaders read the enclosing
+//                aligned dwords and realign them with v_alignbit; they never
+//                read a dword past the one holding the unit's last byte.
+//   2. codes  -- the unit's 32 codes as four 32-bit words of 8 codes in bytes
+//                (byte b of word j is the code of weight 4j+b of the unit...
+//                see each format), each code already a non-negative integer.
+//   3. value  -- w = fma(code, a, b) in fp32.  For every format the two
+//                coefficients a and b are exact in fp32 and the product
+//                code*a is exact, so the single rounding of the fma gives the
+//                fp32 round-to-nearest-even of the formula's exact value.
+//
+// Formulas (the block formats the candle pull request "Metal: 64-token tile
+// for the quantized matrix-matrix kernel" lists in section "What changes",
+// plus the 4-bit affine groups of the tiny-llm pull request "perf: Optimize
+// quantized matmul for small decode batches"):
+//   Q4_0   w = d*(q-8)         -> fma(q, d, -8d)
+//   Q8_0   w = d*q, q signed   -> fma(q+128, d, -128d)
+//   Q4_K   w = d*sc*q - dmin*m -> fma(q, d*sc, -(dmin*m))
+//   Q6_K   w = d*sc*(q-32)     -> fma(q, d*sc, -32*d*sc)
+//   A4G64  w = scale*q + bias  -> fma(q, scale, bias)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+using u8 = uint8_t;
+using u16 = uint16_t;
+using u32 = uint32_t;
+using u64 = uint64_t;
+
+enum : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_A4G64 = 4 };
+
+template <int F> struct FmtInfo;
+template <> struct FmtInfo<FMT_Q4_0> { static constexpr int BW = 32, BB = 18; };
+template <> struct FmtInfo<FMT_Q8_0> { static constexpr int BW = 32, BB = 34; };
+template <> struct FmtInfo<FMT_Q4_K> { static constexpr int BW = 256, BB = 144; };
+template <> struct FmtInfo<FMT_Q6_K> { static constexpr int BW = 256, BB = 210; };
+template <> struct FmtInfo<FMT_A4G64> { static constexpr int BW = 64, BB = 36; };
+
+// fp16 bit pattern (low 16 bits) -> exact fp32 (subnormals included).
+__device__ __forceinline__ float h2f(u32 bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<u16>(bits & 0xFFFFu)));
+}
+
+// Byte b of v as a float (v_cvt_f32_ubyte{b}).
+__device__ __forceinline__ float byte_f(u32 v, int b) {
+  return static_cast<float>((v >> (8 * b)) & 0xFFu);
+}
+
+__device__ __forceinline__ u16 load_u16(const u8* p) {
+  return *reinterpret_cast<const u16*>(p);
+}
+
+// Bytes [off, off + NBYTES) of `base` (base 4-byte aligned, off 2-byte aligned) as
+// (NBYTES+3)/4 words, word j holding bytes off+4j .. off+4j+3 (little-endian).
+// Reads only dwords that contain at least one byte of the range.
+template <int NBYTES>
+__device__ __forceinline__ void load_bytes(const u8* base, u64 off, u32 (&w)[(NBYTES + 3) / 4]) {
+  constexpr int NW = (NBYTES + 3) / 4;
+  const u32* p = reinterpret_cast<const u32*>(base) + (off >> 2);
+  const u32 sh = static_cast<u32>(off & 3u) * 8u;
+  u32 raw[NW + 1];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) raw[i] = p[i];
+  // the (NW+1)-th dword is needed only when the range is not dword aligned
+  const u32 last = static_cast<u32>(((off + NBYTES - 1) >> 2) - (off >> 2));
+  raw[NW] = (last >= static_cast<u32>(NW)) ? p[NW] : 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
+}
+
+// A decoded unit: 32 codes in 8 words, and w_k = fma(code_k, a, b) where the
+// coefficient pair may change once, at weight 16 (Q6_K's two sub-blocks).
+struct Unit {
+  u32 c[8];      // code of weight 4j+b of the unit = byte b of c[j]
+  float a0, b0;  // coefficients for weights 0..15
+  float a1, b1;  // coefficients for weights 16..31
+};
+
+// ---------------------------------------------------------------------------------------------
+// Loaders: base = start of the (expert's) block stream (16-byte aligned),
+// row_off = byte offset of the row, u = unit index within the row.
+
+template <int F> struct Decoder;
+
+// Q4_0: block u; weight i (0..15) low nibble of qs[i], weight 16+i high nibble.
+template <> struct Decoder<FMT_Q4_0> {
+  struct Raw { u32 q[4]; u32 d; };
+  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
+    const u64 bo = row_off + 18ull * u;
+    load_bytes<16>(base, bo + 2, r.q);
+    r.d = load_u16(base + bo);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o.c[j] = r.q[j] & 0x0F0F0F0Fu;             // weights 4j .. 4j+3
+      o.c[4 + j] = (r.q[j] >> 4) & 0x0F0F0F0Fu;  // weights 16+4j .. 16+4j+3
+    }
+    const float d = h2f(r.d);
+    o.a0 = o.a1 = d;
+    o.b0 = o.b1 = -8.0f * d;
+  }
+};
+
+// Q8_0: block u; int8 codes, biased by 128 so they convert as unsigned bytes.
+template <> struct Decoder<FMT_Q8_0> {
+  struct Raw { u32 q[8]; u32 d; };
+  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
+    const u64 bo = row_off + 34ull * u;
+    load_bytes<32>(base, bo + 2, r.q);
+    r.d = load_u16(base + bo);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o.c[j] = r.q[j] ^ 0x80808080u;
+    const float d = h2f(r.d);
+    o.a0 = o.a1 = d;
+    o.b0 = o.b1 = -128.0f * d;
+  }
+};
+
+// Q4_K: super-block u/8, sub-block j = u%8: codes are the (j odd ? high : low)
+// nibbles of qs[32*(j/2) .. +31]; sc_j and m_j are 6-bit fields of the
+// 96-bit string at bits 6j and 48+6j.  Super-blocks are 144 = 9*16 bytes, so
+// with a 16-byte aligned base every super-block is 16-byte aligned.
+template <> struct Decoder<FMT_Q4_K> {
+  struct Raw { u32 h[4]; u32 q[8]; int j; };
+  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
+    const u64 so = row_off + 144ull * (u >> 3);
+    r.j = u & 7;
+    const uint4 h = *reinterpret_cast<const uint4*>(base + so);
+    const uint4* q = reinterpret_cast<const uint4*>(base + so + 16 + 32 * (r.j >> 1));
+    const uint4 q0 = q[0], q1 = q[1];
+    r.h[0] = h.x; r.h[1] = h.y; r.h[2] = h.z; r.h[3] = h.w;
+    r.q[0] = q0.x; r.q[1] = q0.y; r.q[2] = q0.z; r.q[3] = q0.w;
+    r.q[4] = q1.x; r.q[5] = q1.y; r.q[6] = q1.z; r.q[7] = q1.w;
+  }
+  __device__ __forceinline__ static u32 field6(const u32 (&h)[4], int bit) {
+    // bit string words: h[1] (bits 0..31), h[2] (32..63), h[3] (64..95)
+    const int wsel = bit >> 5;
+    const u32 lo = wsel == 0 ? h[1] : (wsel == 1 ? h[2] : h[3]);
+    const u32 hi = wsel == 0 ? h[2] : (wsel == 1 ? h[3] : 0u);
+    return __builtin_amdgcn_alignbit(hi, lo, static_cast<u32>(bit & 31)) & 63u;
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 sh = 4u * static_cast<u32>(r.j & 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.c[k] = (r.q[k] >> sh) & 0x0F0F0F0Fu;
+    const float d = h2f(r.h[0]);
+    const float dmin = h2f(r.h[0] >> 16);
+    const float sc = static_cast<float>(field6(r.h, 6 * r.j));
+    const float m = static_cast<float>(field6(r.h, 48 + 6 * r.j));
+    o.a0 = o.a1 = d * sc;         // exact: 11-bit significand x 6-bit integer
+    o.b0 = o.b1 = -(dmin * m);    // exact
+  }
+};
+
+// Q6_K: super-block u/8, a = u%8 covers weights 32a .. 32a+31 (sub-blocks 2a, 2a+1).
+// Low nibbles: ql[32*(a%4) + i], high nibble when a >= 4.  Top bits: bits
+// 2*(a/2) .. +1 of qh[32*(a%2) + i].
+template <> struct Decoder<FMT_Q6_K> {
+  struct Raw { u32 ql[8]; u32 qh[8]; u32 d; u32 sc; int a; };
+  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
+    const u64 so = row_off + 210ull * (u >> 3);
+    r.a = u & 7;
+    load_bytes<32>(base, so + 18 + 32 * (r.a & 3), r.ql);
+    load_bytes<32>(base, so + 146 + 32 * (r.a & 1), r.qh);
+    r.d = load_u16(base + so);
+    r.sc = load_u16(base + so + 2 + 2 * r.a);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 lsh = 4u * static_cast<u32>(r.a >> 2);
+    const u32 hsh = 2u * static_cast<u32>(r.a >> 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      o.c[k] = ((r.ql[k] >> lsh) & 0x0F0F0F0Fu) | (((r.qh[k] >> hsh) & 0x03030303u) << 4);
+    const float d = h2f(r.d);
+    const float s0 = static_cast<float>(static_cast<int8_t>(r.sc & 0xFFu));
+    const float s1 = static_cast<float>(static_cast<int8_t>((r.sc >> 8) & 0xFFu));
+    o.a0 = d * s0;                // exact: 11 + 7 significant bits
+    o.a1 = d * s1;
+    o.b0 = -32.0f * o.a0;         // exact (power of two)
+    o.b1 = -32.0f * o.a1;
+  }
+};
+
+// A4G64: group u/2, half h = u%2: codes are the (h ? high : low) nibbles of qs[0..31].
+// Groups are 36 bytes, so every group is 4-byte aligned.
+template <> struct Decoder<FMT_A4G64> {
+  struct Raw { u32 q[8]; u32 hdr; int h; };
+  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
+    const u64 go = row_off + 36ull * (u >> 1);
+    r.h = u & 1;
+    const u32* p = reinterpret_cast<const u32*>(base + go);
+    r.hdr = p[0];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.q[k] = p[1 + k];
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 sh = 4u * static_cast<u32>(r.h);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.c[k] = (r.q[k] >> sh) & 0x0F0F0F0Fu;
+    o.a0 = o.a1 = h2f(r.hdr);
+    o.b0 = o.b1 = h2f(r.hdr >> 16);
+  }
+};
+
+// Weight i (0..31) of an unpacked unit, in K order.
+//  Q4_0 / Q8_0 / Q4_K / Q6_K / A4G64 all place weight i at byte (i%4) of word
+//  (i/4) -- except Q4_0, whose words 0..3 hold weights 0..15 and words 4..7
+//  hold weights 16..31 in the same byte order, which is the same thing.
+__device__ __forceinline__ float unit_weight(const Unit& o, int i) {
+  const float q = byte_f(o.c[i >> 2], i & 3);
+  return i < 16 ? __builtin_fmaf(q, o.a0, o.b0) : __builtin_fmaf(q, o.a1, o.b1);
+}
+
+template <int F>
+__device__ __forceinline__ void decode_unit(const u8* base, u64 row_off, int u, float (&w)[32]) {
+  typename Decoder<F>::Raw r;
+  Decoder<F>::load(base, row_off, u, r);
+  Unit o;
+  Decoder<F>::unpack(r, o);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = unit_weight(o, i);
+}
+
+}  // namespace qmm

@@ -1,0 +1,29 @@
+// internal.hpp -- launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+struct MatDesc {
+  const uint8_t* blocks;  // device, 16-byte aligned
+  int fmt;                // FMT_*
+  int64_t n_experts, M, K;
+  uint64_t row_bytes;
+};
+
+// Largest expert count the expert-indexed path accepts (its presence bitmap
+// lives in LDS), and the largest token / slot counts of the matrix-vector paths.
+constexpr int64_t kMaxExperts = 8192;
+constexpr int64_t kMaxGemvTokens = 32;
+constexpr int64_t kMaxSlots = 64;
+
+hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f16, hipStream_t s);
+hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);
+hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
+                          const int32_t* ids, float* y, hipStream_t s);
+hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile,
+                       hipStream_t s);
+
+}  // namespace qmm

@@ -1,0 +1,187 @@
+/*
+ * qmm.h -- fused dequantize-and-multiply of block-quantized weights on MI355X (gfx950).
+ *
+ * y = x . W^T, where W (M rows x K) is stored as packed quantized blocks that the
+ * kernels decode themselves, x holds N activation tokens of K values, and y is
+ * N x M fp32.  This is the operation all three source pages optimise:
+ *   - candle pull request "Metal: 64-token tile for the quantized matrix-matrix
+ *     kernel" (sections "What changes" and "Why the tile sets the weight reuse"):
+ *     the matrix-matrix path over 32- or 64-token tiles, and the one-token
+ *     matrix-vector path;
+ *   - llama.cpp pull request "metal : fix idle threads in mul_mv_iq3_xxs for
+ *     ne00 < 1024" (sections "Overview" and "Additional information"): the
+ *     matrix-vector path at narrow K and its expert-indexed (MUL_MAT_ID) form;
+ *   - tiny-llm pull request "perf: Optimize quantized matmul for small decode
+ *     batches" (section "Summary"): the matrix-vector path at 1..16 tokens.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - Pointers named "device" must point to device memory of the current HIP
+ *    device; the library never dereferences them on the host.
+ *  - The library never allocates or frees device memory and never synchronises.
+ *    Every call that launches work is asynchronous on the given stream; a device
+ *    fault surfaces at the caller's next synchronisation.
+ *  - Argument checks happen before any launch.  On error nothing is launched,
+ *    the call returns a negative qmm_status, and qmm_last_error() holds a
+ *    thread-local description.  No C++ exception crosses this interface.
+ *  - Buffers passed in (blocks, x, ids) are borrowed: they must stay alive and
+ *    unmodified until the stream has passed the launched work.  y must not
+ *    alias x, ids or the blocks.
+ *  - A handle is immutable after qmm_create, so concurrent calls with one handle
+ *    on different streams are safe.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t *qmm_stream_t;
+
+/*
+ * Block formats (byte layouts are this library's; the pages print none).
+ * fp16 fields are little-endian IEEE binary16.  Row r of a matrix starts at byte
+ * r * qmm_row_bytes(type, K); expert e of a stacked tensor at e * M * row_bytes.
+ *
+ *  QMM_Q4_0   32 weights / 18 B: [0,2) d | [2,18) qs[16]; weight i = low nibble of
+ *             qs[i], weight i+16 = high nibble.  w = d * (q - 8).
+ *  QMM_Q8_0   32 weights / 34 B: [0,2) d | [2,34) int8 q[32].  w = d * q.
+ *  QMM_Q4_K   256 weights / 144 B: [0,2) d | [2,4) dmin | [4,16) 96-bit little-endian
+ *             string of sixteen 6-bit fields (field f at bit 6f: sc_0..sc_7, then
+ *             m_0..m_7) | [16,144) qs[128]: weight 64p+i = low nibble of qs[32p+i],
+ *             weight 64p+32+i = high nibble (p = 0..3, i = 0..31).
+ *             w = d * sc_j * q - dmin * m_j with j = weight / 32.
+ *  QMM_Q6_K   256 weights / 210 B: [0,2) d | [2,18) int8 sc[16] | [18,146) ql[128]:
+ *             weight i (< 128) low nibble of ql[i], weight i+128 high nibble |
+ *             [146,210) qh[64]: bits 2b..2b+1 of qh[i] are the top two bits of
+ *             weight i+64b.  q = low4 | high2 << 4.  w = d * sc_j * (q - 32), j = weight / 16.
+ *  QMM_A4G64  64 weights / 36 B: [0,2) scale | [2,4) bias | [4,36) qs[32]; weight i =
+ *             low nibble of qs[i], weight i+32 = high nibble.  w = scale * q + bias.
+ *
+ * Every product in these formulas is exact in fp32, so the dequantized weight is
+ * the fp32 round-to-nearest-even of the formula's exact value.
+ */
+typedef enum {
+  QMM_Q4_0 = 0,
+  QMM_Q8_0 = 1,
+  QMM_Q4_K = 2,
+  QMM_Q6_K = 3,
+  QMM_A4G64 = 4
+} qmm_type;
+
+/* Element type of activations (x) and of qmm_dequantize's output. */
+typedef enum { QMM_F32 = 0, QMM_F16 = 1 } qmm_dtype;
+
+/* Token tile of the matrix-matrix path (candle pull request, sections "What
+ * changes" and "Where the 64-token tile is used"): AUTO applies
+ * qmm_tile_for_tokens(N); 32 and 64 force a tile. */
+typedef enum { QMM_TILE_AUTO = 0, QMM_TILE_32 = 32, QMM_TILE_64 = 64 } qmm_tile;
+
+typedef int qmm_status;
+#define QMM_OK 0
+#define QMM_E_ARG (-1)    /* null pointer or invalid value */
+#define QMM_E_TYPE (-2)   /* unknown qmm_type or qmm_dtype */
+#define QMM_E_SHAPE (-3)  /* M, K, N, S or expert out of range */
+#define QMM_E_ALIGN (-4)  /* a pointer is not aligned as required */
+#define QMM_E_DEVICE (-5) /* no HIP device, or the current device is not gfx950 */
+#define QMM_E_HIP (-6)    /* a HIP runtime error (text in qmm_last_error) */
+
+typedef struct qmm_matrix qmm_matrix;
+
+/*
+ * qmm_create -- describe a quantized weight tensor.
+ *   out        receives the handle (host memory owned by the library; free it with
+ *              qmm_destroy).
+ *   type       block format.
+ *   blocks     DEVICE pointer, 16-byte aligned, holding n_experts * M * row_bytes(K)
+ *              bytes in the layout above.  Borrowed, not copied: it must outlive
+ *              the handle and stay unmodified.
+ *   n_experts  1 for a plain matrix; E for the stacked experts of qmm_gemm_id.
+ *   M, K       rows and reduction length; K a positive multiple of the block's
+ *              weight count (32, 32, 256, 256, 64); M >= 1.
+ * Checks that the current device is gfx950 (QMM_E_DEVICE otherwise) and records it.
+ */
+qmm_status qmm_create(qmm_matrix **out, qmm_type type, const void *blocks,
+                      int64_t n_experts, int64_t M, int64_t K);
+
+/* qmm_destroy -- free a handle's host metadata.  NULL is accepted. */
+qmm_status qmm_destroy(qmm_matrix *h);
+
+/*
+ * qmm_gemv -- matrix-vector path for 1..32 tokens (llama.cpp and tiny-llm pull
+ * requests above): y[t, r] = sum_k x[t, k] * w[r, k], fp32 accumulation.
+ *   h   a handle with n_experts == 1.
+ *   x   DEVICE, [N, K] contiguous, element type xt (fp32 or fp16), 16-byte aligned.
+ *   N   0..32; 0 launches nothing and returns QMM_OK; above 32 -> QMM_E_SHAPE.
+ *   y   DEVICE, [N, M] contiguous fp32, 4-byte aligned; every element is written.
+ * Lanes of each 64-wide wavefront are spread over (row, 32-weight chunk) pairs so
+ * none idles at narrow K, and the token count picks a kernel instance that gives
+ * no register to absent tokens.
+ */
+qmm_status qmm_gemv(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
+                    float *y, qmm_stream_t stream);
+
+/*
+ * qmm_gemm -- matrix-matrix path for any N (candle pull request above).  Each
+ * workgroup dequantizes a tile of weight rows once per K step into LDS as fp16
+ * (round to nearest even of the fp32 weight) and multiplies it on the matrix
+ * cores, with fp32 accumulation, by a tile of 32 or 64 tokens.
+ *   x     DEVICE, [N, K] contiguous fp32 or fp16, 16-byte aligned; fp32 values are
+ *         rounded to fp16 (nearest even) when staged.
+ *   N     >= 0; a batch of sequences is passed flattened (N = batch * tokens).
+ *   y     DEVICE, [N, M] fp32, 4-byte aligned.
+ *   tile  QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64.  Results are bit-identical
+ *         for either tile: every output is accumulated in the same order.
+ */
+qmm_status qmm_gemm(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
+                    float *y, qmm_tile tile, qmm_stream_t stream);
+
+/*
+ * qmm_gemm_id -- expert-indexed matrix-vector path (MUL_MAT_ID in the llama.cpp
+ * pull request above): y[t, s, r] = sum_k x_ts[k] * w_{ids[t, s]}[r, k].
+ *   h           handle with n_experts = E >= 1 (experts stacked in `blocks`).
+ *   x           DEVICE, fp32 or fp16, 16-byte aligned.  x_per_slot = 1: [N, S, K],
+ *               slot (t, s) reads row t*S + s.  x_per_slot = 0: [N, K], every slot
+ *               of token t reads row t.
+ *   N           0..32 tokens (0: no launch); S 1..64 slots per token.
+ *   ids         DEVICE int32 [N, S], 4-byte aligned.  Duplicate ids are computed
+ *               independently; an id outside [0, E) makes its output row all NaN.
+ *   y           DEVICE fp32 [N, S, M].
+ * The (token, slot) pairs are grouped by expert on the device, so each active
+ * expert's blocks are streamed once per call; no host synchronisation.
+ */
+qmm_status qmm_gemm_id(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
+                       int64_t S, int x_per_slot, const int32_t *ids, float *y,
+                       qmm_stream_t stream);
+
+/*
+ * qmm_dequantize -- decode one expert's matrix (expert 0 for a plain matrix).
+ *   out  DEVICE [M, K] of type ot, 16-byte aligned.  QMM_F32: the exact dequantized
+ *        weights.  QMM_F16: the fp16 values the matrix-matrix path stages in LDS.
+ */
+qmm_status qmm_dequantize(const qmm_matrix *h, int64_t expert, void *out, qmm_dtype ot,
+                          qmm_stream_t stream);
+
+/* qmm_tile_for_tokens -- 64 when a 64-token tile pads no more tokens than a
+ * 32-token tile, else 32 (candle pull request, section "Where the 64-token tile
+ * is used").  Host-only and pure; N < 0 returns 0. */
+int qmm_tile_for_tokens(int64_t N);
+
+/* Helpers.  qmm_row_bytes returns 0 for an unknown type or a K that is not a
+ * positive multiple of the block; the block queries return 0 for an unknown type. */
+size_t qmm_row_bytes(qmm_type type, int64_t K);
+int qmm_block_weights(qmm_type type);
+int qmm_block_bytes(qmm_type type);
+const char *qmm_status_string(qmm_status s);
+const char *qmm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

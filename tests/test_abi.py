@@ -1,0 +1,99 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every function
+include/qmm.h declares, and its host-only functions and argument checks behave
+as documented.  No call here launches device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def _lib():
+    from block_quantized_weight_matmul_amd import _lib as L
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_id",
+                     "qmm_dequantize", "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    assert os.path.exists(L.LIB_PATH)
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in qmm.h but not exported"
+
+
+def test_tile_rule_matches_oracle():
+    L = _lib()
+    for n in list(range(0, 3000)) + [2 ** 20, 2 ** 24 + 7]:
+        assert L.lib.qmm_tile_for_tokens(n) == oracle.tile_for_tokens(n), n
+    assert L.lib.qmm_tile_for_tokens(-1) == 0
+
+
+def test_row_bytes_and_blocks():
+    L = _lib()
+    for name, t in L.TYPES.items():
+        bw, bb = oracle.FORMATS[name]
+        assert L.lib.qmm_block_weights(t) == bw
+        assert L.lib.qmm_block_bytes(t) == bb
+        for K in (bw, 2 * bw, 768 if 768 % bw == 0 else bw * 3, 9728 if 9728 % bw == 0 else bw * 38):
+            assert L.lib.qmm_row_bytes(t, K) == oracle.row_bytes(name, K)
+        assert L.lib.qmm_row_bytes(t, bw + 16) == 0
+        assert L.lib.qmm_row_bytes(t, 0) == 0
+        assert L.lib.qmm_row_bytes(t, -bw) == 0
+    assert L.lib.qmm_row_bytes(7, 256) == 0
+    assert L.lib.qmm_block_weights(-1) == 0
+
+
+def test_status_strings():
+    L = _lib()
+    for code, name in L.STATUS.items():
+        assert L.lib.qmm_status_string(code).decode() == name
+
+
+def test_argument_errors_before_device():
+    """Checks that fail before the library looks for a device."""
+    L = _lib()
+    lib = L.lib
+    h = ctypes.c_void_p()
+    buf = ctypes.create_string_buffer(4096 + 32)
+    base = (ctypes.addressof(buf) + 15) & ~15
+    assert lib.qmm_create(None, 0, ctypes.c_void_p(base), 1, 4, 32) == -1
+    assert lib.qmm_create(ctypes.byref(h), 9, ctypes.c_void_p(base), 1, 4, 32) == -2
+    assert lib.qmm_create(ctypes.byref(h), 0, None, 1, 4, 32) == -1
+    assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base + 2), 1, 4, 32) == -4
+    assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base), 1, 4, 48) == -3
+    assert lib.qmm_create(ctypes.byref(h), 2, ctypes.c_void_p(base), 1, 4, 128) == -3
+    assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base), 0, 4, 32) == -3
+    assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base), 1, 0, 32) == -3
+    assert "16-byte" in lib.qmm_last_error().decode() or lib.qmm_last_error()
+    assert lib.qmm_gemv(None, ctypes.c_void_p(base), 0, 1, ctypes.c_void_p(base), None) == -1
+    assert lib.qmm_gemm(None, ctypes.c_void_p(base), 0, 1, ctypes.c_void_p(base), 0, None) == -1
+    assert lib.qmm_gemm_id(None, ctypes.c_void_p(base), 0, 1, 1, 1, ctypes.c_void_p(base),
+                           ctypes.c_void_p(base), None) == -1
+    assert lib.qmm_dequantize(None, 0, ctypes.c_void_p(base), 0, None) == -1
+    assert lib.qmm_destroy(None) == 0
+
+
+def test_binding_refuses_bad_type_name():
+    import block_quantized_weight_matmul_amd as q
+    with pytest.raises(ValueError):
+        q.qmm_row_bytes("q5_1", 256)
+    assert q.qmm_row_bytes("q6_k", 256) == 210

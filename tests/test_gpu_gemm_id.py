@@ -1,0 +1,113 @@
+"""Expert-indexed matrix-vector path (qmm_gemm_id, MUL_MAT_ID in the llama.cpp pull
+request "metal : fix idle threads in mul_mv_iq3_xxs for ne00 < 1024") against
+the oracle: tolerance 1e-5 * S, exact equality with the dense path when every
+slot picks one expert, NaN rows for ids outside [0, E)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_matmul_amd as q
+from tests.gpu_helpers import FORMATS, assert_within, count_differences, make_matrix, oracle, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _stack(fmt, E, M, K, seed):
+    blob = np.concatenate([make_matrix(fmt, M, K, [seed, e]) for e in range(E)])
+    rb = oracle.row_bytes(fmt, K)
+    ws = [oracle.dequantize(fmt, blob[e * M * rb:(e + 1) * M * rb], M, K) for e in range(E)]
+    return blob, ws
+
+
+def _ids(g, N, S, E):
+    return np.stack([g.choice(E, S, replace=False) for _ in range(N)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("N,S", [(1, 1), (2, 4), (5, 8), (12, 8), (24, 8), (32, 2)])
+def test_gemm_id_per_slot(fmt, N, S):
+    E, M = 10, 96
+    K = 512 if 512 % oracle.block_weights(fmt) == 0 else 2 * oracle.block_weights(fmt)
+    blob, ws = _stack(fmt, E, M, K, 61)
+    g = np.random.default_rng([62, N, S])
+    ids = _ids(g, N, S, E)
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL,
+                  f"gemm_id {fmt} N={N} S={S}")
+
+
+@pytest.mark.parametrize("xdtype", [np.float32, np.float16])
+def test_gemm_id_shared_x(xdtype):
+    fmt, E, M, K, N, S = "q4_0", 16, 130, 512, 7, 4
+    blob, ws = _stack(fmt, E, M, K, 63)
+    g = np.random.default_rng(63)
+    ids = _ids(g, N, S, E)
+    x = g.standard_normal((N, K)).astype(np.float32).astype(xdtype)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL,
+                  "gemm_id shared x")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_id_equals_dense_for_one_expert(fmt):
+    """Every slot routed to expert e: identical bits to the dense path on expert e."""
+    E, M, N, S = 4, 70, 3, 2
+    K = 1024 if 1024 % oracle.block_weights(fmt) == 0 else 4 * oracle.block_weights(fmt)
+    blob, ws = _stack(fmt, E, M, K, 64)
+    rb = oracle.row_bytes(fmt, K)
+    g = np.random.default_rng(64)
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qs = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    for e in range(E):
+        ids = np.full((N, S), e, np.int32)
+        y = to_host(qs.gemm_id(to_dev(x), to_dev(ids)))
+        dense = q.QMatrix(to_dev(blob[e * M * rb:(e + 1) * M * rb]), fmt, M, K)
+        yd = to_host(dense.gemv(to_dev(x.reshape(N * S, K)))).reshape(N, S, M)
+        assert count_differences(y, yd) == 0, f"{fmt} expert {e}"
+
+
+def test_gemm_id_invalid_ids_give_nan_rows():
+    fmt, E, M, K, N, S = "q8_0", 6, 100, 256, 4, 3
+    blob, ws = _stack(fmt, E, M, K, 65)
+    g = np.random.default_rng(65)
+    ids = _ids(g, N, S, E)
+    ids[0, 1] = -1
+    ids[2, 0] = E
+    ids[3, 2] = 1 << 30
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    ref = oracle.matmul_id_ref(x, ids, ws)
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(np.isnan(y[bad]))
+    assert_within(y[~bad], ref[~bad], oracle.tolerance_scale_id(x, ids, ws)[~bad], TOL, "valid rows")
+
+
+def test_gemm_id_duplicate_ids_many_pairs():
+    """Duplicate ids within tokens: 32 tokens x 8 slots all on 2 experts (128 pairs
+    per expert, several passes of the token bucket)."""
+    fmt, E, M, K, N, S = "a4g64", 3, 64, 512, 32, 8
+    blob, ws = _stack(fmt, E, M, K, 66)
+    g = np.random.default_rng(66)
+    ids = g.integers(1, 3, size=(N, S)).astype(np.int32)
+    x = g.standard_normal((N, S, K)).astype(np.float16)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL, "dups")
+
+
+def test_gemm_id_zero_tokens_is_noop():
+    fmt, E, M, K = "q4_0", 2, 32, 64
+    blob, _ = _stack(fmt, E, M, K, 67)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    ids = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    x = torch.zeros((1, 1, K), device="cuda")
+    y = torch.full((1, 1, M), 5.0, device="cuda")
+    q.qmm_gemm_id(qm.handle, x, 0, 1, 1, ids, y)
+    assert np.all(to_host(y) == 5.0)

@@ -1,0 +1,95 @@
+"""Matrix-vector path (qmm_gemv) against the oracle.
+
+Tolerance: |y - y_ref| <= 1e-5 * S with S = sum_k |x w| (fp32 accumulation of
+exact fp32 weights; each lane sums 32 products in a fresh chain, partial sums
+then add up over at most K/32 chunks and a log2(64)-step butterfly, so the
+worst-case bound is (32 + K/32/lanes + 6) * 2^-24 * S, below 1e-5 * S for every
+K here).  One-hot activations must reproduce the dequantized weights exactly."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_matmul_amd as q
+from tests.gpu_helpers import FORMATS, assert_within, make_matrix, oracle, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _run(fmt, M, K, N, xdtype, seed):
+    blob = make_matrix(fmt, M, K, seed)
+    w = oracle.dequantize(fmt, blob, M, K)
+    g = np.random.default_rng([seed, 1] if isinstance(seed, int) else list(seed) + [1])
+    x = g.standard_normal((N, K)).astype(np.float32).astype(xdtype)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    y = to_host(qm.gemv(to_dev(x)))
+    return assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
+                         f"gemv {fmt} M={M} K={K} N={N} {np.dtype(xdtype).name}")
+
+
+def _ks(fmt):
+    bw = oracle.block_weights(fmt)
+    return sorted({k for k in (bw, 256, 512, 768, 1024, 2560) if k % bw == 0})
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8, 11, 16, 24, 32])
+def test_gemv_tokens(fmt, N):
+    for K in _ks(fmt):
+        _run(fmt, 67, K, N, np.float32, [41, N, K])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("M", [1, 5, 64, 257])
+def test_gemv_rows_fp16(fmt, M):
+    for K in _ks(fmt):
+        _run(fmt, M, K, 3, np.float16, [42, M, K])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemv_narrow_k_rows(fmt):
+    """The matrix-vector shapes of the llama.cpp review thread: m = 4096 at k = 512,
+    768, 1024 (one token)."""
+    for K in (512, 768, 1024):
+        if K % oracle.block_weights(fmt) == 0:
+            _run(fmt, 4096, K, 1, np.float32, [43, K])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemv_one_hot_is_exact(fmt):
+    """x = e_k per token: each output must equal w[:, k] exactly, which also proves
+    every (row, chunk) pair is computed once: a chunk done twice would give 2w,
+    a skipped one 0."""
+    bw = oracle.block_weights(fmt)
+    K = 1024 if 1024 % bw == 0 else 4 * bw
+    M = 133
+    blob = make_matrix(fmt, M, K, [44])
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    ks = list(range(0, K, K // 32))[:32]
+    ks[-1] = K - 1
+    x = np.zeros((len(ks), K), np.float32)
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0
+    y = to_host(qm.gemv(to_dev(x)))
+    for t, k in enumerate(ks):
+        assert np.array_equal(y[t], w[:, k]), f"{fmt}: token {t} (k={k})"
+
+
+def test_gemv_zero_tokens_is_noop():
+    fmt, M, K = "q4_0", 32, 64
+    qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [45])), fmt, M, K)
+    x = torch.zeros((1, K), device="cuda")
+    y = torch.full((1, M), 7.0, device="cuda")
+    q.qmm_gemv(qm.handle, x, 0, y)
+    assert np.all(to_host(y) == 7.0)
+
+
+def test_gemv_deterministic():
+    fmt, M, K = "q6_k", 300, 2560
+    qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [46])), fmt, M, K)
+    x = to_dev(np.random.default_rng(46).standard_normal((5, K)).astype(np.float32))
+    a, b = to_host(qm.gemv(x)), to_host(qm.gemv(x))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
