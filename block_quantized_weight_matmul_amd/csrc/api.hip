@@ -116,6 +116,8 @@ qmm_status qmm_create(qmm_matrix** out, qmm_type type, const void* blocks, int64
   if (rb == 0 || K > INT_MAX / 2)
     return fail(QMM_E_SHAPE, "K=%lld is not a positive multiple of %d (or too large)",
                 static_cast<long long>(K), kBW[type]);
+  if (static_cast<double>(M) * static_cast<double>(rb) >= 4294967296.0)
+    return fail(QMM_E_SHAPE, "one matrix (M * row bytes) must be below 4 GiB");
   if (static_cast<double>(n_experts) * static_cast<double>(M) * static_cast<double>(rb) > 9.0e18)
     return fail(QMM_E_SHAPE, "tensor too large");
   int dev = -1;

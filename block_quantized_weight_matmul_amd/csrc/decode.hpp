@@ -23,7 +23,7 @@
 // plus the 4-bit affine groups of the tiny-llm pull request "perf: Optimize
 // quantized matmul for small decode batches"):
 //   Q4_0   w = d*(q-8)         -> fma(q, d, -8d)
-//   Q8_0   w = d*q, q signed   -> fma(q+128, d, -128d)
+//   Q8_0   w = d*q, q signed   -> fma(q, d, 0) (code stored as q+128, bias removed exactly)
 //   Q4_K   w = d*sc*q - dmin*m -> fma(q, d*sc, -(dmin*m))
 //   Q6_K   w = d*sc*(q-32)     -> fma(q, d*sc, -32*d*sc)
 //   A4G64  w = scale*q + bias  -> fma(q, scale, bias)
@@ -62,19 +62,21 @@ __device__ __forceinline__ u16 load_u16(const u8* p) {
   return *reinterpret_cast<const u16*>(p);
 }
 
-// Bytes [off, off + NBYTES) of `base` (base 4-byte aligned, off 2-byte aligned) as
-// (NBYTES+3)/4 words, word j holding bytes off+4j .. off+4j+3 (little-endian).
-// Reads only dwords that contain at least one byte of the range.
+// The NBYTES bytes at `src` (any alignment) as (NBYTES+3)/4 little-endian words,
+// word j holding bytes src[4j .. 4j+3]: the enclosing dword-aligned words are
+// loaded and realigned with v_alignbit.  Reads only dwords that contain at least
+// one byte of the range, so it never touches memory past the range's last dword.
 template <int NBYTES>
-__device__ __forceinline__ void load_bytes(const u8* base, u64 off, u32 (&w)[(NBYTES + 3) / 4]) {
+__device__ __forceinline__ void load_bytes(const u8* src, u32 (&w)[(NBYTES + 3) / 4]) {
   constexpr int NW = (NBYTES + 3) / 4;
-  const u32* p = reinterpret_cast<const u32*>(base) + (off >> 2);
-  const u32 sh = static_cast<u32>(off & 3u) * 8u;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+  const u32* p = reinterpret_cast<const u32*>(a & ~static_cast<uintptr_t>(3));
+  const u32 sh = static_cast<u32>(a & 3u) * 8u;
   u32 raw[NW + 1];
 #pragma unroll
   for (int i = 0; i < NW; ++i) raw[i] = p[i];
   // the (NW+1)-th dword is needed only when the range is not dword aligned
-  const u32 last = static_cast<u32>(((off + NBYTES - 1) >> 2) - (off >> 2));
+  const u32 last = static_cast<u32>(((a + NBYTES - 1) >> 2) - (a >> 2));
   raw[NW] = (last >= static_cast<u32>(NW)) ? p[NW] : 0u;
 #pragma unroll
   for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
@@ -88,18 +90,30 @@ struct Unit {
   float a1, b1;  // coefficients for weights 16..31
 };
 
+// Hides a value from the optimiser (emits nothing), so that byte extraction of a
+// masked word is done with v_cvt_f32_ubyte{0..3} on the word rather than
+// re-deriving each byte with a bit-field extract.
+__device__ __forceinline__ u32 opaque(u32 v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
 // ---------------------------------------------------------------------------------------------
-// Loaders: base = start of the (expert's) block stream (16-byte aligned),
-// row_off = byte offset of the row, u = unit index within the row.
+// Loaders: base = start of a matrix (or of one expert's matrix), row_off = byte
+// offset of the row from base (32 bits: a matrix is below 4 GiB), u = unit index
+// within the row.  Q4_K and A4G64 read whole dwords directly: their blocks are
+// 144 and 36 bytes, so with a 16-byte aligned tensor every super-block (group)
+// of every expert is 16 (4) byte aligned.  The other formats realign.
 
 template <int F> struct Decoder;
 
 // Q4_0: block u; weight i (0..15) low nibble of qs[i], weight 16+i high nibble.
 template <> struct Decoder<FMT_Q4_0> {
+  static constexpr float kCodeBias = 0.0f;
   struct Raw { u32 q[4]; u32 d; };
-  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
-    const u64 bo = row_off + 18ull * u;
-    load_bytes<16>(base, bo + 2, r.q);
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 bo = row_off + 18u * u;
+    load_bytes<16>(base + bo + 2, r.q);
     r.d = load_u16(base + bo);
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
@@ -116,10 +130,11 @@ template <> struct Decoder<FMT_Q4_0> {
 
 // Q8_0: block u; int8 codes, biased by 128 so they convert as unsigned bytes.
 template <> struct Decoder<FMT_Q8_0> {
+  static constexpr float kCodeBias = 128.0f;  // code - 128 is the signed q
   struct Raw { u32 q[8]; u32 d; };
-  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
-    const u64 bo = row_off + 34ull * u;
-    load_bytes<32>(base, bo + 2, r.q);
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 bo = row_off + 34u * u;
+    load_bytes<32>(base + bo + 2, r.q);
     r.d = load_u16(base + bo);
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
@@ -127,7 +142,7 @@ template <> struct Decoder<FMT_Q8_0> {
     for (int j = 0; j < 8; ++j) o.c[j] = r.q[j] ^ 0x80808080u;
     const float d = h2f(r.d);
     o.a0 = o.a1 = d;
-    o.b0 = o.b1 = -128.0f * d;
+    o.b0 = o.b1 = 0.0f;
   }
 };
 
@@ -136,23 +151,32 @@ template <> struct Decoder<FMT_Q8_0> {
 // 96-bit string at bits 6j and 48+6j.  Super-blocks are 144 = 9*16 bytes, so
 // with a 16-byte aligned base every super-block is 16-byte aligned.
 template <> struct Decoder<FMT_Q4_K> {
+  static constexpr float kCodeBias = 0.0f;
   struct Raw { u32 h[4]; u32 q[8]; int j; };
-  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
-    const u64 so = row_off + 144ull * (u >> 3);
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 so = row_off + 144u * (u >> 3);
     r.j = u & 7;
-    const uint4 h = *reinterpret_cast<const uint4*>(base + so);
-    const uint4* q = reinterpret_cast<const uint4*>(base + so + 16 + 32 * (r.j >> 1));
-    const uint4 q0 = q[0], q1 = q[1];
-    r.h[0] = h.x; r.h[1] = h.y; r.h[2] = h.z; r.h[3] = h.w;
-    r.q[0] = q0.x; r.q[1] = q0.y; r.q[2] = q0.z; r.q[3] = q0.w;
-    r.q[4] = q1.x; r.q[5] = q1.y; r.q[6] = q1.z; r.q[7] = q1.w;
+    const u32* h = reinterpret_cast<const u32*>(base + so);
+    const u32* q = reinterpret_cast<const u32*>(base + so + 16 + 32 * (r.j >> 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.h[k] = h[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.q[k] = q[k];
   }
-  __device__ __forceinline__ static u32 field6(const u32 (&h)[4], int bit) {
-    // bit string words: h[1] (bits 0..31), h[2] (32..63), h[3] (64..95)
-    const int wsel = bit >> 5;
-    const u32 lo = wsel == 0 ? h[1] : (wsel == 1 ? h[2] : h[3]);
-    const u32 hi = wsel == 0 ? h[2] : (wsel == 1 ? h[3] : 0u);
-    return __builtin_amdgcn_alignbit(hi, lo, static_cast<u32>(bit & 31)) & 63u;
+  // sc_j = bits [6j, 6j+6) and m_j = bits [48+6j, 54+6j) of the 96-bit string in
+  // h[1] (bits 0..31), h[2] (32..63), h[3] (64..95): funnel-shift the pair of
+  // words holding the field (selected as values, so nothing is indexed).
+  __device__ __forceinline__ static u32 field_sc(const Raw& r) {
+    const u32 b = 6u * static_cast<u32>(r.j);  // 0..42
+    const u32 lo = b < 32 ? r.h[1] : r.h[2];
+    const u32 hi = b < 32 ? r.h[2] : r.h[3];
+    return __builtin_amdgcn_alignbit(hi, lo, b & 31u) & 63u;
+  }
+  __device__ __forceinline__ static u32 field_m(const Raw& r) {
+    const u32 b = 48u + 6u * static_cast<u32>(r.j);  // 48..90
+    const u32 lo = b < 64 ? r.h[2] : r.h[3];
+    const u32 hi = b < 64 ? r.h[3] : 0u;
+    return __builtin_amdgcn_alignbit(hi, lo, b & 31u) & 63u;
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
     const u32 sh = 4u * static_cast<u32>(r.j & 1);
@@ -160,8 +184,8 @@ template <> struct Decoder<FMT_Q4_K> {
     for (int k = 0; k < 8; ++k) o.c[k] = (r.q[k] >> sh) & 0x0F0F0F0Fu;
     const float d = h2f(r.h[0]);
     const float dmin = h2f(r.h[0] >> 16);
-    const float sc = static_cast<float>(field6(r.h, 6 * r.j));
-    const float m = static_cast<float>(field6(r.h, 48 + 6 * r.j));
+    const float sc = static_cast<float>(field_sc(r));
+    const float m = static_cast<float>(field_m(r));
     o.a0 = o.a1 = d * sc;         // exact: 11-bit significand x 6-bit integer
     o.b0 = o.b1 = -(dmin * m);    // exact
   }
@@ -171,12 +195,13 @@ template <> struct Decoder<FMT_Q4_K> {
 // Low nibbles: ql[32*(a%4) + i], high nibble when a >= 4.  Top bits: bits
 // 2*(a/2) .. +1 of qh[32*(a%2) + i].
 template <> struct Decoder<FMT_Q6_K> {
+  static constexpr float kCodeBias = 0.0f;
   struct Raw { u32 ql[8]; u32 qh[8]; u32 d; u32 sc; int a; };
-  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
-    const u64 so = row_off + 210ull * (u >> 3);
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 so = row_off + 210u * (u >> 3);
     r.a = u & 7;
-    load_bytes<32>(base, so + 18 + 32 * (r.a & 3), r.ql);
-    load_bytes<32>(base, so + 146 + 32 * (r.a & 1), r.qh);
+    load_bytes<32>(base + so + 18 + 32 * (r.a & 3), r.ql);
+    load_bytes<32>(base + so + 146 + 32 * (r.a & 1), r.qh);
     r.d = load_u16(base + so);
     r.sc = load_u16(base + so + 2 + 2 * r.a);
   }
@@ -199,9 +224,10 @@ template <> struct Decoder<FMT_Q6_K> {
 // A4G64: group u/2, half h = u%2: codes are the (h ? high : low) nibbles of qs[0..31].
 // Groups are 36 bytes, so every group is 4-byte aligned.
 template <> struct Decoder<FMT_A4G64> {
+  static constexpr float kCodeBias = 0.0f;
   struct Raw { u32 q[8]; u32 hdr; int h; };
-  __device__ __forceinline__ static void load(const u8* base, u64 row_off, int u, Raw& r) {
-    const u64 go = row_off + 36ull * (u >> 1);
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 go = row_off + 36u * (u >> 1);
     r.h = u & 1;
     const u32* p = reinterpret_cast<const u32*>(base + go);
     r.hdr = p[0];
@@ -217,23 +243,35 @@ template <> struct Decoder<FMT_A4G64> {
   }
 };
 
-// Weight i (0..31) of an unpacked unit, in K order.
-//  Q4_0 / Q8_0 / Q4_K / Q6_K / A4G64 all place weight i at byte (i%4) of word
-//  (i/4) -- except Q4_0, whose words 0..3 hold weights 0..15 and words 4..7
-//  hold weights 16..31 in the same byte order, which is the same thing.
-__device__ __forceinline__ float unit_weight(const Unit& o, int i) {
-  const float q = byte_f(o.c[i >> 2], i & 3);
-  return i < 16 ? __builtin_fmaf(q, o.a0, o.b0) : __builtin_fmaf(q, o.a1, o.b1);
+// The 32 codes of an unpacked unit as floats, in K order (weight i sits in byte
+// i%4 of word i/4), with the format's code bias removed (exact: small integers).
+template <int F>
+__device__ __forceinline__ void unit_codes(const Unit& o, float (&q)[32]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const u32 m = opaque(o.c[k]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) q[4 * k + b] = byte_f(m, b) - Decoder<F>::kCodeBias;
+  }
+}
+
+// The unit's 32 dequantized weights: w = fma(q, a, b), one rounding of an exact
+// product and an exact addend, i.e. the fp32 rounding of the formula's value.
+template <int F>
+__device__ __forceinline__ void unit_weights(const Unit& o, float (&w)[32]) {
+  float q[32];
+  unit_codes<F>(o, q);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i] = i < 16 ? __builtin_fmaf(q[i], o.a0, o.b0) : __builtin_fmaf(q[i], o.a1, o.b1);
 }
 
 template <int F>
-__device__ __forceinline__ void decode_unit(const u8* base, u64 row_off, int u, float (&w)[32]) {
+__device__ __forceinline__ void decode_unit(const u8* base, u32 row_off, int u, float (&w)[32]) {
   typename Decoder<F>::Raw r;
   Decoder<F>::load(base, row_off, u, r);
   Unit o;
   Decoder<F>::unpack(r, o);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) w[i] = unit_weight(o, i);
+  unit_weights<F>(o, w);
 }
 
 }  // namespace qmm

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void k_dequant(const u8* W, u64 rb, int M, int
   const int row = static_cast<int>(idx / nU);
   const int u = static_cast<int>(idx % nU);
   float w[32];
-  decode_unit<F>(W, (u64)row * rb, u, w);
+  decode_unit<F>(W, static_cast<u32>(row) * static_cast<u32>(rb), u, w);
   const u64 base = (u64)row * nU * 32 + 32ull * u;
   if (out_f16) {
     half8* p = reinterpret_cast<half8*>(reinterpret_cast<_Float16*>(out) + base);

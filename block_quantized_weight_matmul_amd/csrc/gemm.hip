@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
       half8* dst = reinterpret_cast<half8*>(&sW[r][32 * uu]);
       if (row < a.M && u < a.nU) {
         float w[32];
-        decode_unit<F>(a.W, (u64)row * a.row_bytes, u, w);
+        decode_unit<F>(a.W, static_cast<u32>(row) * static_cast<u32>(a.row_bytes), u, w);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[j] = cvt8(&w[8 * j]);
       } else {

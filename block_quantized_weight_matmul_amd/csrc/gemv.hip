@@ -1,27 +1,41 @@
 // gemv.hip -- matrix-vector paths: dense (1..32 tokens) and expert-indexed.
 //
-// Lane map.  A "row group" is LPR consecutive lanes of a 64-wide wavefront
-// (LPR = 4..64) that share the rows of the group and split the row's 32-weight
-// units between them: lane li takes units li, li+LPR, li+2*LPR, ...  The host
-// picks LPR from K so that the units divide evenly over the lanes where
-// possible -- at K = 512 (16 units) a row takes 16 lanes and a wave holds four
-// rows, so no lane idles.  This is the idea of the llama.cpp pull request
-// "metal : fix idle threads in mul_mv_iq3_xxs for ne00 < 1024" (section
-// "Overview": several lanes per 32-weight chunk row set when there are fewer
-// chunks than lanes), generalised: every (row, chunk) pair is computed once,
-// and lanes beyond a row's last chunk add nothing (section "Additional
-// information").  Each lane carries R rows at once so one load of a chunk of
-// activations serves R rows.
+// Work items.  The unit of work is one "item": one row's 32-weight unit (one
+// Q4_0/Q8_0 block, half an A4G64 group, a Q4_K sub-block, two Q6_K sub-blocks)
+// against every token of the call.  A workgroup owns a contiguous slice of
+// RW rows and spreads the slice's RW * (K/32) items over its threads, item
+// index = row * units + unit, thread t taking items t, t + T, t + 2T, ...  So
+// consecutive lanes read consecutive units of a row (coalesced; units that
+// share code bytes are read by neighbouring lanes of one instruction), and no
+// lane idles whatever K is: at K = 512 a wavefront covers four rows of 16
+// units.  This is the idea of the llama.cpp pull request "metal : fix idle
+// threads in mul_mv_iq3_xxs for ne00 < 1024" (section "Overview": when a row
+// has fewer 32-weight chunks than lanes, lanes share the chunks of several
+// rows), taken to its end: every (row, chunk) pair is computed exactly once
+// (section "Additional information").
 //
-// Token buckets.  The kernel is instantiated per token bucket NB (1, 2, 3, 4,
-// 6, 8, 12, 16, 24, 32) so absent tokens get no registers -- the launch-shape
+// Latency.  Grids hold one or two workgroups per CU, sized so each thread has
+// at most four items; a thread issues the loads of all its items before it
+// decodes the first, so a workgroup's weight bytes are in flight at once.
+// Activations are staged in LDS once per workgroup (in K chunks when they do
+// not fit) together with the sum of each 16-activation half: the only global
+// loads of the item loop are weight bytes (global loads retire in order for
+// s_waitcnt, so an activation load behind a weight prefetch would wait out the
+// prefetch).
+//
+// Token buckets.  Kernels are instantiated per token bucket NB (1, 2, 3, 4, 6,
+// 8, 12, 16, 24, 32) so absent tokens get no registers -- the launch-shape
 // idea of the tiny-llm pull request "perf: Optimize quantized matmul for small
 // decode batches" (section "Summary"), on the token axis.
 //
-// Accuracy.  Each unit's 32 products are summed in a fresh fp32 chain, which is
-// then added to the lane's accumulator; lanes of a row group are combined by a
-// fixed butterfly (DPP within 16 lanes, then cross-row shuffles).  Every weight
-// is the exact fp32 dequantized value.
+// Arithmetic.  With w = a*q + b on each 16-weight half of a unit (one (a, b)
+// pair per half; both halves share it except in Q6_K), an item's partial sum
+// is a0*Sq0 + b0*Sx0 + a1*Sq1 + b1*Sx1 with Sq = sum q*x over the half (a fresh
+// 16-term fp32 chain) and Sx the staged half sum: one conversion and one fma
+// per weight and token.  Partials go to LDS; each output is then the sum of its
+// row's partials in a fixed order (lane l adds units l, l+64, ...; then a
+// butterfly over the wave), so results are deterministic and independent of
+// the launch shape, and the dense and expert-indexed paths agree bit for bit.
 #include <utility>
 
 #include "decode.hpp"
@@ -33,12 +47,11 @@ struct GemvArgs {
   const u8* W;          // block stream of expert 0
   u64 row_bytes;
   u64 expert_bytes;     // M * row_bytes
-  int M, nU;            // rows; 32-weight units per row (K / 32)
-  int lpr_log2;         // log2(lanes per row group)
-  int R;                // rows per lane (must equal the template R)
+  int M, nU, K;         // rows; 32-weight units per row (K / 32); activation row length
+  int rows_per_wg;      // RW
+  int chunk_units;      // units of activations staged in LDS at a time
   const void* x;
   int x_f16;
-  int K;                // activation row length
   float* y;
   int N;                // tokens (dense)
   const int32_t* ids;   // expert-indexed mode
@@ -51,151 +64,208 @@ __device__ __forceinline__ float dpp_mov(float v) {
                                                                0xF, 0xF, false));
 }
 
-// Sum over the 2^lg consecutive lanes of a row group; every lane of the group
-// receives the same value (each step adds a pair of values in both orders,
-// which IEEE addition makes identical).
-__device__ __forceinline__ float group_sum(float v, int lg) {
-  if (lg >= 1) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
-  if (lg >= 2) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
-  if (lg >= 3) v += dpp_mov<0x141>(v);   // row_half_mirror: quads of an 8-lane half
-  if (lg >= 4) v += dpp_mov<0x140>(v);   // row_mirror: halves of a 16-lane row
-  if (lg >= 5) v += __shfl_xor(v, 16);
-  if (lg >= 6) v += __shfl_xor(v, 32);
+// Sum over the 64 lanes of a wave; every lane receives the same value (each step
+// adds a pair of values in both orders, which IEEE addition makes identical).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);   // row_half_mirror: quads of an 8-lane half
+  v += dpp_mov<0x140>(v);   // row_mirror: halves of a 16-lane row
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 
-// 32 activations x[row][32u .. 32u+31] as fp32.
-__device__ __forceinline__ void load_x32(const void* x, int x_f16, int row, int K, int u, float (&v)[32]) {
-  if (x_f16) {
-    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-    const h8* p = reinterpret_cast<const h8*>(reinterpret_cast<const _Float16*>(x) + (u64)row * K + 32 * u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const h8 h = p[j];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[8 * j + e] = static_cast<float>(h[e]);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + (u64)row * K + 32 * u);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 f = p[j];
-      v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-    }
+// Token t of a call reads activation row tm.x(t) and writes output row tm.y(t):
+// the identity for the dense path; for the expert-indexed path, t indexes the
+// LDS list of (token, slot) pairs routed to the workgroup's expert.
+struct TokMap {
+  const int* pairs;  // LDS, or nullptr for the identity
+  int S;             // slots per token
+  int per_slot;      // activations per (token, slot) rather than per token
+  __device__ __forceinline__ int x(int t) const {
+    if (!pairs) return t;
+    const int p = pairs[t];
+    return per_slot ? p : p / S;
   }
+  __device__ __forceinline__ int y(int t) const { return pairs ? pairs[t] : t; }
+};
+
+// LDS layout (floats).  Staged activations: token t, chunk unit uu at
+// (t * KC + uu) * kXStride (4 pad floats per unit spread consecutive units over
+// the LDS banks); their half sums at sx[(t * KC + uu) * 2 + h]; item partials at
+// part[(t * RW + row) * nU + u].
+constexpr int kXStride = 36;
+
+__host__ __device__ constexpr int lds_floats(int NB, int KC, int RW, int nU) {
+  return NB * KC * (kXStride + 2) + NB * RW * nU;
 }
 
-__device__ __forceinline__ float dot32(const float (&w)[32], const float (&x)[32]) {
-  float p = w[0] * x[0];
-#pragma unroll
-  for (int k = 1; k < 32; ++k) p = __builtin_fmaf(w[k], x[k], p);
-  return p;
-}
-
-// One wave's share: this lane's row group owns rows row(i) = row_base + i*G + rg
-// (i < R; G = row groups per wave), and lane li of the group takes units
-// li, li+LPR, ...  Tokens t < ntok read activation row xrow[t] and write y row yrow[t].
-template <int F, int NB, int R>
-__device__ __forceinline__ void gemv_rows(const u8* W, u64 rb, int M, int nU, int lg, int row_base,
-                                          const void* x, int x_f16, int K, const int (&xrow)[NB],
-                                          const int (&yrow)[NB], int ntok, float* y) {
-  const int lane = threadIdx.x & 63;
-  const int LPR = 1 << lg;
-  const int G = 64 >> lg;
-  const int li = lane & (LPR - 1);
-  const int rg = lane >> lg;
-  int row[R];
-  bool rv[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    row[i] = row_base + i * G + rg;
-    rv[i] = row[i] < M;
-  }
-  float acc[R][NB];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int t = 0; t < NB; ++t) acc[i][t] = 0.0f;
-
-  for (int u = li; u < nU; u += LPR) {
-    // rows past M load row M-1 (in bounds); their sums are never stored
-    typename Decoder<F>::Raw raw[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) Decoder<F>::load(W, (u64)(rv[i] ? row[i] : M - 1) * rb, u, raw[i]);
-    if constexpr (NB <= 4) {
-      // activations of every token in registers; decode one row at a time
-      float xv[NB][32];
-#pragma unroll
-      for (int t = 0; t < NB; ++t)
-        if (t < ntok) load_x32(x, x_f16, xrow[t], K, u, xv[t]);
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        Unit o;
-        Decoder<F>::unpack(raw[i], o);
-        float w[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) w[k] = unit_weight(o, k);
-#pragma unroll
-        for (int t = 0; t < NB; ++t)
-          if (t < ntok) acc[i][t] += dot32(w, xv[t]);
-      }
+// Stage activations of units [c0, c0 + cw) of tokens t < ntok as fp32, then the
+// sum of each 16-activation half (fixed order).  Ends with a barrier.
+__device__ __forceinline__ void stage_x(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0,
+                                        int cw, int KC, float* s_x, float* s_sx) {
+  const int per_tok = cw * 8;  // float4 slots per token
+  for (int idx = threadIdx.x; idx < ntok * per_tok; idx += blockDim.x) {
+    const int t = idx / per_tok;
+    const int rem = idx - t * per_tok;
+    const int uu = rem >> 3;
+    const int q4 = rem & 7;
+    const u64 k = (u64)tm.x(t) * K + 32 * (c0 + uu) + 4 * q4;
+    float4 v;
+    if (x_f16) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 h = *reinterpret_cast<const h4*>(reinterpret_cast<const _Float16*>(x) + k);
+      v = make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+                      static_cast<float>(h[3]));
     } else {
-      // decoded weights of every row in registers; one token's activations at a time
-      float w[R][32];
+      v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + k);
+    }
+    *reinterpret_cast<float4*>(&s_x[(t * KC + uu) * kXStride + 4 * q4]) = v;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ntok * cw * 2; idx += blockDim.x) {
+    const int t = idx / (cw * 2);
+    const int rem = idx - t * cw * 2;
+    const int uu = rem >> 1;
+    const int h = rem & 1;
+    const float* p = &s_x[(t * KC + uu) * kXStride + 16 * h];
+    float s = p[0];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        Unit o;
-        Decoder<F>::unpack(raw[i], o);
+    for (int i = 1; i < 16; ++i) s += p[i];
+    s_sx[(t * KC + uu) * 2 + h] = s;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void read_x32(const float* s_x, float (&v)[32]) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) w[i][k] = unit_weight(o, k);
+  for (int j = 0; j < 8; ++j) {
+    const float4 f = *reinterpret_cast<const float4*>(s_x + 4 * j);
+    v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+  }
+}
+
+// sum of q[i]*x[i] over one 16-weight half (first product, then 15 fmas)
+__device__ __forceinline__ float half_dot(const float (&q)[32], const float (&x)[32], int h) {
+  float s = q[16 * h] * x[16 * h];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) s = __builtin_fmaf(q[16 * h + i], x[16 * h + i], s);
+  return s;
+}
+
+// An item's partial sum a0*Sq0 + b0*Sx0 + a1*Sq1 + b1*Sx1 (Q8_0 has no b terms).
+template <int F>
+__device__ __forceinline__ float item_partial(const Unit& o, const float (&q)[32], const float (&x)[32],
+                                              float sx0, float sx1) {
+  const float sq0 = half_dot(q, x, 0), sq1 = half_dot(q, x, 1);
+  if constexpr (F == FMT_Q8_0) {
+    return __builtin_fmaf(o.a0, sq0, o.a1 * sq1);
+  } else {
+    return __builtin_fmaf(o.a0, sq0, __builtin_fmaf(o.b0, sx0, __builtin_fmaf(o.a1, sq1, o.b1 * sx1)));
+  }
+}
+
+// Items per thread per batch: a thread issues the loads of all its items of a
+// batch before decoding any (the host sizes workgroups so that one batch
+// usually covers the whole slice).
+constexpr int kIpt = 4;
+
+// Rows [r0, r0 + rows) of the matrix at W (rows <= RW), all tokens t < ntok.
+// Byte offsets within one matrix fit 32 bits (checked by the host).
+template <int F, int NB>
+__device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, int K, int r0, int rows, int RW,
+                                          int KC, const void* x, int x_f16, const TokMap& tm, int ntok, float* y,
+                                          float* lds) {
+  float* s_x = lds;
+  float* s_sx = s_x + NB * KC * kXStride;
+  float* s_part = s_sx + NB * KC * 2;
+  const int T = blockDim.x;
+  const int tid = threadIdx.x;
+
+  for (int c0 = 0; c0 < nU; c0 += KC) {
+    const int cw = min(KC, nU - c0);
+    const int items = rows * cw;
+    const int drow = T / cw, du = T - drow * cw;  // item index step T as (rows, units)
+    for (int b0 = 0; b0 < items; b0 += T * kIpt) {
+      // this thread's items of the batch: b0 + tid + j*T, j < n
+      const int first = b0 + tid;
+      const int n = first < items ? min(kIpt, (items - first + T - 1) / T) : 0;
+      int row = first / cw;
+      int uu = first - row * cw;
+      typename Decoder<F>::Raw raw[kIpt];
+      int irow[kIpt], iu[kIpt];
+#pragma unroll
+      for (int j = 0; j < kIpt; ++j) {
+        irow[j] = row;
+        iu[j] = uu;
+        if (j < n) Decoder<F>::load(W, (u32)(r0 + row) * rb, c0 + uu, raw[j]);
+        row += drow;
+        uu += du;
+        if (uu >= cw) { uu -= cw; ++row; }
+      }
+      if (b0 == 0) {
+        if (c0 > 0) __syncthreads();  // readers of the previous chunk are done
+        stage_x(x, x_f16, K, tm, ntok, c0, cw, KC, s_x, s_sx);
       }
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        if (t < ntok) {
-          float xv[32];
-          load_x32(x, x_f16, xrow[t], K, u, xv);
+      for (int j = 0; j < kIpt; ++j) {
+        if (j < n) {
+          Unit o;
+          float q[32];
+          Decoder<F>::unpack(raw[j], o);
+          unit_codes<F>(o, q);
 #pragma unroll
-          for (int i = 0; i < R; ++i) acc[i][t] += dot32(w[i], xv);
+          for (int t = 0; t < NB; ++t) {
+            if (t < ntok) {
+              float xv[32];
+              const int xo = t * KC + iu[j];
+              read_x32(s_x + xo * kXStride, xv);
+              s_part[(t * RW + irow[j]) * nU + c0 + iu[j]] =
+                  item_partial<F>(o, q, xv, s_sx[xo * 2], s_sx[xo * 2 + 1]);
+            }
+          }
         }
       }
     }
   }
+  __syncthreads();
 
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      if (t < ntok) {
-        const float v = group_sum(acc[i][t], lg);
-        if (li == 0 && rv[i]) y[(u64)yrow[t] * M + row[i]] = v;
-      }
-    }
+  // one wave per (row, token): lane l adds units l, l+64, ..., then the butterfly
+  const int wave = tid >> 6, lane = tid & 63, nw = T >> 6;
+  for (int rt = wave; rt < rows * ntok; rt += nw) {
+    const int row = rt / ntok, t = rt - row * ntok;
+    const float* pp = s_part + (t * RW + row) * nU;
+    float v = 0.0f;
+    for (int u = lane; u < nU; u += 64) v += pp[u];
+    v = wave_sum(v);
+    if (lane == 0) y[(u64)tm.y(t) * M + r0 + row] = v;
+  }
+  __syncthreads();  // LDS is reused by the caller's next pass
 }
 
-template <int F, int NB, int R>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-  const int wave = threadIdx.x >> 6;
-  const int waves = blockDim.x >> 6;
-  const int G = 64 >> a.lpr_log2;
-  const int row_base = (blockIdx.x * waves + wave) * (G * R);
-  int xrow[NB], yrow[NB];
-#pragma unroll
-  for (int t = 0; t < NB; ++t) xrow[t] = yrow[t] = t;
-  gemv_rows<F, NB, R>(a.W, a.row_bytes, a.M, a.nU, a.lpr_log2, row_base, a.x, a.x_f16, a.K, xrow, yrow,
-                      a.N, a.y);
+extern __shared__ float s_dyn[];  // sized at launch: lds_floats(NB, KC, RW, nU)
+
+template <int F, int NB>
+__global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
+  const int r0 = blockIdx.x * a.rows_per_wg;
+  const int rows = min(a.rows_per_wg, a.M - r0);
+  const TokMap tm{nullptr, 1, 1};
+  gemv_rows<F, NB>(a.W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows, a.rows_per_wg, a.chunk_units,
+                   a.x, a.x_f16, tm, a.N, a.y, s_dyn);
 }
 
 // Expert-indexed: blockIdx.y = rank k of the expert among the distinct valid ids
-// of this call (ascending), blockIdx.x = row tile.  Each workgroup builds, in LDS,
+// of this call (ascending), blockIdx.x = row slice.  Each workgroup builds, in LDS,
 // the presence bitmap of the ids, finds its expert and the (token, slot) pairs
-// routed to it, and streams that expert's rows of its tile once per NB pairs.
+// routed to it, and streams that expert's rows of its slice once per NB pairs.
 constexpr int kIdBitmapWords = static_cast<int>(kMaxExperts / 32);
 constexpr int kIdMaxPairs = static_cast<int>(kMaxGemvTokens * kMaxSlots);
 
-template <int F, int NB, int R>
-__global__ __launch_bounds__(256) void k_gemv_id(GemvArgs a) {
+template <int F, int NB>
+__global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
   __shared__ u32 s_bits[kIdBitmapWords];
-  __shared__ int s_cnt[256];
+  __shared__ int s_cnt[512];
   __shared__ int s_pairs[kIdMaxPairs];
   __shared__ int s_expert, s_npairs;
 
@@ -203,11 +273,8 @@ __global__ __launch_bounds__(256) void k_gemv_id(GemvArgs a) {
   const int nthr = blockDim.x;
   const int P = a.N * a.S;
   const int nwords = (a.E + 31) >> 5;
-  const int wave = threadIdx.x >> 6;
-  const int waves = blockDim.x >> 6;
-  const int G = 64 >> a.lpr_log2;
-  const int rows_per_wg = waves * G * R;
-  const int row_tile0 = blockIdx.x * rows_per_wg;
+  const int r0 = blockIdx.x * a.rows_per_wg;
+  const int rows = min(a.rows_per_wg, a.M - r0);
 
   for (int w = tid; w < nwords; w += nthr) s_bits[w] = 0u;
   if (tid == 0) { s_expert = -1; s_npairs = 0; }
@@ -218,7 +285,7 @@ __global__ __launch_bounds__(256) void k_gemv_id(GemvArgs a) {
   }
   __syncthreads();
 
-  // k-th set bit: thread t counts words [t*wpt, (t+1)*wpt), then an exclusive scan.
+  // k-th set bit: thread t counts words [t*wpt, (t+1)*wpt), then an inclusive scan.
   const int k = blockIdx.y;
   const int wpt = (nwords + nthr - 1) / nthr;
   int cnt = 0;
@@ -249,14 +316,13 @@ __global__ __launch_bounds__(256) void k_gemv_id(GemvArgs a) {
   const int e = s_expert;
 
   // Ids outside [0, E) have no matrix: their output rows are NaN (written by the
-  // rank-0 workgroups, which exist for every row tile).
+  // rank-0 workgroups, which exist for every row slice).
   if (blockIdx.y == 0) {
     const float qnan = __builtin_nanf("");
-    const int rows = min(rows_per_wg, a.M - row_tile0);
     for (int p = 0; p < P; ++p) {
       const int id = a.ids[p];
       if (id < 0 || id >= a.E)
-        for (int r = tid; r < rows; r += nthr) a.y[(u64)p * a.M + row_tile0 + r] = qnan;
+        for (int r = tid; r < rows; r += nthr) a.y[(u64)p * a.M + r0 + r] = qnan;
     }
   }
   if (e < 0) return;  // uniform over the workgroup
@@ -267,18 +333,10 @@ __global__ __launch_bounds__(256) void k_gemv_id(GemvArgs a) {
   const int np = s_npairs;
 
   const u8* W = a.W + (u64)e * a.expert_bytes;
-  const int row_base = row_tile0 + wave * (G * R);
-  for (int c0 = 0; c0 < np; c0 += NB) {
-    const int ntok = min(NB, np - c0);
-    int xrow[NB], yrow[NB];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const int p = t < ntok ? s_pairs[c0 + t] : 0;
-      xrow[t] = a.x_per_slot ? p : p / a.S;
-      yrow[t] = p;
-    }
-    gemv_rows<F, NB, R>(W, a.row_bytes, a.M, a.nU, a.lpr_log2, row_base, a.x, a.x_f16, a.K, xrow, yrow,
-                        ntok, a.y);
+  for (int c = 0; c < np; c += NB) {
+    const TokMap tm{s_pairs + c, a.S, a.x_per_slot};
+    gemv_rows<F, NB>(W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows, a.rows_per_wg, a.chunk_units,
+                     a.x, a.x_f16, tm, min(NB, np - c), a.y, s_dyn);
   }
 }
 
@@ -296,28 +354,15 @@ int bucket_index(int n) {
   return -1;
 }
 
-// Rows per lane for a token bucket: more rows share each activation load when
-// activations sit in registers (NB <= 4); fewer rows keep registers in check above.
-constexpr int rows_per_lane(int NB) { return NB <= 2 ? 4 : (NB <= 8 ? 2 : 1); }
-
 typedef void (*GemvKernel)(GemvArgs);
-
-template <int F, int BI>
-constexpr GemvKernel dense_kernel() {
-  return k_gemv<F, kBuckets[BI], rows_per_lane(kBuckets[BI])>;
-}
-template <int F, int BI>
-constexpr GemvKernel id_kernel() {
-  return k_gemv_id<F, kBuckets[BI], rows_per_lane(kBuckets[BI])>;
-}
 
 template <int F, int... BI>
 constexpr void fill_dense(GemvKernel* t, std::integer_sequence<int, BI...>) {
-  ((t[BI] = dense_kernel<F, BI>()), ...);
+  ((t[BI] = k_gemv<F, kBuckets[BI]>), ...);
 }
 template <int F, int... BI>
 constexpr void fill_id(GemvKernel* t, std::integer_sequence<int, BI...>) {
-  ((t[BI] = id_kernel<F, BI>()), ...);
+  ((t[BI] = k_gemv_id<F, kBuckets[BI]>), ...);
 }
 
 struct Tables {
@@ -343,37 +388,35 @@ const Tables& tables() {
   return t;
 }
 
-// Lanes per row group: the power of two in 4..64 that leaves the fewest lanes
-// idle on the last pass over the row's units (ties go to the wider group).
-int choose_lpr_log2(int nU) {
-  int best = 6;
-  long best_idle = 0, best_slots = 1;
-  for (int lg = 6; lg >= 2; --lg) {
-    const long L = 1L << lg;
-    const long slots = ((nU + L - 1) / L) * L;
-    const long idle = slots - nU;
-    if (lg == 6 || idle * best_slots < best_idle * slots) {  // strictly fewer idle lanes (fraction)
-      best = lg;
-      best_idle = idle;
-      best_slots = slots;
-    }
-  }
-  return best;
-}
+constexpr int kCUs = 256;
+constexpr int kLdsBudget = 64 * 1024;  // bytes of dynamic LDS per workgroup
 
 struct Shape {
-  int lg, R, waves, rows_per_wg;
+  int RW;       // rows per workgroup
+  int KC;       // activation units staged per chunk
+  int threads;  // workgroup size
+  int grid;     // row slices
+  size_t lds;   // dynamic LDS bytes
 };
 
-Shape gemv_shape(int nU, int M, int NB) {
+// A workgroup of RW rows (clamped so that its items fit 512 threads x ipt and its
+// partial sums use at most half the LDS budget); threads: one per ipt items, in
+// whole waves, 64..512; the activation chunk takes the LDS that is left.
+Shape make_shape(int M, int nU, int NB, int RW, int ipt) {
   Shape s;
-  s.lg = choose_lpr_log2(nU);
-  s.R = rows_per_lane(NB);
-  const int rows_per_wave = (64 >> s.lg) * s.R;
-  // up to 4 waves per workgroup while that still leaves >= 512 workgroups
-  s.waves = 4;
-  while (s.waves > 1 && (M + s.waves * rows_per_wave - 1) / (s.waves * rows_per_wave) < 512) s.waves >>= 1;
-  s.rows_per_wg = s.waves * rows_per_wave;
+  const int max_rw_threads = (512 * ipt) / nU;
+  const int max_rw_lds = (kLdsBudget / 2 / 4) / (NB * nU);
+  if (RW > max_rw_threads) RW = max_rw_threads;
+  if (RW > max_rw_lds) RW = max_rw_lds;
+  if (RW > M) RW = M;
+  if (RW < 1) RW = 1;
+  s.RW = RW;
+  int threads = ((RW * nU + ipt - 1) / ipt + 63) / 64 * 64;
+  s.threads = threads > 512 ? 512 : (threads < 64 ? 64 : threads);
+  int KC = (kLdsBudget / 4 - NB * RW * nU) / (NB * (kXStride + 2));
+  s.KC = KC > nU ? nU : (KC < 1 ? 1 : KC);
+  s.grid = (M + RW - 1) / RW;
+  s.lds = static_cast<size_t>(lds_floats(NB, s.KC, RW, nU)) * sizeof(float);
   return s;
 }
 
@@ -383,22 +426,23 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
   const int bi = bucket_index(N);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
-  const Shape s = gemv_shape(nU, static_cast<int>(m.M), kBuckets[bi]);
+  const int M = static_cast<int>(m.M);
+  // about two workgroups per CU
+  const Shape s = make_shape(M, nU, kBuckets[bi], (M + 2 * kCUs - 1) / (2 * kCUs), 2);
   GemvArgs a{};
   a.W = m.blocks;
   a.row_bytes = m.row_bytes;
   a.expert_bytes = m.row_bytes * static_cast<u64>(m.M);
   a.M = static_cast<int>(m.M);
   a.nU = nU;
-  a.lpr_log2 = s.lg;
-  a.R = s.R;
+  a.K = static_cast<int>(m.K);
+  a.rows_per_wg = s.RW;
+  a.chunk_units = s.KC;
   a.x = x;
   a.x_f16 = x_f16;
-  a.K = static_cast<int>(m.K);
   a.y = y;
   a.N = N;
-  const dim3 grid((m.M + s.rows_per_wg - 1) / s.rows_per_wg);
-  hipLaunchKernelGGL(tables().dense[m.fmt][bi], grid, dim3(64 * s.waves), 0, st, a);
+  hipLaunchKernelGGL(tables().dense[m.fmt][bi], dim3(s.grid), dim3(s.threads), s.lds, st, a);
   return hipGetLastError();
 }
 
@@ -409,28 +453,31 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   const int bi = bucket_index(N < 8 ? N : 8);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
-  Shape s = gemv_shape(nU, static_cast<int>(m.M), kBuckets[bi]);
+  const int64_t P = static_cast<int64_t>(N) * S;
+  const int ranks = static_cast<int>(P < m.n_experts ? P : m.n_experts);
+  // the grid is ranks x row slices: about two workgroups per CU over all the
+  // active experts
+  const int M = static_cast<int>(m.M);
+  const int slices = (2 * kCUs + ranks - 1) / ranks;
+  const Shape s = make_shape(M, nU, kBuckets[bi], (M + slices - 1) / slices, 2);
   GemvArgs a{};
   a.W = m.blocks;
   a.row_bytes = m.row_bytes;
   a.expert_bytes = m.row_bytes * static_cast<u64>(m.M);
-  a.M = static_cast<int>(m.M);
+  a.M = M;
   a.nU = nU;
-  a.lpr_log2 = s.lg;
-  a.R = s.R;
+  a.K = static_cast<int>(m.K);
+  a.rows_per_wg = s.RW;
+  a.chunk_units = s.KC;
   a.x = x;
   a.x_f16 = x_f16;
-  a.K = static_cast<int>(m.K);
   a.y = y;
   a.N = N;
   a.ids = ids;
   a.S = S;
   a.x_per_slot = x_per_slot;
   a.E = static_cast<int>(m.n_experts);
-  const int64_t P = static_cast<int64_t>(N) * S;
-  const int ranks = static_cast<int>(P < m.n_experts ? P : m.n_experts);
-  const dim3 grid((m.M + s.rows_per_wg - 1) / s.rows_per_wg, ranks);
-  hipLaunchKernelGGL(tables().id[m.fmt][bi], grid, dim3(64 * s.waves), 0, st, a);
+  hipLaunchKernelGGL(tables().id[m.fmt][bi], dim3(s.grid, ranks), dim3(s.threads), s.lds, st, a);
   return hipGetLastError();
 }
 

@@ -103,7 +103,8 @@ typedef struct qmm_matrix qmm_matrix;
  *              the handle and stay unmodified.
  *   n_experts  1 for a plain matrix; E for the stacked experts of qmm_gemm_id.
  *   M, K       rows and reduction length; K a positive multiple of the block's
- *              weight count (32, 32, 256, 256, 64); M >= 1.
+ *              weight count (32, 32, 256, 256, 64); M >= 1; one matrix
+ *              (M * row_bytes(K)) below 4 GiB.
  * Checks that the current device is gfx950 (QMM_E_DEVICE otherwise) and records it.
  */
 qmm_status qmm_create(qmm_matrix **out, qmm_type type, const void *blocks,

@@ -111,3 +111,22 @@ def test_gemm_id_zero_tokens_is_noop():
     y = torch.full((1, 1, M), 5.0, device="cuda")
     q.qmm_gemm_id(qm.handle, x, 0, 1, 1, ids, y)
     assert np.all(to_host(y) == 5.0)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q6_k"])
+def test_gemm_id_experts_not_dword_aligned(fmt):
+    """Experts of an odd number of blocks of 18, 34 or 210 bytes: expert e > 0
+    starts 2 bytes off a dword boundary."""
+    E, M, N, S = 5, 3, 4, 3
+    K = oracle.block_weights(fmt)
+    assert (M * oracle.row_bytes(fmt, K)) % 4 == 2
+    blob, ws = _stack(fmt, E, M, K, 68)
+    g = np.random.default_rng(68)
+    ids = _ids(g, N, S, E)
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL, "odd experts")
+    for e in range(E):
+        got = to_host(qm.dequantize(e))
+        assert np.array_equal(got, ws[e]), f"expert {e}"
