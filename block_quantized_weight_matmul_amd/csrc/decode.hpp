@@ -164,19 +164,20 @@ template <> struct Decoder<FMT_Q4_K> {
     for (int k = 0; k < 8; ++k) r.q[k] = q[k];
   }
   // sc_j = bits [6j, 6j+6) and m_j = bits [48+6j, 54+6j) of the 96-bit string in
-  // h[1] (bits 0..31), h[2] (32..63), h[3] (64..95): funnel-shift the pair of
-  // words holding the field (selected as values, so nothing is indexed).
+  // h[1] (bits 0..31), h[2] (32..63), h[3] (64..95).  Both candidate funnel shifts
+  // are computed and one is selected, so no word is picked by a runtime index
+  // (which the compiler would turn into a load from private memory).
   __device__ __forceinline__ static u32 field_sc(const Raw& r) {
     const u32 b = 6u * static_cast<u32>(r.j);  // 0..42
-    const u32 lo = b < 32 ? r.h[1] : r.h[2];
-    const u32 hi = b < 32 ? r.h[2] : r.h[3];
-    return __builtin_amdgcn_alignbit(hi, lo, b & 31u) & 63u;
+    const u32 t0 = __builtin_amdgcn_alignbit(r.h[2], r.h[1], b & 31u);
+    const u32 t1 = __builtin_amdgcn_alignbit(r.h[3], r.h[2], b & 31u);
+    return (b < 32 ? t0 : t1) & 63u;
   }
   __device__ __forceinline__ static u32 field_m(const Raw& r) {
     const u32 b = 48u + 6u * static_cast<u32>(r.j);  // 48..90
-    const u32 lo = b < 64 ? r.h[2] : r.h[3];
-    const u32 hi = b < 64 ? r.h[3] : 0u;
-    return __builtin_amdgcn_alignbit(hi, lo, b & 31u) & 63u;
+    const u32 t0 = __builtin_amdgcn_alignbit(r.h[3], r.h[2], b & 31u);
+    const u32 t1 = r.h[3] >> (b & 31u);
+    return (b < 64 ? t0 : t1) & 63u;
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
     const u32 sh = 4u * static_cast<u32>(r.j & 1);
@@ -273,5 +274,145 @@ __device__ __forceinline__ void decode_unit(const u8* base, u32 row_off, int u, 
   Decoder<F>::unpack(r, o);
   unit_weights<F>(o, w);
 }
+
+}  // namespace qmm
+
+namespace qmm {
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-vector work items: RUNS runs of 32 weights that share their bytes, so the
+// scale fields and code bytes are fetched and unpacked once for all of them.
+//   Q4_0, Q8_0  one block (1 run, unit i).
+//   Q4_K        sub-blocks 2p, 2p+1 of a super-block (units 2i, 2i+1): the low and
+//               high nibbles of the same 32 code bytes, one 16-byte header.
+//   Q6_K        runs a and a+4 of a super-block (units 8s+a, 8s+a+4, a = i%4): the
+//               low and high nibbles of the same 32 ql bytes and two bit pairs of
+//               the same 32 qh bytes.
+//   A4G64       one group (units 2i, 2i+1): both nibbles of 32 code bytes.
+// A high-nibble run keeps its codes in place (16*q in each byte) and carries
+// a/16 instead of a: (a/16)*(16q) is the same fp32 value as a*q (power-of-two
+// scalings are exact), and so is every partial sum of such products.
+template <int F> struct Item;
+
+template <> struct Item<FMT_Q4_0> {
+  static constexpr int RUNS = 1;
+  using Raw = Decoder<FMT_Q4_0>::Raw;
+  __device__ __forceinline__ static int unit(int i, int) { return i; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    Decoder<FMT_Q4_0>::load(base, row_off, i, r);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[1]) { Decoder<FMT_Q4_0>::unpack(r, o[0]); }
+};
+
+template <> struct Item<FMT_Q8_0> {
+  static constexpr int RUNS = 1;
+  using Raw = Decoder<FMT_Q8_0>::Raw;
+  __device__ __forceinline__ static int unit(int i, int) { return i; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    Decoder<FMT_Q8_0>::load(base, row_off, i, r);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[1]) { Decoder<FMT_Q8_0>::unpack(r, o[0]); }
+};
+
+template <> struct Item<FMT_Q4_K> {
+  static constexpr int RUNS = 2;
+  struct Raw { u32 h[4]; u32 q[8]; int p; };
+  __device__ __forceinline__ static int unit(int i, int run) { return 2 * i + run; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    const u32 so = row_off + 144u * static_cast<u32>(i >> 2);
+    r.p = i & 3;
+    const u32* h = reinterpret_cast<const u32*>(base + so);
+    const u32* q = reinterpret_cast<const u32*>(base + so + 16 + 32 * r.p);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.h[k] = h[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.q[k] = q[k];
+  }
+  // 12-bit field pairs (sc_{2p}, sc_{2p+1}) at bit 12p and (m_{2p}, m_{2p+1}) at
+  // bit 48+12p of the bit string h[1..3]; candidates computed, then selected (no
+  // runtime-indexed word, see Decoder<FMT_Q4_K>).
+  __device__ __forceinline__ static u32 sc_pair(const Raw& r) {
+    const u32 b = 12u * static_cast<u32>(r.p);  // 0..36
+    const u32 t0 = __builtin_amdgcn_alignbit(r.h[2], r.h[1], b & 31u);
+    const u32 t1 = __builtin_amdgcn_alignbit(r.h[3], r.h[2], b & 31u);
+    return (b < 32 ? t0 : t1) & 0xFFFu;
+  }
+  __device__ __forceinline__ static u32 m_pair(const Raw& r) {
+    const u32 b = 48u + 12u * static_cast<u32>(r.p);  // 48..84
+    const u32 t0 = __builtin_amdgcn_alignbit(r.h[3], r.h[2], b & 31u);
+    const u32 t1 = r.h[3] >> (b & 31u);
+    return (b < 64 ? t0 : t1) & 0xFFFu;
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[2]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[0].c[k] = r.q[k] & 0x0F0F0F0Fu;
+      o[1].c[k] = r.q[k] & 0xF0F0F0F0u;  // 16 * code
+    }
+    const float d = h2f(r.h[0]);
+    const float dmin = h2f(r.h[0] >> 16);
+    const u32 sc = sc_pair(r);
+    const u32 m = m_pair(r);
+    o[0].a0 = o[0].a1 = d * static_cast<float>(sc & 63u);
+    o[0].b0 = o[0].b1 = -(dmin * static_cast<float>(m & 63u));
+    o[1].a0 = o[1].a1 = d * static_cast<float>(sc >> 6) * 0.0625f;
+    o[1].b0 = o[1].b1 = -(dmin * static_cast<float>(m >> 6));
+  }
+};
+
+template <> struct Item<FMT_Q6_K> {
+  static constexpr int RUNS = 2;
+  struct Raw { u32 ql[8]; u32 qh[8]; u32 d; u32 sc0, sc1; int a; };
+  __device__ __forceinline__ static int unit(int i, int run) { return 8 * (i >> 2) + (i & 3) + 4 * run; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    const u32 so = row_off + 210u * static_cast<u32>(i >> 2);
+    r.a = i & 3;
+    load_bytes<32>(base + so + 18 + 32 * r.a, r.ql);
+    load_bytes<32>(base + so + 146 + 32 * (r.a & 1), r.qh);
+    r.d = load_u16(base + so);
+    r.sc0 = load_u16(base + so + 2 + 2 * r.a);    // sub-blocks 2a, 2a+1
+    r.sc1 = load_u16(base + so + 10 + 2 * r.a);   // sub-blocks 2a+8, 2a+9
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[2]) {
+    const u32 hs = 2u * static_cast<u32>(r.a >> 1);  // run a: bits hs, run a+4: bits hs+4
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[0].c[k] = (r.ql[k] & 0x0F0F0F0Fu) | (((r.qh[k] >> hs) & 0x03030303u) << 4);
+      o[1].c[k] = ((r.ql[k] >> 4) & 0x0F0F0F0Fu) | (((r.qh[k] >> (hs + 4)) & 0x03030303u) << 4);
+    }
+    const float d = h2f(r.d);
+    const u32 sc[2] = {r.sc0, r.sc1};
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      o[run].a0 = d * static_cast<float>(static_cast<int8_t>(sc[run] & 0xFFu));
+      o[run].a1 = d * static_cast<float>(static_cast<int8_t>((sc[run] >> 8) & 0xFFu));
+      o[run].b0 = -32.0f * o[run].a0;
+      o[run].b1 = -32.0f * o[run].a1;
+    }
+  }
+};
+
+template <> struct Item<FMT_A4G64> {
+  static constexpr int RUNS = 2;
+  struct Raw { u32 q[8]; u32 hdr; };
+  __device__ __forceinline__ static int unit(int i, int run) { return 2 * i + run; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    const u32* p = reinterpret_cast<const u32*>(base + row_off + 36u * static_cast<u32>(i));
+    r.hdr = p[0];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.q[k] = p[1 + k];
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[2]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[0].c[k] = r.q[k] & 0x0F0F0F0Fu;
+      o[1].c[k] = r.q[k] & 0xF0F0F0F0u;  // 16 * code
+    }
+    const float scale = h2f(r.hdr), bias = h2f(r.hdr >> 16);
+    o[0].a0 = o[0].a1 = scale;
+    o[1].a0 = o[1].a1 = scale * 0.0625f;
+    o[0].b0 = o[0].b1 = o[1].b0 = o[1].b1 = bias;
+  }
+};
 
 }  // namespace qmm

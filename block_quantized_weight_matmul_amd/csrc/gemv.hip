@@ -169,14 +169,18 @@ __device__ __forceinline__ float item_partial(const Unit& o, const float (&q)[32
 // Items per thread per batch: a thread issues the loads of all its items of a
 // batch before decoding any (the host sizes workgroups so that one batch
 // usually covers the whole slice).
-constexpr int kIpt = 4;
+constexpr int ipt_max(int NB) { return NB <= 8 ? 4 : (NB <= 16 ? 3 : 2); }
 
 // Rows [r0, r0 + rows) of the matrix at W (rows <= RW), all tokens t < ntok.
-// Byte offsets within one matrix fit 32 bits (checked by the host).
+// Byte offsets within one matrix fit 32 bits (checked by the host).  KC is a
+// multiple of 8 units, so chunk boundaries never split an item's runs.
 template <int F, int NB>
 __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, int K, int r0, int rows, int RW,
                                           int KC, const void* x, int x_f16, const TokMap& tm, int ntok, float* y,
                                           float* lds) {
+  using It = Item<F>;
+  constexpr int RUNS = It::RUNS;
+  constexpr int kIpt = ipt_max(NB);
   float* s_x = lds;
   float* s_sx = s_x + NB * KC * kXStride;
   float* s_part = s_sx + NB * KC * 2;
@@ -185,24 +189,26 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
 
   for (int c0 = 0; c0 < nU; c0 += KC) {
     const int cw = min(KC, nU - c0);
-    const int items = rows * cw;
-    const int drow = T / cw, du = T - drow * cw;  // item index step T as (rows, units)
+    const int ipr = cw / RUNS;        // items per row in the chunk
+    const int i0 = c0 / RUNS;         // first item of the chunk
+    const int items = rows * ipr;
+    const int drow = T / ipr, di = T - drow * ipr;  // item index step T as (rows, items)
     for (int b0 = 0; b0 < items; b0 += T * kIpt) {
       // this thread's items of the batch: b0 + tid + j*T, j < n
       const int first = b0 + tid;
       const int n = first < items ? min(kIpt, (items - first + T - 1) / T) : 0;
-      int row = first / cw;
-      int uu = first - row * cw;
-      typename Decoder<F>::Raw raw[kIpt];
-      int irow[kIpt], iu[kIpt];
+      int row = first / ipr;
+      int ii = first - row * ipr;
+      typename It::Raw raw[kIpt];
+      int irow[kIpt], iit[kIpt];
 #pragma unroll
       for (int j = 0; j < kIpt; ++j) {
         irow[j] = row;
-        iu[j] = uu;
-        if (j < n) Decoder<F>::load(W, (u32)(r0 + row) * rb, c0 + uu, raw[j]);
+        iit[j] = i0 + ii;
+        if (j < n) It::load(W, (u32)(r0 + row) * rb, i0 + ii, raw[j]);
         row += drow;
-        uu += du;
-        if (uu >= cw) { uu -= cw; ++row; }
+        ii += di;
+        if (ii >= ipr) { ii -= ipr; ++row; }
       }
       if (b0 == 0) {
         if (c0 > 0) __syncthreads();  // readers of the previous chunk are done
@@ -211,18 +217,21 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
 #pragma unroll
       for (int j = 0; j < kIpt; ++j) {
         if (j < n) {
-          Unit o;
-          float q[32];
-          Decoder<F>::unpack(raw[j], o);
-          unit_codes<F>(o, q);
+          Unit o[RUNS];
+          It::unpack(raw[j], o);
 #pragma unroll
-          for (int t = 0; t < NB; ++t) {
-            if (t < ntok) {
-              float xv[32];
-              const int xo = t * KC + iu[j];
-              read_x32(s_x + xo * kXStride, xv);
-              s_part[(t * RW + irow[j]) * nU + c0 + iu[j]] =
-                  item_partial<F>(o, q, xv, s_sx[xo * 2], s_sx[xo * 2 + 1]);
+          for (int r = 0; r < RUNS; ++r) {
+            const int u = It::unit(iit[j], r);
+            float q[32];
+            unit_codes<F>(o[r], q);
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+              if (t < ntok) {
+                float xv[32];
+                const int xo = t * KC + (u - c0);
+                read_x32(s_x + xo * kXStride, xv);
+                s_part[(t * RW + irow[j]) * nU + u] = item_partial<F>(o[r], q, xv, s_sx[xo * 2], s_sx[xo * 2 + 1]);
+              }
             }
           }
         }
@@ -414,7 +423,8 @@ Shape make_shape(int M, int nU, int NB, int RW, int ipt) {
   int threads = ((RW * nU + ipt - 1) / ipt + 63) / 64 * 64;
   s.threads = threads > 512 ? 512 : (threads < 64 ? 64 : threads);
   int KC = (kLdsBudget / 4 - NB * RW * nU) / (NB * (kXStride + 2));
-  s.KC = KC > nU ? nU : (KC < 1 ? 1 : KC);
+  KC = KC / 8 * 8;  // chunks hold whole super-blocks, so an item's runs share a chunk
+  s.KC = KC >= nU ? nU : (KC < 8 ? 8 : KC);
   s.grid = (M + RW - 1) / RW;
   s.lds = static_cast<size_t>(lds_floats(NB, s.KC, RW, nU)) * sizeof(float);
   return s;
