@@ -15,10 +15,11 @@ launch overhead; the kernels are the ones an eager call runs).
 
 Also reported:
   roofline      the dominant kernel (the GEMV instance with the most time per
-                step): algorithmic bytes per launch / its mean duration from HIP
-                events around each launch, against 8 TB/s; "traffic" from the
-                rocprofv3 counter summary in profiles/ when it was taken on the
-                current kernel source, else null.
+                step): algorithmic bytes per launch / its mean launch time, from
+                HIP events around a graph of back-to-back launches of each
+                projection, against 8 TB/s; "traffic" from the rocprofv3 counter
+                summary in profiles/ when it was taken on the current kernel
+                source, else null.
   cpu_baseline  the CPU oracle (NumPy dequantization + fp64 matmul) on a bounded
                 sample of the same workload, in the same unit.
   extras        the other workloads: the single Q4_0 256x512 matvec, 4-bit
@@ -54,7 +55,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--event-launches", type=int, default=60, help="launches per projection in the event pass")
+    p.add_argument("--event-launches", type=int, default=64, help="launches per projection in the per-kernel pass")
     p.add_argument("--calls", type=int, default=20, help="calls per timed sample in the extras")
     p.add_argument("--rounds", type=int, default=6, help="timed samples per extra case (median)")
     p.add_argument("--copy-probe", action="store_true", help="only run a 256 MiB device copy (counter calibration)")
@@ -172,20 +173,15 @@ def decode_layer(torch, q, W, args):
     ms_per_step = wall_s * 1e3 / args.steps
     value = layer_weight_bytes * args.steps / wall_s / 1e9
 
-    # per-launch event pass: eager launches, each bracketed by events on the stream it runs on
+    # per-kernel pass: for each projection, a graph of R back-to-back launches (rotating
+    # copies) timed with HIP events on the stream it is replayed on; mean per launch
     R = args.event_launches
-    dur = np.zeros((P, R))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    mean_us = np.zeros(P)
     for j in range(P):
-        for r in range(R):
-            c = r % rot.copies
-            evs[r][0].record()
-            q.qmm_gemv(handles[c][j].handle, xs[j], 1, ys[j])
-            evs[r][1].record()
-        torch.cuda.synchronize()
-        dur[j] = [a.elapsed_time(b) for a, b in evs]
-    mean_us = dur.mean(axis=1) * 1e3
-
+        g = capture(torch, lambda j=j: [q.qmm_gemv(handles[r % rot.copies][j].handle, xs[j], 1, ys[j])
+                                       for r in range(R)])
+        mean_us[j] = time_graph(torch, g, 5) * 1e3 / R
+        del g
     # kernels are instantiated per block format (the token bucket is fixed at one token)
     per_kernel = {}
     for j, m in enumerate(mats):
