@@ -171,6 +171,9 @@ qmm_status qmm_gemm(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N,
     return fail(QMM_E_ARG, "tile must be QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64 (got %d)", static_cast<int>(tile));
   if (N < 0 || N > (1LL << 24))
     return fail(QMM_E_SHAPE, "qmm_gemm takes 0..2^24 tokens (got %lld)", static_cast<long long>(N));
+  if (h->d.K >= qmm::kMaxGemmK)
+    return fail(QMM_E_SHAPE, "qmm_gemm takes K below %lld (handle has K=%lld)",
+                static_cast<long long>(qmm::kMaxGemmK), static_cast<long long>(h->d.K));
   qmm_status s;
   if ((s = check_x(x, xt)) != QMM_OK || (s = check_y(y)) != QMM_OK) return s;
   if (N == 0) return ok();

@@ -2,25 +2,33 @@
 //
 // Candle pull request "Metal: 64-token tile for the quantized matrix-matrix
 // kernel": a workgroup owns a tile of weight rows; on every step along K it
-// reads those rows' blocks, dequantizes them once into LDS and multiplies them
-// by the tokens of its tile (section "Why the tile sets the weight reuse"), so
-// each weight is fetched and decoded once per token tile.  The tile is 32 or
-// 64 tokens (section "What changes"), and the two tiles must give bit-identical
-// outputs (section "Same results, bit for bit").
+// reads those rows' blocks, dequantizes them once and multiplies them by every
+// token of its token tile (section "Why the tile sets the weight reuse"); the
+// token tile is 32 or 64, the 64-token tile used only when it pads no more
+// tokens (section "Where the 64-token tile is used"), and both give
+// bit-identical outputs (section "Same results, bit for bit").
 //
-// Here: MT = 64 weight rows x T tokens per workgroup of 4 waves.  Per K step of
-// KC = 128 weights, each thread decodes one 32-weight unit to fp32 (the exact
-// dequantized value), rounds it to fp16 (nearest even) and writes it to LDS; the
-// activation tile is staged as fp16 beside it.  Wave w then owns weight rows
-// 16w .. 16w+15 and all T tokens: for each 32-deep slice it issues one
-// v_mfma_f32_16x16x32_f16 per 16-token block, accumulating in fp32.
+// On gfx950.  A workgroup of 4 waves owns 64*RB weight rows and a super-tile of
+// TT tokens (64, 128 or 256), made of whole 32- or 64-token tiles: the token
+// tile T is the padding granularity of the last super-tile, the waste the rule
+// above trades against reuse, and TT is the reuse the matrix cores need (a
+// weight decoded costs a few VALU operations, which the 16-cycle
+// v_mfma_f32_16x16x32_f16 only hides when each weight meets >= 128 tokens).
+// Each wave owns 16*RB rows and decodes them straight into the A operand of
+// the MFMA (lane l: row l % 16, weights 8*(l/16) .. +7 of a 32-deep step): the
+// exact fp32 weight, rounded to fp16 nearest-even -- the value the pages stage
+// in threadgroup memory -- kept in registers rather than LDS, since no other
+// wave reads it.  Activations are staged as fp16 in LDS, double buffered over
+// 64-deep K stages, and read as B operands by all four waves; the weight bytes
+// and activations of stage s+1 are fetched while stage s is multiplied.
 //
-// Bit identity of the two tiles: an output (row r, token t) is always produced
-// by the wave owning rows 16*floor((r % 64)/16), in the accumulator of token
-// block floor((t % T)/16), at lane position (r % 16, t % 16), from the same
-// LDS values, over the same K steps in the same order.  Only the number of
-// token blocks per wave differs between T = 32 and T = 64.
+// Bit identity of the tiles: output (row r, token t) is accumulated by the wave
+// owning r, at lane (r % 16, t % 16) of one 16x16 block, from the same fp16
+// operands over the same 32-deep steps in the same order, whatever T, TT and
+// RB are; T only changes how many padding blocks of the last super-tile are
+// computed (and never stored).
 #include <climits>
+#include <type_traits>
 
 #include "decode.hpp"
 #include "internal.hpp"
@@ -32,144 +40,575 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const u8* W;
-  u64 row_bytes;
+  u32 row_bytes;
   int M, nU, K;
   const void* x;
-  int x_f16;
   int N;
   float* y;
-  int n_row_tiles;  // ceil(M / kMT); blockIdx.x = token_tile * n_row_tiles + row_tile
+  int y_vec;        // y rows can take 16-byte stores (M % 4 == 0, y 16-byte aligned)
+  int T;            // token tile (32 or 64)
+  int n_row_tiles;  // blockIdx.x = super_tile * n_row_tiles + row_tile
 };
 
-constexpr int kMT = 64;         // weight rows per workgroup
-constexpr int kKC = 128;        // K per LDS stage (4 units)
-constexpr int kKP = kKC + 8;    // padded LDS row length (halves)
+constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
 
-__device__ __forceinline__ half8 cvt8(const float* f) {
+// LDS slot (in halves) of k-chunk c (8 values) of token row r of a stage buffer:
+// 128-byte rows, chunk index XOR-swizzled by r % 8 so the 16 rows a B-operand
+// read touches fall in distinct bank groups.
+__device__ __forceinline__ int x_slot(int r, int c) { return r * kKS + 8 * (c ^ (r & 7)); }
+
+// ---------------------------------------------------------------------------------------------
+// A operands.  The K order inside a 64-deep stage is permuted so that each lane
+// decodes 16 weights of one unit with one set of coefficients: lane group
+// g = l / 16 takes unit g / 2 of the stage, weights 16(g % 2) .. +15, which feed
+// step j = 0, 1 as k-chunk 2g + j (8 weights).  The activations are read with
+// the same chunk order, so each step is still a sum over 32 distinct K positions
+// and the stage over all 64; every output uses the same order whatever the tile.
+//
+// Codes become fp16 without a conversion per weight: a byte b placed under the
+// exponent byte 0x64 is the fp16 value 1024 + b (ulp 1 in [1024, 2048)), two per
+// v_perm_b32; 1024 + z is then subtracted exactly in packed fp16.  The weight is
+// formed either in packed fp16 -- when d * (q - z) is exact in fp32 and d is an
+// fp16 value, one fp16 rounding of it is the fp16 rounding of the fp32 weight --
+// or with v_fma_mix (fp16 code, fp32 coefficients, fp32 fma rounded to fp16),
+// which rounds the same exact fp32 weight the dequantizer produces.
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2v bits_h2(u32 v) { return __builtin_bit_cast(half2v, v); }
+
+// fp16 pairs (1024 + byte0, 1024 + byte1) and (1024 + byte2, 1024 + byte3) of c
+__device__ __forceinline__ half2v code_pair_lo(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0x64646464u, 0x00050004u)); }
+__device__ __forceinline__ half2v code_pair_hi(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0x64646464u, 0x00070006u)); }
+
+// 8 weights from two code words (4 codes each, in bytes), packed fp16 path:
+// w = (code - zero) * d, with 1024 + zero subtracted exactly first.
+__device__ __forceinline__ half8 weights_pk(u32 c0, u32 c1, half2v off, half2v d) {
+  const half2v p0 = (code_pair_lo(c0) - off) * d;
+  const half2v p1 = (code_pair_hi(c0) - off) * d;
+  const half2v p2 = (code_pair_lo(c1) - off) * d;
+  const half2v p3 = (code_pair_hi(c1) - off) * d;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 8 weights, fp32-coefficient path: w = fp16(fma(code - off, a, b)); off is
+// subtracted exactly in fp16 (or 0 when b already absorbs it).
+template <bool SUB>
+__device__ __forceinline__ half8 weights_mix(u32 c0, u32 c1, half2v off, float a, float b) {
+  half2v p[4] = {code_pair_lo(c0), code_pair_hi(c0), code_pair_lo(c1), code_pair_hi(c1)};
   half8 h;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(f[e]);
+  for (int i = 0; i < 4; ++i) {
+    const half2v q = SUB ? p[i] - off : p[i];
+    h[2 * i] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(q[0]), a, b));
+    h[2 * i + 1] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(q[1]), a, b));
+  }
   return h;
 }
 
-template <int F, int T>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 sW[kMT][kKP];
-  __shared__ __attribute__((aligned(16))) _Float16 sX[T][kKP];
+// Weight bytes are addressed as a 32-bit offset from the matrix base (a matrix
+// is below 4 GiB and its base 16-byte aligned), so the loads take the base from
+// scalar registers and one 32-bit offset per lane.
+__device__ __forceinline__ u32 ld32(const u8* base, u32 off) {
+  return *reinterpret_cast<const u32*>(base + static_cast<u64>(off));
+}
+__device__ __forceinline__ u32 ld16(const u8* base, u32 off) {
+  return *reinterpret_cast<const u16*>(base + static_cast<u64>(off));
+}
+__device__ __forceinline__ uint4 ld128(const u8* base, u32 off) {
+  return *reinterpret_cast<const uint4*>(base + static_cast<u64>(off));
+}
+// 16 bytes at a dword-aligned offset, as one dwordx4 load.
+typedef u32 u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ void ld128_a4(const u8* base, u32 off, u32 (&w)[4]) {
+  const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(base + static_cast<u64>(off));
+  w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+}
+// 16 bytes at base + off (off any alignment) as little-endian words: the dwordx4
+// at the enclosing dword plus the dword holding the last byte (a repeat of the
+// fourth when off is dword aligned), realigned with v_alignbit.  Two loads, no
+// branch, and nothing read past the dword of the range's last byte.
+__device__ __forceinline__ void ld_bytes16(const u8* base, u32 off, u32 (&w)[4]) {
+  u32 raw[4];
+  ld128_a4(base, off & ~3u, raw);
+  const u32 last = ld32(base, (off + 15u) & ~3u);
+  const u32 sh = (off & 3u) * 8u;
+  w[0] = __builtin_amdgcn_alignbit(raw[1], raw[0], sh);
+  w[1] = __builtin_amdgcn_alignbit(raw[2], raw[1], sh);
+  w[2] = __builtin_amdgcn_alignbit(raw[3], raw[2], sh);
+  w[3] = __builtin_amdgcn_alignbit(last, raw[3], sh);
+}
+
+// zero_second(g): the lanes of the stage's second unit get zero coefficients
+// (all-zero weights), for a last stage whose second unit lies past K.
+template <int F> struct AStage;
+
+// Q4_0 (unit = block): weights 16h .. 16h+15 are nibble h of code bytes 0 .. 15.
+template <> struct AStage<FMT_Q4_0> {
+  u32 q[4];
+  u32 d;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
+    const u32 bo = row_off + 18u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
+    ld_bytes16(W, bo + 2, q);
+    d = ld16(W, bo);
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const u32 sh = 4u * static_cast<u32>(g & 1);
+    const half2v dd = bits_h2(d * 0x10001u);
+    const half2v off = half2v{1032, 1032};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      A[j] = weights_pk((q[2 * j] >> sh) & 0x0F0F0F0Fu, (q[2 * j + 1] >> sh) & 0x0F0F0F0Fu, off, dd);
+  }
+};
+
+// Q8_0: weights 16h .. 16h+15 are code bytes 16h .. +15 (int8; ^0x80 gives q + 128).
+template <> struct AStage<FMT_Q8_0> {
+  u32 q[4];
+  u32 d;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
+    const u32 bo = row_off + 34u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
+    ld_bytes16(W, bo + 2 + 16 * (g & 1), q);
+    d = ld16(W, bo);
+  }
+  __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
+    const half2v dd = bits_h2(d * 0x10001u);
+    const half2v off = half2v{1152, 1152};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_pk(q[2 * j] ^ 0x80808080u, q[2 * j + 1] ^ 0x80808080u, off, dd);
+  }
+};
+
+// Q4_K: the stage is sub-blocks 2p (low nibbles) and 2p+1 (high nibbles) of code
+// bytes 32p .. 32p+31; lane group g takes sub-block 2p + g/2, bytes 32p + 16(g%2)
+// .. +15.  A high nibble stays in place (16 * code) and meets a / 16: the product
+// is the same exact fp32 value.
+template <> struct AStage<FMT_Q4_K> {
+  u32 h[4];
+  u32 q[4];
+  int p;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) h[0] = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 so = row_off + 144u * static_cast<u32>(u0 >> 3);
+    p = (u0 >> 1) & 3;
+    const uint4 hv = ld128(W, so);
+    const uint4 qv = ld128(W, so + 16 + 32 * p + 16 * (g & 1));
+    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
+    q[0] = qv.x; q[1] = qv.y; q[2] = qv.z; q[3] = qv.w;
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const u32 hi = static_cast<u32>(g >> 1);
+    // sc_j, m_j (j = 2p + hi): 6-bit fields at bits 6j and 48 + 6j of h[1..3]
+    const u32 bs = 6u * (2u * static_cast<u32>(p) + hi);
+    const u32 s0 = __builtin_amdgcn_alignbit(h[2], h[1], bs & 31u);
+    const u32 s1 = __builtin_amdgcn_alignbit(h[3], h[2], bs & 31u);
+    const u32 sc = (bs < 32 ? s0 : s1) & 63u;
+    const u32 bm = 48u + bs;
+    const u32 m0 = __builtin_amdgcn_alignbit(h[3], h[2], bm & 31u);
+    const u32 m1 = h[3] >> (bm & 31u);
+    const u32 m = (bm < 64 ? m0 : m1) & 63u;
+    const float a = h2f(h[0]) * static_cast<float>(sc) * (hi ? 0.0625f : 1.0f);  // exact
+    const float b = -(h2f(h[0] >> 16) * static_cast<float>(m));                     // exact
+    const u32 mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    const half2v off = half2v{1024, 1024};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_mix<true>(q[2 * j] & mask, q[2 * j + 1] & mask, off, a, b);
+  }
+};
+
+// Q6_K: the stage is units a0, a0+1 (a0 even); lane group g takes unit a = a0 + g/2,
+// weights 16(g%2) .. +15: nibble a/4 of ql[32(a%4) + i] and bits 2(a/2) .. +1 of
+// qh[32(a%2) + i], i = 16(g%2) .. +15, all in sub-block 2a + g%2 (one scale).
+// fma(1024 + q, a, -1056 a) is the exact (q - 32) a rounded once: -1056 a is exact.
+template <> struct AStage<FMT_Q6_K> {
+  u32 ql[4];
+  u32 qh[4];
+  u32 d;
+  u32 sc;
+  int a;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 so = row_off + 210u * static_cast<u32>(u0 >> 3);
+    a = (u0 & 7) + (g >> 1);
+    ld_bytes16(W, so + 18 + 32 * (a & 3) + 16 * (g & 1), ql);
+    ld_bytes16(W, so + 146 + 32 * (a & 1) + 16 * (g & 1), qh);
+    d = ld16(W, so);
+    sc = W[static_cast<u64>(so + 2 + 2 * a + (g & 1))];
+  }
+  __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
+    const u32 lsh = 4u * static_cast<u32>(a >> 2);
+    const u32 hsh = 2u * static_cast<u32>(a >> 1);
+    const float ac = h2f(d) * static_cast<float>(static_cast<int8_t>(sc & 0xFFu));  // exact
+    const float bc = -1056.0f * ac;                                                 // exact
+    u32 c[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c[w] = ((ql[w] >> lsh) & 0x0F0F0F0Fu) | (((qh[w] >> hsh) & 0x03030303u) << 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_mix<false>(c[2 * j], c[2 * j + 1], half2v{0, 0}, ac, bc);
+  }
+};
+
+// A4G64: the stage is one group; lane group g takes nibble g/2 of code bytes
+// 16(g%2) .. +15 (high nibble in place with scale / 16).
+template <> struct AStage<FMT_A4G64> {
+  u32 hdr;
+  u32 q[4];
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) hdr = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 go = row_off + 36u * static_cast<u32>(u0 >> 1);
+    hdr = ld32(W, go);
+    ld128_a4(W, go + 4 + 16 * (g & 1), q);
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const bool hi = (g >> 1) != 0;
+    const float a = h2f(hdr) * (hi ? 0.0625f : 1.0f);  // exact
+    const float b = h2f(hdr >> 16);
+    const u32 mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+    const half2v off = half2v{1024, 1024};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_mix<true>(q[2 * j] & mask, q[2 * j + 1] & mask, off, a, b);
+  }
+};
+
+// ---------------------------------------------------------------------------------------------
+// Activations of one stage: K [k0, k0 + 64) of tokens [tok0, tok0 + TT), as TT*8
+// chunks of 8 values spread over the 256 threads; held in registers from load
+// to store so the global loads stay in flight across the stage's products.
+// fp32 input is rounded to fp16 (nearest even) at store time.  Stored in the
+// natural chunk order; the K permutation of the A operands is applied when the
+// B operands are read.
+template <int TT, bool XF16> struct XStage;
+
+// Loads are unconditional: token rows past N read token N-1 instead (they only
+// feed outputs of tokens that are never stored).  Each lane's chunks sit at fixed
+// 32-bit byte offsets from the super-tile's first row (TT * K * element size is
+// below 4 GiB), the stage's K offset goes into the scalar base.  K past the end
+// (K / 32 odd, last stage) is read clamped and cleared at store time.
+template <int TT, int ES>
+struct XLanes {
+  static constexpr int kChunks = TT * kKS / 8 / 256;
+  u32 off[kChunks];
+  __device__ __forceinline__ void init(int K, int N, int tok0, int tid) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = tid + c * 256;
+      const int row = min(tok0 + (idx >> 3), N - 1) - tok0;
+      off[c] = (static_cast<u32>(row) * static_cast<u32>(K) + 8u * (idx & 7)) * ES;
+    }
+  }
+  // byte offset of chunk c for stage base k0, with the K clamp of a tail stage
+  __device__ __forceinline__ u32 at(int c, int K, int k0, int tid, bool tail) const {
+    if (!tail) return off[c];
+    const int kk = k0 + 8 * ((tid + c * 256) & 7);
+    return off[c] - static_cast<u32>(max(kk - (K - 8), 0)) * ES;
+  }
+};
+
+template <int TT> struct XStage<TT, true> {
+  static constexpr int kChunks = TT * kKS / 8 / 256;
+  half8 v[kChunks];
+  __device__ __forceinline__ void load(const u8* xb, const XLanes<TT, 2>& xl, int K, int k0, int tid, bool tail) {
+    const u8* base = xb + static_cast<u64>(k0) * 2;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      v[c] = *reinterpret_cast<const half8*>(base + static_cast<u64>(xl.at(c, K, k0, tid, tail)));
+  }
+  __device__ __forceinline__ void store(_Float16* sx, int tid) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = tid + c * 256;
+      *reinterpret_cast<half8*>(&sx[x_slot(idx >> 3, idx & 7)]) = v[c];
+    }
+  }
+};
+
+template <int TT> struct XStage<TT, false> {
+  static constexpr int kChunks = TT * kKS / 8 / 256;
+  float4 v[kChunks][2];
+  __device__ __forceinline__ void load(const u8* xb, const XLanes<TT, 4>& xl, int K, int k0, int tid, bool tail) {
+    const u8* base = xb + static_cast<u64>(k0) * 4;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const float4* p = reinterpret_cast<const float4*>(base + static_cast<u64>(xl.at(c, K, k0, tid, tail)));
+      v[c][0] = p[0];
+      v[c][1] = p[1];
+    }
+  }
+  __device__ __forceinline__ void store(_Float16* sx, int tid) const {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = tid + c * 256;
+      const float4 f0 = v[c][0], f1 = v[c][1];
+      *reinterpret_cast<half8*>(&sx[x_slot(idx >> 3, idx & 7)]) =
+          half8{static_cast<_Float16>(f0.x), static_cast<_Float16>(f0.y), static_cast<_Float16>(f0.z),
+                static_cast<_Float16>(f0.w), static_cast<_Float16>(f1.x), static_cast<_Float16>(f1.y),
+                static_cast<_Float16>(f1.z), static_cast<_Float16>(f1.w)};
+    }
+  }
+};
+
+// Clears the K positions [k_end, 64) of a stage buffer (a stage reaching past K).
+template <int TT>
+__device__ __forceinline__ void clear_k_tail(_Float16* sx, int tid, int k_end) {
+  constexpr int kChunks = TT * kKS / 8 / 256;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int idx = tid + c * 256;
+    if (8 * (idx & 7) >= k_end) *reinterpret_cast<half8*>(&sx[x_slot(idx >> 3, idx & 7)]) = half8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// The stage's products: B operands of token block t from LDS (lane: token
+// 16t + l % 16, k-chunks 2g and 2g+1 at offsets o0 and o1 of the block's first
+// row), each used by the wave's RB row blocks.  FULL: all NTB blocks; else only
+// blocks t < ntb (the last super-tile, filled to whole T-token tiles).
+template <bool FULL, int RB, int NTB>
+__device__ __forceinline__ void stage_products(const _Float16* sx, int o0, int o1, const half8 (&A)[RB][2],
+                                               floatx4 (&acc)[RB][NTB], int ntb) {
+#pragma unroll
+  for (int t = 0; t < NTB; ++t) {
+    if (FULL || t < ntb) {
+      const half8 B0 = *reinterpret_cast<const half8*>(sx + 16 * t * kKS + o0);
+      const half8 B1 = *reinterpret_cast<const half8*>(sx + 16 * t * kKS + o1);
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[b][0], B0, acc[b][t], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[b][1], B1, acc[b][t], 0, 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Workgroup barrier for the stage hand-over: the wave's own LDS writes are
+// complete (lgkmcnt 0) before it arrives, so every wave sees the stage's
+// activations after it; global loads in flight (the prefetch of the next two
+// stages) are not waited for, unlike a full __syncthreads() fence.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One workgroup's K loop for token blocks [0, NTB) (FULL) or [0, ntb).  The
+// products of stage s run while the wave decodes the A operands of stage s+1,
+// so the matrix cores and the VALU work side by side within one wave.  Weight
+// bytes are fetched three stages ahead of their products (two ahead of their
+// decode) and activations two ahead: stage s refills the weight set it just
+// decoded with stage s+3, fetches the activations of stage s+2 into registers,
+// and writes those of stage s+1 (fetched during stage s-1) into the other LDS
+// buffer.  Stages are taken two at a time so the register sets swap roles
+// without copies.
+template <int F, int RB, int TT, bool XF16, bool FULL>
+__device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT * kKS], floatx4 (&acc)[RB][TT / 16],
+                                       const u32 (&row_off)[RB], int tok0, int ntb, int o0, int o1, int tid, int g) {
+  const int nstages = (a.nU + 1) >> 1;
+  AStage<F> w0[RB], w1[RB];
+  XStage<TT, XF16> x0, x1;
+  half8 A0[RB][2], A1[RB][2];
+  constexpr int ES = XF16 ? 2 : 4;
+  XLanes<TT, ES> xl;
+  xl.init(a.K, a.N, tok0, tid);
+  const u8* xb = reinterpret_cast<const u8*>(a.x) + static_cast<u64>(tok0) * static_cast<u64>(a.K) * ES;
+
+  // a stage past K (K / 32 odd, last stage) has its activations read clamped and
+  // cleared, and its second unit's weights zeroed; LAST: s may be such a stage
+  auto tail = [&](int s) { return kKS * s + kKS > a.K; };
+  auto fetch_w = [&](int s, AStage<F>(&w)[RB]) {
+#pragma unroll
+    for (int b = 0; b < RB; ++b) w[b].load(a.W, row_off[b], 2 * s, a.nU, g);
+  };
+  auto fetch_x = [&](int s, XStage<TT, XF16>& xs, bool last) { xs.load(xb, xl, a.K, kKS * s, tid, last && tail(s)); };
+  auto put = [&](int s, const XStage<TT, XF16>& xs, bool last) {
+    xs.store(sX[s & 1], tid);
+    if (last && tail(s)) clear_k_tail<TT>(sX[s & 1], tid, a.K - kKS * s);
+  };
+  auto decode = [&](int s, AStage<F>(&w)[RB], half8(&A)[RB][2], bool last) {
+    if (last && 2 * s + 1 == a.nU) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b) w[b].zero_second(g);
+    }
+#pragma unroll
+    for (int b = 0; b < RB; ++b) w[b].operands(g, A[b]);
+  };
+  // stage s: Ac = its A operands, wn = weight set of stage s+1 (decoded into An,
+  // then refilled with s+3), xs = activation set refilled with s+2, xo = stage
+  // s+1.  In the steady state (STEADY) stages s+1 .. s+3 exist and none is the
+  // last, so the step is one branch-free block the scheduler can interleave.
+  auto step = [&](auto steady, int s, AStage<F>(&wn)[RB], half8(&Ac)[RB][2], half8(&An)[RB][2],
+                  XStage<TT, XF16>& xs, const XStage<TT, XF16>& xo) {
+    constexpr bool STEADY = decltype(steady)::value;
+    const bool next = STEADY || s + 1 < nstages;
+    const bool fetch2 = STEADY || s + 2 < nstages;
+    const bool fetch3 = STEADY || s + 3 < nstages;
+    if (next) decode(s + 1, wn, An, !STEADY);
+    if (fetch3) fetch_w(s + 3, wn);
+    if (fetch2) fetch_x(s + 2, xs, !STEADY);
+    stage_products<FULL>(sX[s & 1], o0, o1, Ac, acc, ntb);
+    if (next) {
+      put(s + 1, xo, !STEADY);
+      stage_barrier();
+    }
+  };
+  using steady_t = std::integral_constant<bool, true>;
+  using edge_t = std::integral_constant<bool, false>;
+
+  fetch_w(0, w0);
+  if (nstages > 1) fetch_w(1, w1);
+  fetch_x(0, x0, true);
+  if (nstages > 1) fetch_x(1, x1, true);
+  put(0, x0, true);
+  decode(0, w0, A0, true);
+  if (nstages > 2) fetch_w(2, w0);
+  stage_barrier();
+
+  int s = 0;
+  for (; s + 4 < nstages; s += 2) {
+    step(steady_t{}, s, w1, A0, A1, x0, x1);
+    step(steady_t{}, s + 1, w0, A1, A0, x1, x0);
+  }
+  // at most four stages left, starting with an even one
+  while (s < nstages) {
+    step(edge_t{}, s, w1, A0, A1, x0, x1);
+    if (++s >= nstages) break;
+    step(edge_t{}, s, w0, A1, A0, x1, x0);
+    ++s;
+  }
+}
+
+template <int F, int RB, int TT, bool XF16>
+__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
+  constexpr int NTB = TT / 16;  // 16-token blocks of the super-tile
+  __shared__ __attribute__((aligned(16))) _Float16 sX[2][TT * kKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int row0 = (blockIdx.x % a.n_row_tiles) * kMT;
-  const int tok0 = (blockIdx.x / a.n_row_tiles) * T;
+  const int g = lane >> 4;
+  const int row_tile = blockIdx.x % a.n_row_tiles;
+  const int tok0 = (blockIdx.x / a.n_row_tiles) * TT;
+  const int rw0 = row_tile * (64 * RB) + (tid >> 6) * (16 * RB);  // this wave's first row
 
-  floatx4 acc[T / 16];
-#pragma unroll
-  for (int b = 0; b < T / 16; ++b) acc[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // 16-token blocks computed: whole T-token tiles up to N (at most the super-tile)
+  const int rem = a.N - tok0;
+  const int ntb = rem >= TT ? NTB : ((rem + a.T - 1) / a.T) * (a.T / 16);
 
-  constexpr int kTPT = 256 / T;       // threads per token row of the activation tile
-  constexpr int kHPT = kKC / kTPT;    // halves per thread (32 or 16)
-
-  for (int u0 = 0; u0 < a.nU; u0 += kKC / 32) {
-    // weights: thread -> (row tid/4, unit u0 + tid%4)
-    {
-      const int r = tid >> 2;
-      const int uu = tid & 3;
-      const int row = row0 + r;
-      const int u = u0 + uu;
-      half8* dst = reinterpret_cast<half8*>(&sW[r][32 * uu]);
-      if (row < a.M && u < a.nU) {
-        float w[32];
-        decode_unit<F>(a.W, static_cast<u32>(row) * static_cast<u32>(a.row_bytes), u, w);
+  u32 row_off[RB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = cvt8(&w[8 * j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-    // activations: thread -> (token tid/kTPT, halves [c*kHPT, (c+1)*kHPT))
-    {
-      const int t = tid / kTPT;
-      const int c = tid % kTPT;
-      const int tok = tok0 + t;
-      const int kb = 32 * u0 + c * kHPT;
-#pragma unroll
-      for (int h = 0; h < kHPT / 8; ++h) {
-        const int k = kb + 8 * h;
-        half8 v = half8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (tok < a.N && k < a.K) {
-          if (a.x_f16) {
-            v = *reinterpret_cast<const half8*>(reinterpret_cast<const _Float16*>(a.x) + (u64)tok * a.K + k);
-          } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + (u64)tok * a.K + k);
-            const float4 f0 = p[0], f1 = p[1];
-            const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-            v = cvt8(f);
-          }
-        }
-        *reinterpret_cast<half8*>(&sX[t][c * kHPT + 8 * h]) = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kKC / 32; ++ks) {
-      const half8 A = *reinterpret_cast<const half8*>(&sW[16 * wave + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int b = 0; b < T / 16; ++b) {
-        const half8 B = *reinterpret_cast<const half8*>(&sX[16 * b + (lane & 15)][32 * ks + 8 * (lane >> 4)]);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, acc[b], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int b = 0; b < RB; ++b) {
+    const int r = rw0 + 16 * b + (lane & 15);
+    row_off[b] = static_cast<u32>(r < a.M ? r : a.M - 1) * a.row_bytes;
   }
+  // B-operand offsets of this lane within a token block: token row l % 16,
+  // k-chunks 2g (step 0) and 2g + 1 (step 1)
+  const int o0 = x_slot(lane & 15, 2 * g);
+  const int o1 = x_slot(lane & 15, 2 * g + 1);
 
-  // D[i][j] of a 16x16 block sits in lane j + 16*(i/4), element i%4.
+  floatx4 acc[RB][NTB];
 #pragma unroll
-  for (int b = 0; b < T / 16; ++b) {
-    const int tok = tok0 + 16 * b + (lane & 15);
+  for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row0 + 16 * wave + 4 * (lane >> 4) + v;
-      if (tok < a.N && row < a.M) a.y[(u64)tok * a.M + row] = acc[b][v];
+    for (int t = 0; t < NTB; ++t) acc[b][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (ntb == NTB)
+    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g);
+  else
+    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g);
+
+  // D[4*(l/16) + v][l % 16] of block (b, t): row rw0 + 16b + 4g + v, token tok0 + 16t + l % 16
+#pragma unroll
+  for (int t = 0; t < NTB; ++t) {
+    const int tok = tok0 + 16 * t + (lane & 15);
+    if (t < ntb && tok < a.N) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int r = rw0 + 16 * b + 4 * g;
+        float* yp = a.y + (u64)tok * a.M + r;
+        if (a.y_vec && r + 3 < a.M) {
+          *reinterpret_cast<float4*>(yp) = make_float4(acc[b][t][0], acc[b][t][1], acc[b][t][2], acc[b][t][3]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (r + v < a.M) yp[v] = acc[b][t][v];
+        }
+      }
     }
   }
 }
 
 namespace {
 typedef void (*GemmKernel)(GemmArgs);
-template <int F>
-GemmKernel pick(int T) {
-  return T == 64 ? k_gemm<F, 64> : k_gemm<F, 32>;
+
+// Workgroup shapes (RB, TT): 128 rows x 128 tokens, 64 x 128 and 64 x 64.  The
+// first two amortise each decoded weight over 128 tokens; the last gives small
+// problems more workgroups.  Q6_K's raw bytes and fp32 activations leave no room
+// for the 128 x 128 shape within 256 registers per lane.
+constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
+  if (RB == 2) return TT == 128 && F != FMT_Q6_K && (xf16 || F != FMT_Q4_K);
+  return TT == 64 || TT == 128;
 }
+
+template <int F, bool XF16, int RB, int TT>
+GemmKernel kernel_if_ok() {
+  if constexpr (shape_ok(F, XF16, RB, TT)) return k_gemm<F, RB, TT, XF16>;
+  return nullptr;
+}
+
+template <int F>
+GemmKernel pick(int RB, int TT, bool xf16) {
+  if (xf16) return RB == 2 ? kernel_if_ok<F, true, 2, 128>() : TT == 128 ? kernel_if_ok<F, true, 1, 128>() : kernel_if_ok<F, true, 1, 64>();
+  return RB == 2 ? kernel_if_ok<F, false, 2, 128>() : TT == 128 ? kernel_if_ok<F, false, 1, 128>() : kernel_if_ok<F, false, 1, 64>();
+}
+
+constexpr int64_t kCUs = 256;
 }  // namespace
 
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile,
                        hipStream_t st) {
   GemmArgs a{};
   a.W = m.blocks;
-  a.row_bytes = m.row_bytes;
+  a.row_bytes = static_cast<u32>(m.row_bytes);
   a.M = static_cast<int>(m.M);
   a.nU = static_cast<int>(m.K / 32);
   a.K = static_cast<int>(m.K);
   a.x = x;
-  a.x_f16 = x_f16;
   a.N = static_cast<int>(N);
   a.y = y;
+  a.y_vec = (m.M % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
+  a.T = tile;
+  // Rows x tokens per workgroup: the first shape, in order of decreasing reuse,
+  // that gives two workgroups per CU (one for Q6_K, whose wider decode favours
+  // reuse over parallelism), else 64 x 64.  Measured on the decode-layer shapes.
+  const int64_t padded = (N + tile - 1) / tile * tile;
+  auto wgs = [&](int rb, int tt) { return ((m.M + 64 * rb - 1) / (64 * rb)) * ((padded + tt - 1) / tt); };
+  static const int kShapes[3][2] = {{2, 128}, {1, 128}, {1, 64}};
+  const int64_t want = m.fmt == FMT_Q6_K ? kCUs : 2 * kCUs;
+  const bool xf16 = x_f16 != 0;
+  int RB = 1, TT = 64;
+  for (const auto& c : kShapes) {
+    if (!shape_ok(m.fmt, xf16, c[0], c[1])) continue;
+    if (c[1] > 64 && padded <= c[1] / 2) continue;  // a super-tile at most half used
+    if (wgs(c[0], c[1]) >= want) {
+      RB = c[0];
+      TT = c[1];
+      break;
+    }
+  }
   GemmKernel k = nullptr;
   switch (m.fmt) {
-    case FMT_Q4_0: k = pick<FMT_Q4_0>(tile); break;
-    case FMT_Q8_0: k = pick<FMT_Q8_0>(tile); break;
-    case FMT_Q4_K: k = pick<FMT_Q4_K>(tile); break;
-    case FMT_Q6_K: k = pick<FMT_Q6_K>(tile); break;
-    case FMT_A4G64: k = pick<FMT_A4G64>(tile); break;
+    case FMT_Q4_0: k = pick<FMT_Q4_0>(RB, TT, xf16); break;
+    case FMT_Q8_0: k = pick<FMT_Q8_0>(RB, TT, xf16); break;
+    case FMT_Q4_K: k = pick<FMT_Q4_K>(RB, TT, xf16); break;
+    case FMT_Q6_K: k = pick<FMT_Q6_K>(RB, TT, xf16); break;
+    case FMT_A4G64: k = pick<FMT_A4G64>(RB, TT, xf16); break;
     default: return hipErrorInvalidValue;
   }
-  a.n_row_tiles = static_cast<int>((m.M + kMT - 1) / kMT);
-  const int64_t blocks = static_cast<int64_t>(a.n_row_tiles) * ((N + tile - 1) / tile);
+  if (!k) return hipErrorInvalidValue;
+  a.n_row_tiles = static_cast<int>((m.M + 64 * RB - 1) / (64 * RB));
+  const int64_t blocks = static_cast<int64_t>(a.n_row_tiles) * ((N + TT - 1) / TT);
   if (blocks > INT_MAX) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,9 @@ struct MatDesc {
 constexpr int64_t kMaxExperts = 8192;
 constexpr int64_t kMaxGemvTokens = 32;
 constexpr int64_t kMaxSlots = 64;
+// The matrix-matrix path addresses a 256-token slab of fp32 activations with
+// 32-bit offsets: K * 4 bytes * 256 must stay below 4 GiB.
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 
 hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f16, hipStream_t s);
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);

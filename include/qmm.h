@@ -135,6 +135,7 @@ qmm_status qmm_gemv(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
  *   x     DEVICE, [N, K] contiguous fp32 or fp16, 16-byte aligned; fp32 values are
  *         rounded to fp16 (nearest even) when staged.
  *   N     >= 0; a batch of sequences is passed flattened (N = batch * tokens).
+ *         The handle's K must be below 2^22 (QMM_E_SHAPE otherwise).
  *   y     DEVICE, [N, M] fp32, 4-byte aligned.
  *   tile  QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64.  Results are bit-identical
  *         for either tile: every output is accumulated in the same order.

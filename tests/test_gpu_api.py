@@ -64,6 +64,14 @@ def test_call_errors():
     assert L.lib.qmm_gemv(stack.handle, xp, 0, 1, yp, s) == -1   # dense call on a stack
     with pytest.raises(q.QmmError):
         qm.gemv(torch.zeros((33, K), device="cuda"))
+    # the matrix-matrix path takes K below 2^22; the check comes before any launch,
+    # so the (too small) block buffer is never read
+    wide = ctypes.c_void_p()
+    blk = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    assert L.lib.qmm_create(ctypes.byref(wide), 0, ctypes.c_void_p(blk.data_ptr()), 1, 1, 1 << 22) == 0
+    assert L.lib.qmm_gemm(wide, xp, 0, 1, yp, 0, s) == -3
+    assert "K below" in L.lib.qmm_last_error().decode()
+    assert L.lib.qmm_destroy(wide) == 0
 
 
 def test_stream_order_on_side_stream():
