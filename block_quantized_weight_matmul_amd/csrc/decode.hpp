@@ -62,25 +62,31 @@ __device__ __forceinline__ u16 load_u16(const u8* p) {
   return *reinterpret_cast<const u16*>(p);
 }
 
-// The NBYTES bytes at `src` (any alignment) as (NBYTES+3)/4 little-endian words,
-// word j holding bytes src[4j .. 4j+3]: the enclosing dword-aligned words are
-// loaded and realigned with v_alignbit.  Reads only dwords that contain at least
-// one byte of the range, so it never touches memory past the range's last dword.
+// NBYTES bytes at any alignment (NBYTES a multiple of 4), kept as the enclosing
+// dword-aligned words and realigned with v_alignbit only when read: load() only
+// issues loads, so the realignment -- and the wait for the data -- comes where
+// the words are used.  The last load is the dword holding the range's last byte
+// (a repeat of the one before it when src is dword aligned), so nothing past
+// that dword is read and no branch guards a load.
 template <int NBYTES>
-__device__ __forceinline__ void load_bytes(const u8* src, u32 (&w)[(NBYTES + 3) / 4]) {
-  constexpr int NW = (NBYTES + 3) / 4;
-  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
-  const u32* p = reinterpret_cast<const u32*>(a & ~static_cast<uintptr_t>(3));
-  const u32 sh = static_cast<u32>(a & 3u) * 8u;
+struct RawBytes {
+  static_assert(NBYTES % 4 == 0, "whole words");
+  static constexpr int NW = NBYTES / 4;
   u32 raw[NW + 1];
+  u32 sh;
+  __device__ __forceinline__ void load(const u8* src) {
+    // pointer arithmetic (not integer casts) keeps the global address space
+    // known, so these stay global loads rather than flat ones
+    const u32 mis = static_cast<u32>(reinterpret_cast<uintptr_t>(src) & 3u);
+    const u32* p = reinterpret_cast<const u32*>(src - mis);
+    sh = mis * 8u;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) raw[i] = p[i];
-  // the (NW+1)-th dword is needed only when the range is not dword aligned
-  const u32 last = static_cast<u32>(((a + NBYTES - 1) >> 2) - (a >> 2));
-  raw[NW] = (last >= static_cast<u32>(NW)) ? p[NW] : 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
-}
+    for (int i = 0; i < NW; ++i) raw[i] = p[i];
+    raw[NW] = p[(mis + NBYTES - 1) >> 2];
+  }
+  // bytes src[4j .. 4j+3] as a little-endian word
+  __device__ __forceinline__ u32 word(int j) const { return __builtin_amdgcn_alignbit(raw[j + 1], raw[j], sh); }
+};
 
 // A decoded unit: 32 codes in 8 words, and w_k = fma(code_k, a, b) where the
 // coefficient pair may change once, at weight 16 (Q6_K's two sub-blocks).
@@ -110,17 +116,18 @@ template <int F> struct Decoder;
 // Q4_0: block u; weight i (0..15) low nibble of qs[i], weight 16+i high nibble.
 template <> struct Decoder<FMT_Q4_0> {
   static constexpr float kCodeBias = 0.0f;
-  struct Raw { u32 q[4]; u32 d; };
+  struct Raw { RawBytes<16> q; u32 d; };
   __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
     const u32 bo = row_off + 18u * u;
-    load_bytes<16>(base + bo + 2, r.q);
+    r.q.load(base + bo + 2);
     r.d = load_u16(base + bo);
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      o.c[j] = r.q[j] & 0x0F0F0F0Fu;             // weights 4j .. 4j+3
-      o.c[4 + j] = (r.q[j] >> 4) & 0x0F0F0F0Fu;  // weights 16+4j .. 16+4j+3
+      const u32 q = r.q.word(j);
+      o.c[j] = q & 0x0F0F0F0Fu;             // weights 4j .. 4j+3
+      o.c[4 + j] = (q >> 4) & 0x0F0F0F0Fu;  // weights 16+4j .. 16+4j+3
     }
     const float d = h2f(r.d);
     o.a0 = o.a1 = d;
@@ -131,15 +138,15 @@ template <> struct Decoder<FMT_Q4_0> {
 // Q8_0: block u; int8 codes, biased by 128 so they convert as unsigned bytes.
 template <> struct Decoder<FMT_Q8_0> {
   static constexpr float kCodeBias = 128.0f;  // code - 128 is the signed q
-  struct Raw { u32 q[8]; u32 d; };
+  struct Raw { RawBytes<32> q; u32 d; };
   __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
     const u32 bo = row_off + 34u * u;
-    load_bytes<32>(base + bo + 2, r.q);
+    r.q.load(base + bo + 2);
     r.d = load_u16(base + bo);
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o.c[j] = r.q[j] ^ 0x80808080u;
+    for (int j = 0; j < 8; ++j) o.c[j] = r.q.word(j) ^ 0x80808080u;
     const float d = h2f(r.d);
     o.a0 = o.a1 = d;
     o.b0 = o.b1 = 0.0f;
@@ -197,12 +204,12 @@ template <> struct Decoder<FMT_Q4_K> {
 // 2*(a/2) .. +1 of qh[32*(a%2) + i].
 template <> struct Decoder<FMT_Q6_K> {
   static constexpr float kCodeBias = 0.0f;
-  struct Raw { u32 ql[8]; u32 qh[8]; u32 d; u32 sc; int a; };
+  struct Raw { RawBytes<32> ql, qh; u32 d; u32 sc; int a; };
   __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
     const u32 so = row_off + 210u * (u >> 3);
     r.a = u & 7;
-    load_bytes<32>(base + so + 18 + 32 * (r.a & 3), r.ql);
-    load_bytes<32>(base + so + 146 + 32 * (r.a & 1), r.qh);
+    r.ql.load(base + so + 18 + 32 * (r.a & 3));
+    r.qh.load(base + so + 146 + 32 * (r.a & 1));
     r.d = load_u16(base + so);
     r.sc = load_u16(base + so + 2 + 2 * r.a);
   }
@@ -211,7 +218,7 @@ template <> struct Decoder<FMT_Q6_K> {
     const u32 hsh = 2u * static_cast<u32>(r.a >> 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      o.c[k] = ((r.ql[k] >> lsh) & 0x0F0F0F0Fu) | (((r.qh[k] >> hsh) & 0x03030303u) << 4);
+      o.c[k] = ((r.ql.word(k) >> lsh) & 0x0F0F0F0Fu) | (((r.qh.word(k) >> hsh) & 0x03030303u) << 4);
     const float d = h2f(r.d);
     const float s0 = static_cast<float>(static_cast<int8_t>(r.sc & 0xFFu));
     const float s1 = static_cast<float>(static_cast<int8_t>((r.sc >> 8) & 0xFFu));
@@ -362,13 +369,13 @@ template <> struct Item<FMT_Q4_K> {
 
 template <> struct Item<FMT_Q6_K> {
   static constexpr int RUNS = 2;
-  struct Raw { u32 ql[8]; u32 qh[8]; u32 d; u32 sc0, sc1; int a; };
+  struct Raw { RawBytes<32> ql, qh; u32 d; u32 sc0, sc1; int a; };
   __device__ __forceinline__ static int unit(int i, int run) { return 8 * (i >> 2) + (i & 3) + 4 * run; }
   __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
     const u32 so = row_off + 210u * static_cast<u32>(i >> 2);
     r.a = i & 3;
-    load_bytes<32>(base + so + 18 + 32 * r.a, r.ql);
-    load_bytes<32>(base + so + 146 + 32 * (r.a & 1), r.qh);
+    r.ql.load(base + so + 18 + 32 * r.a);
+    r.qh.load(base + so + 146 + 32 * (r.a & 1));
     r.d = load_u16(base + so);
     r.sc0 = load_u16(base + so + 2 + 2 * r.a);    // sub-blocks 2a, 2a+1
     r.sc1 = load_u16(base + so + 10 + 2 * r.a);   // sub-blocks 2a+8, 2a+9
@@ -377,8 +384,9 @@ template <> struct Item<FMT_Q6_K> {
     const u32 hs = 2u * static_cast<u32>(r.a >> 1);  // run a: bits hs, run a+4: bits hs+4
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      o[0].c[k] = (r.ql[k] & 0x0F0F0F0Fu) | (((r.qh[k] >> hs) & 0x03030303u) << 4);
-      o[1].c[k] = ((r.ql[k] >> 4) & 0x0F0F0F0Fu) | (((r.qh[k] >> (hs + 4)) & 0x03030303u) << 4);
+      const u32 ql = r.ql.word(k), qh = r.qh.word(k);
+      o[0].c[k] = (ql & 0x0F0F0F0Fu) | (((qh >> hs) & 0x03030303u) << 4);
+      o[1].c[k] = ((ql >> 4) & 0x0F0F0F0Fu) | (((qh >> (hs + 4)) & 0x03030303u) << 4);
     }
     const float d = h2f(r.d);
     const u32 sc[2] = {r.sc0, r.sc1};

@@ -124,20 +124,23 @@ __device__ __forceinline__ void ld128_a4(const u8* base, u32 off, u32 (&w)[4]) {
   const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(base + static_cast<u64>(off));
   w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
 }
-// 16 bytes at base + off (off any alignment) as little-endian words: the dwordx4
-// at the enclosing dword plus the dword holding the last byte (a repeat of the
-// fourth when off is dword aligned), realigned with v_alignbit.  Two loads, no
-// branch, and nothing read past the dword of the range's last byte.
-__device__ __forceinline__ void ld_bytes16(const u8* base, u32 off, u32 (&w)[4]) {
-  u32 raw[4];
-  ld128_a4(base, off & ~3u, raw);
-  const u32 last = ld32(base, (off + 15u) & ~3u);
-  const u32 sh = (off & 3u) * 8u;
-  w[0] = __builtin_amdgcn_alignbit(raw[1], raw[0], sh);
-  w[1] = __builtin_amdgcn_alignbit(raw[2], raw[1], sh);
-  w[2] = __builtin_amdgcn_alignbit(raw[3], raw[2], sh);
-  w[3] = __builtin_amdgcn_alignbit(last, raw[3], sh);
-}
+// 16 bytes at base + off (off any alignment): the dwordx4 at the enclosing dword
+// plus the dword holding the last byte (a repeat of the fourth when off is
+// dword aligned), kept raw and realigned with v_alignbit when read, so the wait
+// for the data comes where the words are used.  Two loads, no branch, nothing
+// read past the dword of the range's last byte.
+struct Bytes16 {
+  u32 raw[5];
+  u32 sh;
+  __device__ __forceinline__ void load(const u8* base, u32 off) {
+    u32 v[4];
+    ld128_a4(base, off & ~3u, v);
+    raw[0] = v[0]; raw[1] = v[1]; raw[2] = v[2]; raw[3] = v[3];
+    raw[4] = ld32(base, (off + 15u) & ~3u);
+    sh = (off & 3u) * 8u;
+  }
+  __device__ __forceinline__ u32 word(int j) const { return __builtin_amdgcn_alignbit(raw[j + 1], raw[j], sh); }
+};
 
 // zero_second(g): the lanes of the stage's second unit get zero coefficients
 // (all-zero weights), for a last stage whose second unit lies past K.
@@ -145,12 +148,12 @@ template <int F> struct AStage;
 
 // Q4_0 (unit = block): weights 16h .. 16h+15 are nibble h of code bytes 0 .. 15.
 template <> struct AStage<FMT_Q4_0> {
-  u32 q[4];
+  Bytes16 q;
   u32 d;
   __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
   __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
     const u32 bo = row_off + 18u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
-    ld_bytes16(W, bo + 2, q);
+    q.load(W, bo + 2);
     d = ld16(W, bo);
   }
   __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
@@ -159,25 +162,25 @@ template <> struct AStage<FMT_Q4_0> {
     const half2v off = half2v{1032, 1032};
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      A[j] = weights_pk((q[2 * j] >> sh) & 0x0F0F0F0Fu, (q[2 * j + 1] >> sh) & 0x0F0F0F0Fu, off, dd);
+      A[j] = weights_pk((q.word(2 * j) >> sh) & 0x0F0F0F0Fu, (q.word(2 * j + 1) >> sh) & 0x0F0F0F0Fu, off, dd);
   }
 };
 
 // Q8_0: weights 16h .. 16h+15 are code bytes 16h .. +15 (int8; ^0x80 gives q + 128).
 template <> struct AStage<FMT_Q8_0> {
-  u32 q[4];
+  Bytes16 q;
   u32 d;
   __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
   __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
     const u32 bo = row_off + 34u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
-    ld_bytes16(W, bo + 2 + 16 * (g & 1), q);
+    q.load(W, bo + 2 + 16 * (g & 1));
     d = ld16(W, bo);
   }
   __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
     const half2v dd = bits_h2(d * 0x10001u);
     const half2v off = half2v{1152, 1152};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) A[j] = weights_pk(q[2 * j] ^ 0x80808080u, q[2 * j + 1] ^ 0x80808080u, off, dd);
+    for (int j = 0; j < 2; ++j) A[j] = weights_pk(q.word(2 * j) ^ 0x80808080u, q.word(2 * j + 1) ^ 0x80808080u, off, dd);
   }
 };
 
@@ -223,8 +226,8 @@ template <> struct AStage<FMT_Q4_K> {
 // qh[32(a%2) + i], i = 16(g%2) .. +15, all in sub-block 2a + g%2 (one scale).
 // fma(1024 + q, a, -1056 a) is the exact (q - 32) a rounded once: -1056 a is exact.
 template <> struct AStage<FMT_Q6_K> {
-  u32 ql[4];
-  u32 qh[4];
+  Bytes16 ql;
+  Bytes16 qh;
   u32 d;
   u32 sc;
   int a;
@@ -232,8 +235,8 @@ template <> struct AStage<FMT_Q6_K> {
   __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
     const u32 so = row_off + 210u * static_cast<u32>(u0 >> 3);
     a = (u0 & 7) + (g >> 1);
-    ld_bytes16(W, so + 18 + 32 * (a & 3) + 16 * (g & 1), ql);
-    ld_bytes16(W, so + 146 + 32 * (a & 1) + 16 * (g & 1), qh);
+    ql.load(W, so + 18 + 32 * (a & 3) + 16 * (g & 1));
+    qh.load(W, so + 146 + 32 * (a & 1) + 16 * (g & 1));
     d = ld16(W, so);
     sc = W[static_cast<u64>(so + 2 + 2 * a + (g & 1))];
   }
@@ -244,7 +247,8 @@ template <> struct AStage<FMT_Q6_K> {
     const float bc = -1056.0f * ac;                                                 // exact
     u32 c[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) c[w] = ((ql[w] >> lsh) & 0x0F0F0F0Fu) | (((qh[w] >> hsh) & 0x03030303u) << 4);
+    for (int w = 0; w < 4; ++w)
+      c[w] = ((ql.word(w) >> lsh) & 0x0F0F0F0Fu) | (((qh.word(w) >> hsh) & 0x03030303u) << 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) A[j] = weights_mix<false>(c[2 * j], c[2 * j + 1], half2v{0, 0}, ac, bc);
   }
@@ -542,10 +546,11 @@ typedef void (*GemmKernel)(GemmArgs);
 
 // Workgroup shapes (RB, TT): 128 rows x 128 tokens, 64 x 128 and 64 x 64.  The
 // first two amortise each decoded weight over 128 tokens; the last gives small
-// problems more workgroups.  Q6_K's raw bytes and fp32 activations leave no room
-// for the 128 x 128 shape within 256 registers per lane.
+// problems more workgroups.  Q6_K's raw bytes and fp32 activations (held twice
+// as wide while in flight) leave no room for the 128 x 128 shape within 256
+// registers per lane.
 constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
-  if (RB == 2) return TT == 128 && F != FMT_Q6_K && (xf16 || F != FMT_Q4_K);
+  if (RB == 2) return TT == 128 && F != FMT_Q6_K && xf16;
   return TT == 64 || TT == 128;
 }
 

@@ -101,6 +101,15 @@ __host__ __device__ constexpr int lds_floats(int NB, int KC, int RW, int nU) {
   return NB * KC * (kXStride + 2) + NB * RW * nU;
 }
 
+// The sum of 16 activations as a balanced pairwise tree: ((e0+e1)+(e2+e3)) for
+// each group of four, then the groups pairwise.  Both staging routines form
+// exactly this tree, so every path sees the same half sums.
+__device__ __forceinline__ float sum4(float a, float b, float c, float d) { return (a + b) + (c + d); }
+__device__ __forceinline__ float half_sum16(const float* p) {
+  return (sum4(p[0], p[1], p[2], p[3]) + sum4(p[4], p[5], p[6], p[7])) +
+         (sum4(p[8], p[9], p[10], p[11]) + sum4(p[12], p[13], p[14], p[15]));
+}
+
 // Stage activations of units [c0, c0 + cw) of tokens t < ntok as fp32, then the
 // sum of each 16-activation half (fixed order).  Ends with a barrier.
 __device__ __forceinline__ void stage_x(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0,
@@ -129,11 +138,88 @@ __device__ __forceinline__ void stage_x(const void* x, int x_f16, int K, const T
     const int rem = idx - t * cw * 2;
     const int uu = rem >> 1;
     const int h = rem & 1;
-    const float* p = &s_x[(t * KC + uu) * kXStride + 16 * h];
-    float s = p[0];
+    s_sx[(t * KC + uu) * 2 + h] = half_sum16(&s_x[(t * KC + uu) * kXStride + 16 * h]);
+  }
+  __syncthreads();
+}
+
+// The activation chunk can instead pass through registers: x_load issues its
+// global loads (kXRegs 16-byte slots per thread, 4 fp32 or 8 fp16 activations
+// each; slot indices past the chunk are clamped, so the loads carry no branch)
+// and x_put converts, writes them to LDS and forms the half sums with DPP.  A
+// caller issues x_load before the weight loads: global loads retire in order for
+// s_waitcnt, so the LDS store then waits for the activations only and the weight
+// bytes stay in flight while they are staged.
+constexpr int kXRegs = 8;
+struct XRegs {
+  uint4 v[kXRegs];
+};
+
+__device__ __forceinline__ int x_slots_per_unit(int x_f16) { return x_f16 ? 4 : 8; }
+
+__device__ __forceinline__ bool x_fits_regs(int x_f16, int ntok, int cw) {
+  return ntok * cw * x_slots_per_unit(x_f16) <= kXRegs * (int)blockDim.x;
+}
+
+__device__ __forceinline__ void x_load(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0, int cw,
+                                       XRegs& r) {
+  const int spu = x_slots_per_unit(x_f16);
+  const int es = x_f16 ? 2 : 4;
+  const int per_tok = cw * spu;
+  const int total = ntok * per_tok;
+  const u8* xb = reinterpret_cast<const u8*>(x);
 #pragma unroll
-    for (int i = 1; i < 16; ++i) s += p[i];
-    s_sx[(t * KC + uu) * 2 + h] = s;
+  for (int j = 0; j < kXRegs; ++j) {
+    if (j * static_cast<int>(blockDim.x) < total) {  // uniform: slot rounds the chunk needs
+      const int idx = min(static_cast<int>(threadIdx.x + j * blockDim.x), total - 1);
+      const int t = idx / per_tok;
+      const int rem = idx - t * per_tok;
+      const int uu = rem / spu;
+      const u64 off = ((u64)tm.x(t) * K + 32 * (c0 + uu)) * es + 16 * (rem - uu * spu);
+      r.v[j] = *reinterpret_cast<const uint4*>(xb + off);
+    }
+  }
+}
+
+__device__ __forceinline__ void x_put(const XRegs& r, int x_f16, int ntok, int cw, int KC, float* s_x,
+                                      float* s_sx) {
+  const int spu = x_slots_per_unit(x_f16);
+  const int per_tok = cw * spu;
+  const int total = ntok * per_tok;
+#pragma unroll
+  for (int j = 0; j < kXRegs; ++j) {
+    if (j * static_cast<int>(blockDim.x) >= total) break;  // uniform
+    const int idx = threadIdx.x + j * blockDim.x;
+    const int ic = min(idx, total - 1);
+    const int t = ic / per_tok;
+    const int rem = ic - t * per_tok;
+    const int uu = rem / spu;
+    const int q = rem - uu * spu;
+    float* dst = &s_x[(t * KC + uu) * kXStride];
+    float hs;
+    if (x_f16) {
+      // 8 activations; a half is two slots (lanes 2k, 2k+1)
+      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+      const h8 h = __builtin_bit_cast(h8, r.v[j]);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = static_cast<float>(h[e]);
+      if (idx < total) {
+        *reinterpret_cast<float4*>(dst + 8 * q) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(dst + 8 * q + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+      hs = sum4(f[0], f[1], f[2], f[3]) + sum4(f[4], f[5], f[6], f[7]);
+      hs += dpp_mov<0xB1>(hs);  // + slot of lane ^ 1
+    } else {
+      // 4 activations; a half is four slots (lanes 4k .. 4k+3)
+      const float4 v = __builtin_bit_cast(float4, r.v[j]);
+      if (idx < total) *reinterpret_cast<float4*>(dst + 4 * q) = v;
+      hs = sum4(v.x, v.y, v.z, v.w);
+      hs += dpp_mov<0xB1>(hs);  // lane ^ 1
+      hs += dpp_mov<0x4E>(hs);  // lane ^ 2
+    }
+    // the first slot of each half writes its sum
+    if (idx < total && (q & (spu / 2 - 1)) == 0) s_sx[(t * KC + uu) * 2 + q / (spu / 2)] = hs;
   }
   __syncthreads();
 }
@@ -166,26 +252,64 @@ __device__ __forceinline__ float item_partial(const Unit& o, const float (&q)[32
   }
 }
 
-// Items per thread per batch: a thread issues the loads of all its items of a
-// batch before decoding any (the host sizes workgroups so that one batch
-// usually covers the whole slice).
-constexpr int ipt_max(int NB) { return NB <= 8 ? 4 : (NB <= 16 ? 3 : 2); }
+// Output (row r, token t) of a workgroup = the sum of its units' partials
+// part[(t * RW + r) * nU + u]: 16 lanes per output, lane j adding units j, j+16,
+// ... in order, then a butterfly over the 16 lanes (DPP within a row of the
+// wave).  Every path ends with this, in this order, so results do not depend on
+// the launch shape and the dense and expert-indexed paths agree bit for bit.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_mov<0xB1>(v);   // lane ^ 1
+  v += dpp_mov<0x4E>(v);   // lane ^ 2
+  v += dpp_mov<0x141>(v);  // row_half_mirror: the other quad of the 8
+  v += dpp_mov<0x140>(v);  // row_mirror: the other 8 of the 16
+  return v;
+}
+
+__device__ __forceinline__ void reduce_rows(const float* s_part, int rows, int ntok, int nU, int RW, int M, int r0,
+                                            const TokMap& tm, float* y) {
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4, j = tid & 15, ngrp = blockDim.x >> 4;
+  for (int o = grp; o < rows * ntok; o += ngrp) {
+    const int row = o / ntok, t = o - row * ntok;
+    const float* pp = s_part + (t * RW + row) * nU;
+    float v = 0.0f;
+    for (int u = j; u < nU; u += 16) v += pp[u];
+    v = sum16(v);
+    if (j == 0) y[(u64)tm.y(t) * M + r0 + row] = v;
+  }
+}
+
+// Items per thread per batch.  A thread holds two batches: while it decodes one,
+// the loads of the next are in flight.
+// Q6_K items carry 34 raw bytes and two scale pairs, so it holds fewer.
+template <int F>
+constexpr int ipt_max(int NB) {
+  if (F == FMT_Q6_K) return NB <= 8 ? 2 : 1;
+  return NB <= 8 ? 3 : (NB <= 16 ? 2 : 1);
+}
 
 // Rows [r0, r0 + rows) of the matrix at W (rows <= RW), all tokens t < ntok.
 // Byte offsets within one matrix fit 32 bits (checked by the host).  KC is a
 // multiple of 8 units, so chunk boundaries never split an item's runs.
-template <int F, int NB>
+template <int F, int NB, bool XR>
 __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, int K, int r0, int rows, int RW,
                                           int KC, const void* x, int x_f16, const TokMap& tm, int ntok, float* y,
                                           float* lds) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
-  constexpr int kIpt = ipt_max(NB);
+  constexpr int kIpt = ipt_max<F>(NB);
   float* s_x = lds;
   float* s_sx = s_x + NB * KC * kXStride;
   float* s_part = s_sx + NB * KC * 2;
   const int T = blockDim.x;
   const int tid = threadIdx.x;
+
+  // A batch: this thread's items b0 + tid + j*T (j < n) of the chunk's item list.
+  struct Batch {
+    typename It::Raw raw[kIpt];
+    int irow[kIpt], iit[kIpt];
+    int n;
+  };
 
   for (int c0 = 0; c0 < nU; c0 += KC) {
     const int cw = min(KC, nU - c0);
@@ -193,35 +317,36 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
     const int i0 = c0 / RUNS;         // first item of the chunk
     const int items = rows * ipr;
     const int drow = T / ipr, di = T - drow * ipr;  // item index step T as (rows, items)
-    for (int b0 = 0; b0 < items; b0 += T * kIpt) {
-      // this thread's items of the batch: b0 + tid + j*T, j < n
+    const int step = T * kIpt;
+
+    // Loads are unconditional (items past the slice repeat its last item and are
+    // not computed): with no branch around them the compiler counts the loads in
+    // flight exactly and waits for each one only where its bytes are used.
+    auto load = [&](int b0, Batch& bt) {
       const int first = b0 + tid;
-      const int n = first < items ? min(kIpt, (items - first + T - 1) / T) : 0;
+      bt.n = first < items ? min(kIpt, (items - first + T - 1) / T) : 0;
       int row = first / ipr;
       int ii = first - row * ipr;
-      typename It::Raw raw[kIpt];
-      int irow[kIpt], iit[kIpt];
 #pragma unroll
       for (int j = 0; j < kIpt; ++j) {
-        irow[j] = row;
-        iit[j] = i0 + ii;
-        if (j < n) It::load(W, (u32)(r0 + row) * rb, i0 + ii, raw[j]);
+        const bool ok = row < rows;
+        bt.irow[j] = ok ? row : rows - 1;
+        bt.iit[j] = i0 + (ok ? ii : ipr - 1);
+        It::load(W, (u32)(r0 + bt.irow[j]) * rb, bt.iit[j], bt.raw[j]);
         row += drow;
         ii += di;
         if (ii >= ipr) { ii -= ipr; ++row; }
       }
-      if (b0 == 0) {
-        if (c0 > 0) __syncthreads();  // readers of the previous chunk are done
-        stage_x(x, x_f16, K, tm, ntok, c0, cw, KC, s_x, s_sx);
-      }
+    };
+    auto compute = [&](const Batch& bt) {
 #pragma unroll
       for (int j = 0; j < kIpt; ++j) {
-        if (j < n) {
+        if (j < bt.n) {
           Unit o[RUNS];
-          It::unpack(raw[j], o);
+          It::unpack(bt.raw[j], o);
 #pragma unroll
           for (int r = 0; r < RUNS; ++r) {
-            const int u = It::unit(iit[j], r);
+            const int u = It::unit(bt.iit[j], r);
             float q[32];
             unit_codes<F>(o[r], q);
 #pragma unroll
@@ -230,38 +355,155 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
                 float xv[32];
                 const int xo = t * KC + (u - c0);
                 read_x32(s_x + xo * kXStride, xv);
-                s_part[(t * RW + irow[j]) * nU + u] = item_partial<F>(o[r], q, xv, s_sx[xo * 2], s_sx[xo * 2 + 1]);
+                s_part[(t * RW + bt.irow[j]) * nU + u] =
+                    item_partial<F>(o[r], q, xv, s_sx[xo * 2], s_sx[xo * 2 + 1]);
               }
             }
           }
         }
       }
+    };
+
+    Batch A, B;
+    if (XR && x_fits_regs(x_f16, ntok, cw)) {
+      XRegs xr;
+      x_load(x, x_f16, K, tm, ntok, c0, cw, xr);
+      load(0, A);
+      if (c0 > 0) __syncthreads();  // readers of the previous chunk are done
+      x_put(xr, x_f16, ntok, cw, KC, s_x, s_sx);
+    } else {
+      load(0, A);
+      if (c0 > 0) __syncthreads();
+      stage_x(x, x_f16, K, tm, ntok, c0, cw, KC, s_x, s_sx);
+    }
+    for (int b0 = 0; b0 < items; b0 += 2 * step) {
+      if (b0 + step < items) load(b0 + step, B);
+      compute(A);
+      if (b0 + step >= items) break;
+      if (b0 + 2 * step < items) load(b0 + 2 * step, A);
+      compute(B);
     }
   }
   __syncthreads();
 
-  // one wave per (row, token): lane l adds units l, l+64, ..., then the butterfly
-  const int wave = tid >> 6, lane = tid & 63, nw = T >> 6;
-  for (int rt = wave; rt < rows * ntok; rt += nw) {
-    const int row = rt / ntok, t = rt - row * ntok;
-    const float* pp = s_part + (t * RW + row) * nU;
-    float v = 0.0f;
-    for (int u = lane; u < nU; u += 64) v += pp[u];
-    v = wave_sum(v);
-    if (lane == 0) y[(u64)tm.y(t) * M + r0 + row] = v;
-  }
+  reduce_rows(s_part, rows, ntok, nU, RW, M, r0, tm, y);
   __syncthreads();  // LDS is reused by the caller's next pass
 }
 
-extern __shared__ float s_dyn[];  // sized at launch: lds_floats(NB, KC, RW, nU)
+extern __shared__ float s_dyn[];  // sized at launch: lds_floats(NB, KC, RW, nU), or RW * nU floats
 
 template <int F, int NB>
 __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
   const int r0 = blockIdx.x * a.rows_per_wg;
   const int rows = min(a.rows_per_wg, a.M - r0);
   const TokMap tm{nullptr, 1, 1};
-  gemv_rows<F, NB>(a.W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows, a.rows_per_wg, a.chunk_units,
-                   a.x, a.x_f16, tm, a.N, a.y, s_dyn);
+  gemv_rows<F, NB, true>(a.W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows, a.rows_per_wg,
+                         a.chunk_units, a.x, a.x_f16, tm, a.N, a.y, s_dyn);
+}
+
+// ---------------------------------------------------------------------------------------------
+// One token.  Threads are laid out unit-major: thread t takes item column
+// i = t % ipr of rows g, g + G, g + 2G, ... (g = t / ipr, G row groups, at most R
+// rows per thread), so it needs the activations of one item only: it loads them
+// straight into registers, before its weight bytes, and reuses them for every
+// row -- no LDS staging and no barrier before the products.  Consecutive threads
+// still read consecutive items of a row.  Partial sums and their reduction are
+// those of the general path, so the results are the same bits.
+template <int F, int R>
+__device__ __forceinline__ void one_items(const typename Item<F>::Raw (&wr)[R], const float (&xv)[Item<F>::RUNS][32],
+                                          int g, int G, int gi, bool active, int rows, int nU, float* s_part,
+                                          int spare) {
+  using It = Item<F>;
+  constexpr int RUNS = It::RUNS;
+  float sx[RUNS][2];
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {
+    sx[r][0] = half_sum16(&xv[r][0]);
+    sx[r][1] = half_sum16(&xv[r][16]);
+  }
+  // every item is computed and stored unconditionally (rows past the slice repeat
+  // its last row and store to a spare slot after the partials): a branch around
+  // the products or the store would let the compiler sink the products, and
+  // their loads, into it, after the wait for the activations
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int row = g + G * k;
+    Unit o[RUNS];
+    It::unpack(wr[k], o);
+#pragma unroll
+    for (int r = 0; r < RUNS; ++r) {
+      float q[32];
+      unit_codes<F>(o[r], q);
+      const float v = item_partial<F>(o[r], q, xv[r], sx[r][0], sx[r][1]);
+      const int slot = active && row < rows ? row * nU + It::unit(gi, r) : spare;
+      s_part[slot] = v;
+    }
+  }
+}
+
+// rows_per_wg = RW, chunk_units = G (row groups); LDS: RW * nU partial sums and
+// one spare slot.
+template <int F, bool XH, int R>
+__global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
+  using It = Item<F>;
+  constexpr int RUNS = It::RUNS;
+  const int RW = a.rows_per_wg;
+  const int r0 = blockIdx.x * RW;
+  const int rows = min(RW, a.M - r0);
+  const int nU = a.nU;
+  const int ipr = nU / RUNS;
+  const int G = a.chunk_units;
+  const int tid = threadIdx.x;
+  const int g = tid / ipr;
+  const bool active = g < G;
+  const int gi = active ? tid - g * ipr : 0;
+  const u8* W = a.W;
+  const u32 rb = static_cast<u32>(a.row_bytes);
+
+  // activations first (their loads retire first), then the weight bytes of up to
+  // R rows (rows past the slice repeat its last row and are not computed)
+  float xv[RUNS][32];
+  typename It::Raw wr[R];
+  if constexpr (XH) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    uint4 xr[RUNS][4];
+#pragma unroll
+    for (int r = 0; r < RUNS; ++r) {
+      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(a.x) + 32 * It::unit(gi, r));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xr[r][k] = p[k];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+    // keep every load above this point: the scheduler would otherwise sink the
+    // weight loads next to their first use, behind the wait for the activations
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const h8 h = __builtin_bit_cast(h8, xr[r][k]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[r][8 * k + e] = static_cast<float>(h[e]);
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < RUNS; ++r) {
+      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + 32 * It::unit(gi, r));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 f = p[k];
+        xv[r][4 * k] = f.x; xv[r][4 * k + 1] = f.y; xv[r][4 * k + 2] = f.z; xv[r][4 * k + 3] = f.w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  one_items<F, R>(wr, xv, g, G, gi, active, rows, nU, s_dyn, RW * nU);
+  __syncthreads();
+  const TokMap tm{nullptr, 1, 1};
+  reduce_rows(s_dyn, rows, 1, nU, RW, a.M, r0, tm, a.y);
 }
 
 // Expert-indexed: blockIdx.y = rank k of the expert among the distinct valid ids
@@ -344,8 +586,11 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
   const u8* W = a.W + (u64)e * a.expert_bytes;
   for (int c = 0; c < np; c += NB) {
     const TokMap tm{s_pairs + c, a.S, a.x_per_slot};
-    gemv_rows<F, NB>(W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows, a.rows_per_wg, a.chunk_units,
-                     a.x, a.x_f16, tm, min(NB, np - c), a.y, s_dyn);
+    // (the K-quant formats stage activations directly: the pass loop leaves no
+    // registers for the activation slots)
+    gemv_rows<F, NB, F != FMT_Q4_K && F != FMT_Q6_K>(W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows,
+                                                     a.rows_per_wg, a.chunk_units, a.x, a.x_f16, tm,
+                                                     min(NB, np - c), a.y, s_dyn);
   }
 }
 
@@ -374,10 +619,22 @@ constexpr void fill_id(GemvKernel* t, std::integer_sequence<int, BI...>) {
   ((t[BI] = k_gemv_id<F, kBuckets[BI]>), ...);
 }
 
+template <int F>
+constexpr void fill_one(GemvKernel (&t)[2][3]) {
+  t[0][0] = k_gemv1<F, false, 1>; t[0][1] = k_gemv1<F, false, 2>; t[0][2] = k_gemv1<F, false, 4>;
+  t[1][0] = k_gemv1<F, true, 1>;  t[1][1] = k_gemv1<F, true, 2>;  t[1][2] = k_gemv1<F, true, 4>;
+}
+
 struct Tables {
   GemvKernel dense[5][kNumBuckets];
   GemvKernel id[5][kNumBuckets];
+  GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   Tables() {
+    fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
+    fill_one<FMT_Q8_0>(one[FMT_Q8_0]);
+    fill_one<FMT_Q4_K>(one[FMT_Q4_K]);
+    fill_one<FMT_Q6_K>(one[FMT_Q6_K]);
+    fill_one<FMT_A4G64>(one[FMT_A4G64]);
     auto seq = std::make_integer_sequence<int, kNumBuckets>{};
     fill_dense<FMT_Q4_0>(dense[FMT_Q4_0], seq);
     fill_dense<FMT_Q8_0>(dense[FMT_Q8_0], seq);
@@ -432,11 +689,43 @@ Shape make_shape(int M, int nU, int NB, int RW, int ipt) {
 
 }  // namespace
 
+// Runs (32-weight units) per work item of each format.
+constexpr int kRuns[5] = {1, 1, 2, 2, 2};
+
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t st) {
   const int bi = bucket_index(N);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
   const int M = static_cast<int>(m.M);
+  const int ipr = nU / kRuns[m.fmt];
+  if (N == 1 && ipr <= 512) {
+    // One token: about one workgroup per CU of G row groups (G * ipr <= 512
+    // threads) x R rows per thread, R in {1, 2, 4} the smallest that covers
+    // M / 256 rows; then RW = G * R, so every thread has R rows to compute.
+    const int Gmax = 512 / ipr;
+    const int want = (M + kCUs - 1) / kCUs;
+    const int R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
+    const int ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
+    int Ge = (want + R - 1) / R;
+    if (Ge > Gmax) Ge = Gmax;
+    const int RW = Ge * R;
+    GemvArgs a{};
+    a.W = m.blocks;
+    a.row_bytes = m.row_bytes;
+    a.M = M;
+    a.nU = nU;
+    a.K = static_cast<int>(m.K);
+    a.rows_per_wg = RW;
+    a.chunk_units = Ge;
+    a.x = x;
+    a.x_f16 = x_f16;
+    a.y = y;
+    a.N = 1;
+    const int threads = (Ge * ipr + 63) / 64 * 64;
+    const size_t lds = (static_cast<size_t>(RW) * nU + 1) * sizeof(float);
+    hipLaunchKernelGGL(tables().one[m.fmt][x_f16 ? 1 : 0][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
+    return hipGetLastError();
+  }
   // about two workgroups per CU
   const Shape s = make_shape(M, nU, kBuckets[bi], (M + 2 * kCUs - 1) / (2 * kCUs), 2);
   GemvArgs a{};
