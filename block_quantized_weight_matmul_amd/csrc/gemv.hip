@@ -110,39 +110,6 @@ __device__ __forceinline__ float half_sum16(const float* p) {
          (sum4(p[8], p[9], p[10], p[11]) + sum4(p[12], p[13], p[14], p[15]));
 }
 
-// Stage activations of units [c0, c0 + cw) of tokens t < ntok as fp32, then the
-// sum of each 16-activation half (fixed order).  Ends with a barrier.
-__device__ __forceinline__ void stage_x(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0,
-                                        int cw, int KC, float* s_x, float* s_sx) {
-  const int per_tok = cw * 8;  // float4 slots per token
-  for (int idx = threadIdx.x; idx < ntok * per_tok; idx += blockDim.x) {
-    const int t = idx / per_tok;
-    const int rem = idx - t * per_tok;
-    const int uu = rem >> 3;
-    const int q4 = rem & 7;
-    const u64 k = (u64)tm.x(t) * K + 32 * (c0 + uu) + 4 * q4;
-    float4 v;
-    if (x_f16) {
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      const h4 h = *reinterpret_cast<const h4*>(reinterpret_cast<const _Float16*>(x) + k);
-      v = make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
-                      static_cast<float>(h[3]));
-    } else {
-      v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + k);
-    }
-    *reinterpret_cast<float4*>(&s_x[(t * KC + uu) * kXStride + 4 * q4]) = v;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < ntok * cw * 2; idx += blockDim.x) {
-    const int t = idx / (cw * 2);
-    const int rem = idx - t * cw * 2;
-    const int uu = rem >> 1;
-    const int h = rem & 1;
-    s_sx[(t * KC + uu) * 2 + h] = half_sum16(&s_x[(t * KC + uu) * kXStride + 16 * h]);
-  }
-  __syncthreads();
-}
-
 // The activation chunk can instead pass through registers: x_load issues its
 // global loads (kXRegs 16-byte slots per thread, 4 fp32 or 8 fp16 activations
 // each; slot indices past the chunk are clamped, so the loads carry no branch)
@@ -162,7 +129,7 @@ __device__ __forceinline__ bool x_fits_regs(int x_f16, int ntok, int cw) {
 }
 
 __device__ __forceinline__ void x_load(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0, int cw,
-                                       XRegs& r) {
+                                       XRegs& r, int base = 0) {
   const int spu = x_slots_per_unit(x_f16);
   const int es = x_f16 ? 2 : 4;
   const int per_tok = cw * spu;
@@ -170,8 +137,8 @@ __device__ __forceinline__ void x_load(const void* x, int x_f16, int K, const To
   const u8* xb = reinterpret_cast<const u8*>(x);
 #pragma unroll
   for (int j = 0; j < kXRegs; ++j) {
-    if (j * static_cast<int>(blockDim.x) < total) {  // uniform: slot rounds the chunk needs
-      const int idx = min(static_cast<int>(threadIdx.x + j * blockDim.x), total - 1);
+    if (base + j * static_cast<int>(blockDim.x) < total) {  // uniform: slot rounds the chunk needs
+      const int idx = min(base + static_cast<int>(threadIdx.x + j * blockDim.x), total - 1);
       const int t = idx / per_tok;
       const int rem = idx - t * per_tok;
       const int uu = rem / spu;
@@ -182,14 +149,14 @@ __device__ __forceinline__ void x_load(const void* x, int x_f16, int K, const To
 }
 
 __device__ __forceinline__ void x_put(const XRegs& r, int x_f16, int ntok, int cw, int KC, float* s_x,
-                                      float* s_sx) {
+                                      float* s_sx, int base = 0) {
   const int spu = x_slots_per_unit(x_f16);
   const int per_tok = cw * spu;
   const int total = ntok * per_tok;
 #pragma unroll
   for (int j = 0; j < kXRegs; ++j) {
-    if (j * static_cast<int>(blockDim.x) >= total) break;  // uniform
-    const int idx = threadIdx.x + j * blockDim.x;
+    if (base + j * static_cast<int>(blockDim.x) >= total) break;  // uniform
+    const int idx = base + threadIdx.x + j * blockDim.x;
     const int ic = min(idx, total - 1);
     const int t = ic / per_tok;
     const int rem = ic - t * per_tok;
@@ -221,7 +188,18 @@ __device__ __forceinline__ void x_put(const XRegs& r, int x_f16, int ntok, int c
     // the first slot of each half writes its sum
     if (idx < total && (q & (spu / 2 - 1)) == 0) s_sx[(t * KC + uu) * 2 + q / (spu / 2)] = hs;
   }
-  __syncthreads();
+}
+
+// Stage a chunk too large for one register round: rounds of kXRegs slots per
+// thread, each issuing all its loads before its stores.
+__device__ __forceinline__ void stage_x(const void* x, int x_f16, int K, const TokMap& tm, int ntok, int c0, int cw,
+                                        int KC, float* s_x, float* s_sx) {
+  const int total = ntok * cw * x_slots_per_unit(x_f16);
+  for (int base = 0; base < total; base += kXRegs * static_cast<int>(blockDim.x)) {
+    XRegs xr;
+    x_load(x, x_f16, K, tm, ntok, c0, cw, xr, base);
+    x_put(xr, x_f16, ntok, cw, KC, s_x, s_sx, base);
+  }
 }
 
 __device__ __forceinline__ void read_x32(const float* s_x, float (&v)[32]) {
@@ -279,13 +257,16 @@ __device__ __forceinline__ void reduce_rows(const float* s_part, int rows, int n
   }
 }
 
+// Tokens per work unit: a call with more tokens spreads them over more threads.
+constexpr int kTokPerUnit = 4;
+
 // Items per thread per batch.  A thread holds two batches: while it decodes one,
 // the loads of the next are in flight.
 // Q6_K items carry 34 raw bytes and two scale pairs, so it holds fewer.
 template <int F>
 constexpr int ipt_max(int NB) {
-  if (F == FMT_Q6_K) return NB <= 8 ? 2 : 1;
-  return NB <= 8 ? 3 : (NB <= 16 ? 2 : 1);
+  if (F == FMT_Q6_K) return NB <= 2 ? 2 : 1;
+  return NB <= 2 ? 3 : 2;
 }
 
 // Rows [r0, r0 + rows) of the matrix at W (rows <= RW), all tokens t < ntok.
@@ -304,10 +285,15 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
   const int T = blockDim.x;
   const int tid = threadIdx.x;
 
-  // A batch: this thread's items b0 + tid + j*T (j < n) of the chunk's item list.
+  // Work unit = (token group, item): an item against NT consecutive tokens of the
+  // call.  Splitting the tokens gives a workgroup more threads than it has items
+  // when the call has many tokens.  A batch is this thread's work units
+  // b0 + tid + j*T (j < n) of the chunk's list, token group major.
+  constexpr int NT = NB < kTokPerUnit ? NB : kTokPerUnit;
+  const int TG = (ntok + NT - 1) / NT;
   struct Batch {
     typename It::Raw raw[kIpt];
-    int irow[kIpt], iit[kIpt];
+    int irow[kIpt], iit[kIpt], t0[kIpt];
     int n;
   };
 
@@ -316,26 +302,25 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
     const int ipr = cw / RUNS;        // items per row in the chunk
     const int i0 = c0 / RUNS;         // first item of the chunk
     const int items = rows * ipr;
-    const int drow = T / ipr, di = T - drow * ipr;  // item index step T as (rows, items)
+    const int works = items * TG;
     const int step = T * kIpt;
 
-    // Loads are unconditional (items past the slice repeat its last item and are
-    // not computed): with no branch around them the compiler counts the loads in
-    // flight exactly and waits for each one only where its bytes are used.
+    // Loads are unconditional (work units past the list repeat its last item and
+    // are not computed): with no branch around them the compiler counts the loads
+    // in flight exactly and waits for each one only where its bytes are used.
     auto load = [&](int b0, Batch& bt) {
       const int first = b0 + tid;
-      bt.n = first < items ? min(kIpt, (items - first + T - 1) / T) : 0;
-      int row = first / ipr;
-      int ii = first - row * ipr;
+      bt.n = first < works ? min(kIpt, (works - first + T - 1) / T) : 0;
 #pragma unroll
       for (int j = 0; j < kIpt; ++j) {
-        const bool ok = row < rows;
-        bt.irow[j] = ok ? row : rows - 1;
-        bt.iit[j] = i0 + (ok ? ii : ipr - 1);
-        It::load(W, (u32)(r0 + bt.irow[j]) * rb, bt.iit[j], bt.raw[j]);
-        row += drow;
-        ii += di;
-        if (ii >= ipr) { ii -= ipr; ++row; }
+        const int w = min(first + j * T, works - 1);
+        const int tg = w / items;
+        const int it = w - tg * items;
+        const int row = it / ipr;
+        bt.irow[j] = row;
+        bt.iit[j] = i0 + (it - row * ipr);
+        bt.t0[j] = tg * NT;
+        It::load(W, (u32)(r0 + row) * rb, bt.iit[j], bt.raw[j]);
       }
     };
     auto compute = [&](const Batch& bt) {
@@ -350,7 +335,8 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
             float q[32];
             unit_codes<F>(o[r], q);
 #pragma unroll
-            for (int t = 0; t < NB; ++t) {
+            for (int tt = 0; tt < NT; ++tt) {
+              const int t = bt.t0[j] + tt;
               if (t < ntok) {
                 float xv[32];
                 const int xo = t * KC + (u - c0);
@@ -376,11 +362,12 @@ __device__ __forceinline__ void gemv_rows(const u8* W, u32 rb, int M, int nU, in
       if (c0 > 0) __syncthreads();
       stage_x(x, x_f16, K, tm, ntok, c0, cw, KC, s_x, s_sx);
     }
-    for (int b0 = 0; b0 < items; b0 += 2 * step) {
-      if (b0 + step < items) load(b0 + step, B);
+    __syncthreads();  // the chunk's activations and half sums are in LDS
+    for (int b0 = 0; b0 < works; b0 += 2 * step) {
+      if (b0 + step < works) load(b0 + step, B);
       compute(A);
-      if (b0 + step >= items) break;
-      if (b0 + 2 * step < items) load(b0 + 2 * step, A);
+      if (b0 + step >= works) break;
+      if (b0 + 2 * step < works) load(b0 + 2 * step, A);
       compute(B);
     }
   }
@@ -516,9 +503,8 @@ constexpr int kIdMaxPairs = static_cast<int>(kMaxGemvTokens * kMaxSlots);
 template <int F, int NB>
 __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
   __shared__ u32 s_bits[kIdBitmapWords];
-  __shared__ int s_cnt[512];
   __shared__ int s_pairs[kIdMaxPairs];
-  __shared__ int s_expert, s_npairs;
+  __shared__ int s_expert, s_npairs, s_bad;
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -528,38 +514,42 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
   const int rows = min(a.rows_per_wg, a.M - r0);
 
   for (int w = tid; w < nwords; w += nthr) s_bits[w] = 0u;
-  if (tid == 0) { s_expert = -1; s_npairs = 0; }
+  if (tid == 0) { s_expert = -1; s_npairs = 0; s_bad = 0; }
   __syncthreads();
   for (int p = tid; p < P; p += nthr) {
     const int e = a.ids[p];
-    if (e >= 0 && e < a.E) atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+    if (e >= 0 && e < a.E)
+      atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+    else
+      s_bad = 1;
   }
   __syncthreads();
 
-  // k-th set bit: thread t counts words [t*wpt, (t+1)*wpt), then an inclusive scan.
+  // k-th set bit, found by the first wave: lane l counts words [l*wpl, (l+1)*wpl),
+  // an inclusive prefix over the lanes, then the lane holding rank k walks its words.
   const int k = blockIdx.y;
-  const int wpt = (nwords + nthr - 1) / nthr;
-  int cnt = 0;
-  for (int w = tid * wpt; w < min(nwords, (tid + 1) * wpt); ++w) cnt += __popc(s_bits[w]);
-  s_cnt[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < nthr; off <<= 1) {
-    const int v = tid >= off ? s_cnt[tid - off] : 0;
-    __syncthreads();
-    s_cnt[tid] += v;
-    __syncthreads();
-  }
-  const int incl = s_cnt[tid];
-  const int excl = incl - cnt;
-  if (k >= excl && k < incl) {
-    int seen = excl;
-    for (int w = tid * wpt; w < min(nwords, (tid + 1) * wpt); ++w) {
-      u32 bits = s_bits[w];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        if (seen == k) s_expert = (w << 5) + b;
-        ++seen;
-        bits &= bits - 1u;
+  if (tid < 64) {
+    const int wpl = (nwords + 63) >> 6;
+    const int w0 = tid * wpl, w1 = min(nwords, w0 + wpl);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(s_bits[w]);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (tid >= off) incl += v;
+    }
+    const int excl = incl - cnt;
+    if (k >= excl && k < incl) {
+      int seen = excl;
+      for (int w = w0; w < w1; ++w) {
+        u32 bits = s_bits[w];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          if (seen == k) s_expert = (w << 5) + b;
+          ++seen;
+          bits &= bits - 1u;
+        }
       }
     }
   }
@@ -568,12 +558,12 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
 
   // Ids outside [0, E) have no matrix: their output rows are NaN (written by the
   // rank-0 workgroups, which exist for every row slice).
-  if (blockIdx.y == 0) {
+  if (blockIdx.y == 0 && s_bad) {
     const float qnan = __builtin_nanf("");
-    for (int p = 0; p < P; ++p) {
+    for (int i = tid; i < P * rows; i += nthr) {
+      const int p = i / rows, r = i - p * rows;
       const int id = a.ids[p];
-      if (id < 0 || id >= a.E)
-        for (int r = tid; r < rows; r += nthr) a.y[(u64)p * a.M + r0 + r] = qnan;
+      if (id < 0 || id >= a.E) a.y[(u64)p * a.M + r0 + r] = qnan;
     }
   }
   if (e < 0) return;  // uniform over the workgroup
@@ -614,6 +604,8 @@ template <int F, int... BI>
 constexpr void fill_dense(GemvKernel* t, std::integer_sequence<int, BI...>) {
   ((t[BI] = k_gemv<F, kBuckets[BI]>), ...);
 }
+// The expert-indexed path takes at most 4 pairs of an expert per pass.
+constexpr int kIdBuckets = 4;  // buckets 1, 2, 3, 4
 template <int F, int... BI>
 constexpr void fill_id(GemvKernel* t, std::integer_sequence<int, BI...>) {
   ((t[BI] = k_gemv_id<F, kBuckets[BI]>), ...);
@@ -627,7 +619,7 @@ constexpr void fill_one(GemvKernel (&t)[2][3]) {
 
 struct Tables {
   GemvKernel dense[5][kNumBuckets];
-  GemvKernel id[5][kNumBuckets];
+  GemvKernel id[5][kIdBuckets];
   GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   Tables() {
     fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
@@ -641,11 +633,12 @@ struct Tables {
     fill_dense<FMT_Q4_K>(dense[FMT_Q4_K], seq);
     fill_dense<FMT_Q6_K>(dense[FMT_Q6_K], seq);
     fill_dense<FMT_A4G64>(dense[FMT_A4G64], seq);
-    fill_id<FMT_Q4_0>(id[FMT_Q4_0], seq);
-    fill_id<FMT_Q8_0>(id[FMT_Q8_0], seq);
-    fill_id<FMT_Q4_K>(id[FMT_Q4_K], seq);
-    fill_id<FMT_Q6_K>(id[FMT_Q6_K], seq);
-    fill_id<FMT_A4G64>(id[FMT_A4G64], seq);
+    auto idseq = std::make_integer_sequence<int, kIdBuckets>{};
+    fill_id<FMT_Q4_0>(id[FMT_Q4_0], idseq);
+    fill_id<FMT_Q8_0>(id[FMT_Q8_0], idseq);
+    fill_id<FMT_Q4_K>(id[FMT_Q4_K], idseq);
+    fill_id<FMT_Q6_K>(id[FMT_Q6_K], idseq);
+    fill_id<FMT_A4G64>(id[FMT_A4G64], idseq);
   }
 };
 
@@ -665,20 +658,20 @@ struct Shape {
   size_t lds;   // dynamic LDS bytes
 };
 
-// A workgroup of RW rows (clamped so that its items fit 512 threads x ipt and its
-// partial sums use at most half the LDS budget); threads: one per ipt items, in
-// whole waves, 64..512; the activation chunk takes the LDS that is left.
-Shape make_shape(int M, int nU, int NB, int RW, int ipt) {
+// A workgroup of RW rows (clamped so that its partial sums use at most half the
+// LDS budget), one thread per work unit (item x token group) up to 512 threads
+// (more: further batches); the activation chunk takes the LDS that is left.
+Shape make_shape(int M, int nU, int runs, int NB, int RW, int max_threads = 512) {
+  const int TG = (NB + kTokPerUnit - 1) / kTokPerUnit;
   Shape s;
-  const int max_rw_threads = (512 * ipt) / nU;
   const int max_rw_lds = (kLdsBudget / 2 / 4) / (NB * nU);
-  if (RW > max_rw_threads) RW = max_rw_threads;
   if (RW > max_rw_lds) RW = max_rw_lds;
   if (RW > M) RW = M;
   if (RW < 1) RW = 1;
   s.RW = RW;
-  int threads = ((RW * nU + ipt - 1) / ipt + 63) / 64 * 64;
-  s.threads = threads > 512 ? 512 : (threads < 64 ? 64 : threads);
+  const int works = RW * (nU / runs) * TG;
+  const int threads = (works + 63) / 64 * 64;
+  s.threads = threads > max_threads ? max_threads : (threads < 64 ? 64 : threads);
   int KC = (kLdsBudget / 4 - NB * RW * nU) / (NB * (kXStride + 2));
   KC = KC / 8 * 8;  // chunks hold whole super-blocks, so an item's runs share a chunk
   s.KC = KC >= nU ? nU : (KC < 8 ? 8 : KC);
@@ -726,8 +719,8 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     hipLaunchKernelGGL(tables().one[m.fmt][x_f16 ? 1 : 0][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
     return hipGetLastError();
   }
-  // about two workgroups per CU
-  const Shape s = make_shape(M, nU, kBuckets[bi], (M + 2 * kCUs - 1) / (2 * kCUs), 2);
+  // about one workgroup per CU
+  const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + kCUs - 1) / kCUs);
   GemvArgs a{};
   a.W = m.blocks;
   a.row_bytes = m.row_bytes;
@@ -747,9 +740,9 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
 
 hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
                           const int32_t* ids, float* y, hipStream_t st) {
-  // pairs per expert: at most N when a token's ids are distinct; larger counts
-  // (duplicate ids) are processed in further passes of NB pairs
-  const int bi = bucket_index(N < 8 ? N : 8);
+  // pairs per expert: at most N when a token's ids are distinct, and about
+  // N * S / E in a routed batch; a workgroup takes them NB <= 4 at a time
+  const int bi = bucket_index(N < 4 ? N : 4);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
   const int64_t P = static_cast<int64_t>(N) * S;
@@ -758,7 +751,8 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   // active experts
   const int M = static_cast<int>(m.M);
   const int slices = (2 * kCUs + ranks - 1) / ranks;
-  const Shape s = make_shape(M, nU, kBuckets[bi], (M + slices - 1) / slices, 2);
+  // (256 threads: each workgroup streams a short slice, and two share a CU)
+  const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + slices - 1) / slices, 256);
   GemvArgs a{};
   a.W = m.blocks;
   a.row_bytes = m.row_bytes;
