@@ -426,7 +426,7 @@ def main():
             "projections": head["projections"],
         },
         "roofline": {
-            "kernel": f"qmm::k_gemv<{dom['fmt']}, 1 token>",
+            "kernel": f"qmm::k_gemv1<{dom['fmt']}, fp32 x> (one-token GEMV)",
             "bound": "hbm",
             "achieved": round(dom["achieved_gbs"], 1),
             "peak": HBM_PEAK_GBS,
