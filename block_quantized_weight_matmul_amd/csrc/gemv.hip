@@ -396,24 +396,35 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 // row -- no LDS staging and no barrier before the products.  Consecutive threads
 // still read consecutive items of a row.  Partial sums and their reduction are
 // those of the general path, so the results are the same bits.
+// The thread's rows g + G k (k < R): weight loads run kAhead items ahead of the
+// products -- loads of item k+kAhead are issued just before item k is computed,
+// a scheduling barrier pinning the order -- so a wave computes the items that
+// have arrived instead of stalling on the issue of loads the memory system cannot
+// take yet.  Every item is computed and stored unconditionally (rows past the
+// slice repeat its last row and store to a spare slot after the partials): a
+// branch around the products or the store would let the compiler sink the
+// products, and their loads, into it.
+constexpr int kAhead = 2;
+
 template <int F, int R>
-__device__ __forceinline__ void one_items(const typename Item<F>::Raw (&wr)[R], const float (&xv)[Item<F>::RUNS][32],
+__device__ __forceinline__ void one_items(const u8* W, u32 rb, int r0, const float (&xv)[Item<F>::RUNS][32],
                                           int g, int G, int gi, bool active, int rows, int nU, float* s_part,
-                                          int spare) {
+                                          int spare, typename Item<F>::Raw (&wr)[R]) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
+  auto load = [&](int k) { It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]); };
   float sx[RUNS][2];
 #pragma unroll
   for (int r = 0; r < RUNS; ++r) {
     sx[r][0] = half_sum16(&xv[r][0]);
     sx[r][1] = half_sum16(&xv[r][16]);
   }
-  // every item is computed and stored unconditionally (rows past the slice repeat
-  // its last row and store to a spare slot after the partials): a branch around
-  // the products or the store would let the compiler sink the products, and
-  // their loads, into it, after the wait for the activations
 #pragma unroll
   for (int k = 0; k < R; ++k) {
+    if (k + kAhead < R) {
+      load(k + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int row = g + G * k;
     Unit o[RUNS];
     It::unpack(wr[k], o);
@@ -425,6 +436,7 @@ __device__ __forceinline__ void one_items(const typename Item<F>::Raw (&wr)[R], 
       const int slot = active && row < rows ? row * nU + It::unit(gi, r) : spare;
       s_part[slot] = v;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -461,8 +473,8 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
       for (int k = 0; k < 4; ++k) xr[r][k] = p[k];
     }
 #pragma unroll
-    for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
-    // keep every load above this point: the scheduler would otherwise sink the
+    for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+    // keep these loads above this point: the scheduler would otherwise sink the
     // weight loads next to their first use, behind the wait for the activations
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -484,10 +496,10 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+    for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  one_items<F, R>(wr, xv, g, G, gi, active, rows, nU, s_dyn, RW * nU);
+  one_items<F, R>(W, rb, r0, xv, g, G, gi, active, rows, nU, s_dyn, RW * nU, wr);
   __syncthreads();
   const TokMap tm{nullptr, 1, 1};
   reduce_rows(s_dyn, rows, 1, nU, RW, a.M, r0, tm, a.y);
