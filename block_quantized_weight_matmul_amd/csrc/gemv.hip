@@ -218,6 +218,99 @@ __device__ __forceinline__ float half_dot(const float (&q)[32], const float (&x)
   return s;
 }
 
+// The same half sum with each code read as an fp16 subnormal, code * 2^-24, and
+// multiplied by x with v_fma_mix_f32 (fp16 operand widened inside the fma): two
+// codes per 32-bit word, built with one and (weights 4j, 4j+2) and one byte
+// permute (weights 4j+1, 4j+3), instead of one conversion per code.  code * 2^-24
+// widens exactly, so every product and partial sum is the one of half_dot scaled
+// by 2^-24, exactly, while it stays a normal fp32 number (|x| above ~2^-100);
+// the caller scales the coefficient by 2^24 instead.  Codes carry no bias.
+__device__ __forceinline__ float code_lo(u32 v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<u16>(v & 0xFFFFu)));
+}
+__device__ __forceinline__ float code_hi(u32 v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<u16>(v >> 16)));
+}
+// An item's codes as fp16 pairs: ev[r][k] holds the codes of weights 4k and 4k+2
+// of run r (low and high half), od[r][k] those of 4k+1 and 4k+3; run r's codes
+// are scaled by 2^sh[r] (a high nibble left in place is 16*code).  The default
+// takes the unit's code bytes apart; Q4_K and Q6_K build the pairs from the raw
+// bytes directly, which saves a mask per word.
+template <int F>
+struct MixPairs {
+  static constexpr int RUNS = Item<F>::RUNS;
+  u32 ev[RUNS][8], od[RUNS][8];
+  static constexpr int sh(int) { return 0; }
+  __device__ __forceinline__ void make(const typename Item<F>::Raw&, const Unit (&o)[RUNS]) {
+#pragma unroll
+    for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ev[r][k] = o[r].c[k] & 0x00FF00FFu;
+        od[r][k] = __builtin_amdgcn_perm(o[r].c[k], o[r].c[k], 0x0C030C01u);
+      }
+  }
+};
+
+// bytes 1 and 3 of v moved to bytes 0 and 2, zeros above them
+__device__ __forceinline__ u32 odd_bytes(u32 v) { return __builtin_amdgcn_perm(v, v, 0x0C030C01u); }
+
+template <>
+struct MixPairs<FMT_Q4_K> {
+  u32 ev[2][8], od[2][8];
+  static constexpr int sh(int) { return 0; }  // run 1 already carries a/16
+  __device__ __forceinline__ void make(const Item<FMT_Q4_K>::Raw& w, const Unit (&)[2]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u32 t = odd_bytes(w.q[k]);
+      ev[0][k] = w.q[k] & 0x000F000Fu;
+      od[0][k] = t & 0x000F000Fu;
+      ev[1][k] = w.q[k] & 0x00F000F0u;
+      od[1][k] = t & 0x00F000F0u;
+    }
+  }
+};
+
+// Q6_K: run 0 code = low nibble | qh bits (hs, hs+1) << 4; run 1 keeps the high
+// nibble in place and puts qh bits (hs+4, hs+5) at bits 8, 9: 16 * code (< 1024).
+template <>
+struct MixPairs<FMT_Q6_K> {
+  u32 ev[2][8], od[2][8];
+  static constexpr int sh(int r) { return r == 1 ? 4 : 0; }
+  __device__ __forceinline__ void make(const Item<FMT_Q6_K>::Raw& w, const Unit (&)[2]) {
+    const u32 up = 4u - 2u * static_cast<u32>(w.a >> 1);  // 4 - hs
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u32 ql = w.ql.word(k), qh = w.qh.word(k);
+      const u32 t = qh << up, qlo = odd_bytes(ql), tod = odd_bytes(qh) << up;
+      ev[0][k] = (ql & 0x000F000Fu) | (t & 0x00300030u);
+      ev[1][k] = (ql & 0x00F000F0u) | (t & 0x03000300u);
+      od[0][k] = (qlo & 0x000F000Fu) | (tod & 0x00300030u);
+      od[1][k] = (qlo & 0x00F000F0u) | (tod & 0x03000300u);
+    }
+  }
+};
+
+// All 2*RUNS half sums of an item, in lockstep: the chains are independent, and
+// interleaving them keeps one chain's dependent fmas apart.
+template <int F, int RUNS>
+__device__ __forceinline__ void half_dots_mix(const MixPairs<F>& p, const float (&x)[RUNS][32],
+                                              float (&s)[RUNS][2]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32 w = e & 1 ? p.od[r][4 * h + k] : p.ev[r][4 * h + k];
+          const float q = e < 2 ? code_lo(w) : code_hi(w);
+          const float xv = x[r][16 * h + 4 * k + e];
+          s[r][h] = k == 0 && e == 0 ? q * xv : __builtin_fmaf(q, xv, s[r][h]);
+        }
+}
+
 // An item's partial sum a0*Sq0 + b0*Sx0 + a1*Sq1 + b1*Sx1 (Q8_0 has no b terms).
 template <int F>
 __device__ __forceinline__ float item_partial(const Unit& o, const float (&q)[32], const float (&x)[32],
@@ -227,6 +320,24 @@ __device__ __forceinline__ float item_partial(const Unit& o, const float (&q)[32
     return __builtin_fmaf(o.a0, sq0, o.a1 * sq1);
   } else {
     return __builtin_fmaf(o.a0, sq0, __builtin_fmaf(o.b0, sx0, __builtin_fmaf(o.a1, sq1, o.b1 * sx1)));
+  }
+}
+
+// item_partial through half_dots_mix, for all runs: the same values, bit for bit.
+template <int F, int RUNS>
+__device__ __forceinline__ void item_partials_mix(const typename Item<F>::Raw& w, const Unit (&o)[RUNS],
+                                                  const float (&x)[RUNS][32], const float (&sx)[RUNS][2],
+                                                  float (&v)[RUNS]) {
+  static_assert(F != FMT_Q8_0, "Q8_0 codes carry a bias");
+  MixPairs<F> p;
+  p.make(w, o);
+  float sq[RUNS][2];
+  half_dots_mix<F, RUNS>(p, x, sq);
+#pragma unroll
+  for (int r = 0; r < RUNS; ++r) {
+    const float sc = static_cast<float>(1u << (24 - MixPairs<F>::sh(r)));  // 2^24 / 2^sh
+    v[r] = __builtin_fmaf(o[r].a0 * sc, sq[r][0],
+                          __builtin_fmaf(o[r].b0, sx[r][0], __builtin_fmaf(o[r].a1 * sc, sq[r][1], o[r].b1 * sx[r][1])));
   }
 }
 
@@ -391,11 +502,21 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 // ---------------------------------------------------------------------------------------------
 // One token.  Threads are laid out unit-major: thread t takes item column
 // i = t % ipr of rows g, g + G, g + 2G, ... (g = t / ipr, G row groups, at most R
-// rows per thread), so it needs the activations of one item only: it loads them
-// straight into registers, before its weight bytes, and reuses them for every
-// row -- no LDS staging and no barrier before the products.  Consecutive threads
-// still read consecutive items of a row.  Partial sums and their reduction are
-// those of the general path, so the results are the same bits.
+// rows per thread), so it needs the activations of one item only, and reuses
+// them for every row.  Consecutive threads still read consecutive items of a row.
+// Partial sums and their reduction are those of the general path, so the results
+// are the same bits.
+//
+// The workgroup stages the activations once: each thread fetches 16-value
+// chunks (at most kX1Rounds), then issues the weight loads of its first items,
+// and only then converts the chunks, forms their half sums and writes both to
+// LDS.  The per-thread activation reads therefore come from LDS instead of
+// every row group fetching the same values through the vector memory path,
+// which is shared with the weight stream.  LDS image: unit u's 32 values at
+// kXU*u .. kXU*u+31, the sums of its halves at kXU*u+32 and +33 (the pad also
+// spreads consecutive threads' 16-byte reads over the banks); one spare unit
+// after the last takes the stores of threads past the end.
+//
 // The thread's rows g + G k (k < R): weight loads run kAhead items ahead of the
 // products -- loads of item k+kAhead are issued just before item k is computed,
 // a scheduling barrier pinning the order -- so a wave computes the items that
@@ -405,20 +526,16 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 // branch around the products or the store would let the compiler sink the
 // products, and their loads, into it.
 constexpr int kAhead = 2;
+constexpr int kXU = 36;        // floats per unit in the LDS image
+constexpr int kX1Rounds = 4;   // chunks per thread: 2 nU chunks, at least nU / 2 threads
 
 template <int F, int R>
 __device__ __forceinline__ void one_items(const u8* W, u32 rb, int r0, const float (&xv)[Item<F>::RUNS][32],
-                                          int g, int G, int gi, bool active, int rows, int nU, float* s_part,
-                                          int spare, typename Item<F>::Raw (&wr)[R]) {
+                                          const float (&sx)[Item<F>::RUNS][2], int g, int G, int gi, bool active,
+                                          int rows, int nU, float* s_part, int spare, typename Item<F>::Raw (&wr)[R]) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
   auto load = [&](int k) { It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]); };
-  float sx[RUNS][2];
-#pragma unroll
-  for (int r = 0; r < RUNS; ++r) {
-    sx[r][0] = half_sum16(&xv[r][0]);
-    sx[r][1] = half_sum16(&xv[r][16]);
-  }
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     if (k + kAhead < R) {
@@ -428,20 +545,64 @@ __device__ __forceinline__ void one_items(const u8* W, u32 rb, int r0, const flo
     const int row = g + G * k;
     Unit o[RUNS];
     It::unpack(wr[k], o);
+    float v[RUNS];
+    if constexpr (F == FMT_Q8_0) {
+      float q[32];
+      unit_codes<F>(o[0], q);
+      v[0] = item_partial<F>(o[0], q, xv[0], sx[0][0], sx[0][1]);
+    } else {
+      item_partials_mix<F, RUNS>(wr[k], o, xv, sx, v);
+    }
 #pragma unroll
     for (int r = 0; r < RUNS; ++r) {
-      float q[32];
-      unit_codes<F>(o[r], q);
-      const float v = item_partial<F>(o[r], q, xv[r], sx[r][0], sx[r][1]);
       const int slot = active && row < rows ? row * nU + It::unit(gi, r) : spare;
-      s_part[slot] = v;
+      s_part[slot] = v[r];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// rows_per_wg = RW, chunk_units = G (row groups); LDS: RW * nU partial sums and
-// one spare slot.
+// 16 activations from global memory (4 fp32 or 2 fp16 slots of 16 bytes)
+template <bool XH>
+__device__ __forceinline__ void x1_fetch(const void* x, int c, uint4 (&v)[4]) {
+  const uint4* p = XH ? reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(x) + 16 * c)
+                      : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + 16 * c);
+#pragma unroll
+  for (int k = 0; k < (XH ? 2 : 4); ++k) v[k] = p[k];
+}
+
+// the chunk's values and half sum into the LDS image (dst: its 16 values)
+template <bool XH>
+__device__ __forceinline__ void x1_put(const uint4 (&v)[4], float* dst, float* dsum) {
+  float f[16];
+  if constexpr (XH) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const h8 h = __builtin_bit_cast(h8, v[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[8 * k + e] = static_cast<float>(h[e]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[4 * k] = __uint_as_float(v[k].x); f[4 * k + 1] = __uint_as_float(v[k].y);
+      f[4 * k + 2] = __uint_as_float(v[k].z); f[4 * k + 3] = __uint_as_float(v[k].w);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<float4*>(dst + 4 * k) = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+  *dsum = half_sum16(f);
+}
+
+// LDS floats of the one-token kernel: activation image (nU + 1 units), then
+// RW * nU partial sums and one spare slot
+inline size_t one_lds_floats(int nU, int RW) {
+  return static_cast<size_t>(kXU) * (nU + 1) + static_cast<size_t>(RW) * nU + 1;
+}
+
+// rows_per_wg = RW, chunk_units = G (row groups)
 template <int F, bool XH, int R>
 __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   using It = Item<F>;
@@ -453,56 +614,56 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   const int ipr = nU / RUNS;
   const int G = a.chunk_units;
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
   const int g = tid / ipr;
   const bool active = g < G;
   const int gi = active ? tid - g * ipr : 0;
   const u8* W = a.W;
   const u32 rb = static_cast<u32>(a.row_bytes);
+  float* s_x = s_dyn;
+  float* s_part = s_dyn + kXU * (nU + 1);
 
-  // activations first (their loads retire first), then the weight bytes of up to
-  // R rows (rows past the slice repeat its last row and are not computed)
-  float xv[RUNS][32];
+  // activation chunks first (their loads retire first), then the weight bytes of
+  // the first items; chunk indices past the end are clamped (a repeated load)
+  const int chunks = 2 * nU;
+  const int nr = (chunks + nthr - 1) / nthr;
+  uint4 xr[kX1Rounds][4];
+#pragma unroll
+  for (int j = 0; j < kX1Rounds; ++j)
+    if (j < nr) x1_fetch<XH>(a.x, min(tid + j * nthr, chunks - 1), xr[j]);
   typename It::Raw wr[R];
-  if constexpr (XH) {
-    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-    uint4 xr[RUNS][4];
 #pragma unroll
-    for (int r = 0; r < RUNS; ++r) {
-      const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(a.x) + 32 * It::unit(gi, r));
+  for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+  // keep the weight loads above the staging: the scheduler would otherwise sink
+  // them next to their first use, behind the wait for the activations
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) xr[r][k] = p[k];
+  for (int j = 0; j < kX1Rounds; ++j)
+    if (j < nr) {
+      const int c = tid + j * nthr;
+      const int base = c < chunks ? kXU * (c >> 1) + 16 * (c & 1) : kXU * nU;
+      const int sum = c < chunks ? kXU * (c >> 1) + 32 + (c & 1) : kXU * nU + 32;
+      x1_put<XH>(xr[j], s_x + base, s_x + sum);
     }
+  __syncthreads();
+
+  float xv[RUNS][32], sx[RUNS][2];
 #pragma unroll
-    for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
-    // keep these loads above this point: the scheduler would otherwise sink the
-    // weight loads next to their first use, behind the wait for the activations
-    __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < RUNS; ++r) {
+    const float* p = s_x + kXU * It::unit(gi, r);
 #pragma unroll
-    for (int r = 0; r < RUNS; ++r)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const h8 h = __builtin_bit_cast(h8, xr[r][k]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[r][8 * k + e] = static_cast<float>(h[e]);
-      }
-  } else {
-#pragma unroll
-    for (int r = 0; r < RUNS; ++r) {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + 32 * It::unit(gi, r));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float4 f = p[k];
-        xv[r][4 * k] = f.x; xv[r][4 * k + 1] = f.y; xv[r][4 * k + 2] = f.z; xv[r][4 * k + 3] = f.w;
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(p + 4 * k);
+      xv[r][4 * k] = f.x; xv[r][4 * k + 1] = f.y; xv[r][4 * k + 2] = f.z; xv[r][4 * k + 3] = f.w;
     }
-#pragma unroll
-    for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
-    __builtin_amdgcn_sched_barrier(0);
+    const float2 h = *reinterpret_cast<const float2*>(p + 32);
+    sx[r][0] = h.x;
+    sx[r][1] = h.y;
   }
-  one_items<F, R>(W, rb, r0, xv, g, G, gi, active, rows, nU, s_dyn, RW * nU, wr);
+  one_items<F, R>(W, rb, r0, xv, sx, g, G, gi, active, rows, nU, s_part, RW * nU, wr);
   __syncthreads();
   const TokMap tm{nullptr, 1, 1};
-  reduce_rows(s_dyn, rows, 1, nU, RW, a.M, r0, tm, a.y);
+  reduce_rows(s_part, rows, 1, nU, RW, a.M, r0, tm, a.y);
 }
 
 // Expert-indexed: blockIdx.y = rank k of the expert among the distinct valid ids
@@ -707,6 +868,8 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     // One token: about one workgroup per CU of G row groups (G * ipr <= 512
     // threads) x R rows per thread, R in {1, 2, 4} the smallest that covers
     // M / 256 rows; then RW = G * R, so every thread has R rows to compute.
+    // Shapes whose activation image and partials do not fit the LDS budget take
+    // the general path below.
     const int Gmax = 512 / ipr;
     const int want = (M + kCUs - 1) / kCUs;
     const int R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
@@ -714,22 +877,24 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     int Ge = (want + R - 1) / R;
     if (Ge > Gmax) Ge = Gmax;
     const int RW = Ge * R;
-    GemvArgs a{};
-    a.W = m.blocks;
-    a.row_bytes = m.row_bytes;
-    a.M = M;
-    a.nU = nU;
-    a.K = static_cast<int>(m.K);
-    a.rows_per_wg = RW;
-    a.chunk_units = Ge;
-    a.x = x;
-    a.x_f16 = x_f16;
-    a.y = y;
-    a.N = 1;
-    const int threads = (Ge * ipr + 63) / 64 * 64;
-    const size_t lds = (static_cast<size_t>(RW) * nU + 1) * sizeof(float);
-    hipLaunchKernelGGL(tables().one[m.fmt][x_f16 ? 1 : 0][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
-    return hipGetLastError();
+    const size_t lds = one_lds_floats(nU, RW) * sizeof(float);
+    if (lds <= static_cast<size_t>(kLdsBudget)) {
+      GemvArgs a{};
+      a.W = m.blocks;
+      a.row_bytes = m.row_bytes;
+      a.M = M;
+      a.nU = nU;
+      a.K = static_cast<int>(m.K);
+      a.rows_per_wg = RW;
+      a.chunk_units = Ge;
+      a.x = x;
+      a.x_f16 = x_f16;
+      a.y = y;
+      a.N = 1;
+      const int threads = (Ge * ipr + 63) / 64 * 64;
+      hipLaunchKernelGGL(tables().one[m.fmt][x_f16 ? 1 : 0][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
+      return hipGetLastError();
+    }
   }
   // about one workgroup per CU
   const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + kCUs - 1) / kCUs);
