@@ -624,13 +624,14 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   float* s_part = s_dyn + kXU * (nU + 1);
 
   // activation chunks first (their loads retire first), then the weight bytes of
-  // the first items; chunk indices past the end are clamped (a repeated load)
+  // the first items; threads past the last chunk fetch nothing and store their
+  // (unset) registers to the spare unit
   const int chunks = 2 * nU;
   const int nr = (chunks + nthr - 1) / nthr;
   uint4 xr[kX1Rounds][4];
 #pragma unroll
   for (int j = 0; j < kX1Rounds; ++j)
-    if (j < nr) x1_fetch<XH>(a.x, min(tid + j * nthr, chunks - 1), xr[j]);
+    if (j < nr && tid + j * nthr < chunks) x1_fetch<XH>(a.x, tid + j * nthr, xr[j]);
   typename It::Raw wr[R];
 #pragma unroll
   for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
@@ -865,16 +866,20 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
   const int M = static_cast<int>(m.M);
   const int ipr = nU / kRuns[m.fmt];
   if (N == 1 && ipr <= 512) {
-    // One token: about one workgroup per CU of G row groups (G * ipr <= 512
-    // threads) x R rows per thread, R in {1, 2, 4} the smallest that covers
-    // M / 256 rows; then RW = G * R, so every thread has R rows to compute.
-    // Shapes whose activation image and partials do not fit the LDS budget take
-    // the general path below.
+    // One token: G row groups (G * ipr <= 512 threads) x R rows per thread.
+    // Two workgroups per CU of one row per thread when that fills at least 3/4
+    // of their waves (the second workgroup's loads and products overlap the
+    // first one's reduction); otherwise about one workgroup per CU, R in
+    // {1, 2, 4} the smallest that covers M / 256 rows.  RW = G * R, so every
+    // thread has R rows to compute.  Shapes whose activation image and partials
+    // do not fit the LDS budget take the general path below.
     const int Gmax = 512 / ipr;
     const int want = (M + kCUs - 1) / kCUs;
-    const int R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
+    const int G2 = (want + 1) / 2;
+    const bool two = G2 <= Gmax && 4 * G2 * ipr >= 3 * ((G2 * ipr + 63) / 64 * 64);
+    const int R = two || want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
     const int ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
-    int Ge = (want + R - 1) / R;
+    int Ge = two ? G2 : (want + R - 1) / R;
     if (Ge > Gmax) Ge = Gmax;
     const int RW = Ge * R;
     const size_t lds = one_lds_floats(nU, RW) * sizeof(float);
