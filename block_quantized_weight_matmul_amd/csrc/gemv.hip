@@ -521,11 +521,13 @@ __global__ __launch_bounds__(512) void k_gemv(GemvArgs a) {
 // products -- loads of item k+kAhead are issued just before item k is computed,
 // a scheduling barrier pinning the order -- so a wave computes the items that
 // have arrived instead of stalling on the issue of loads the memory system cannot
-// take yet.  Every item is computed and stored unconditionally (rows past the
+// take yet.  One item ahead measured faster than two, three or four on the
+// decode-layer shapes: more loads in flight per thread only lengthen the queue
+// in front of every wave's first item.  Every item is computed and stored unconditionally (rows past the
 // slice repeat its last row and store to a spare slot after the partials): a
 // branch around the products or the store would let the compiler sink the
 // products, and their loads, into it.
-constexpr int kAhead = 2;
+constexpr int kAhead = 1;
 constexpr int kXU = 36;        // floats per unit in the LDS image
 constexpr int kX1Rounds = 4;   // chunks per thread: 2 nU chunks, at least nU / 2 threads
 
@@ -795,6 +797,7 @@ struct Tables {
   GemvKernel dense[5][kNumBuckets];
   GemvKernel id[5][kIdBuckets];
   GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
+  int one_regs[5][2][3];    // their VGPRs per lane (512 when unknown)
   Tables() {
     fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
     fill_one<FMT_Q8_0>(one[FMT_Q8_0]);
@@ -813,6 +816,13 @@ struct Tables {
     fill_id<FMT_Q4_K>(id[FMT_Q4_K], idseq);
     fill_id<FMT_Q6_K>(id[FMT_Q6_K], idseq);
     fill_id<FMT_A4G64>(id[FMT_A4G64], idseq);
+    for (int f = 0; f < 5; ++f)
+      for (int h = 0; h < 2; ++h)
+        for (int r = 0; r < 3; ++r) {
+          hipFuncAttributes at{};
+          const bool ok = hipFuncGetAttributes(&at, reinterpret_cast<const void*>(one[f][h][r])) == hipSuccess;
+          one_regs[f][h][r] = ok && at.numRegs > 0 ? at.numRegs : 512;
+        }
   }
 };
 
@@ -866,20 +876,34 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
   const int M = static_cast<int>(m.M);
   const int ipr = nU / kRuns[m.fmt];
   if (N == 1 && ipr <= 512) {
-    // One token: G row groups (G * ipr <= 512 threads) x R rows per thread.
-    // Two workgroups per CU of one row per thread when that fills at least 3/4
-    // of their waves (the second workgroup's loads and products overlap the
-    // first one's reduction); otherwise about one workgroup per CU, R in
-    // {1, 2, 4} the smallest that covers M / 256 rows.  RW = G * R, so every
-    // thread has R rows to compute.  Shapes whose activation image and partials
-    // do not fit the LDS budget take the general path below.
+    // One token: G row groups (G * ipr <= 512 threads) x R rows per thread,
+    // RW = G * R rows per workgroup, so every thread has R rows to compute.
+    // Two workgroups per CU when R in {1, 2} makes G * ipr fill at least 3/4 of
+    // their waves and the kernel's registers let both sit on the CU at once (the
+    // second workgroup's loads and products overlap the first one's reduction);
+    // otherwise about one workgroup per CU, R in {1, 2, 4} the smallest that
+    // covers M / 256 rows.  Shapes whose activation image and partials do not
+    // fit the LDS budget take the general path below.
     const int Gmax = 512 / ipr;
     const int want = (M + kCUs - 1) / kCUs;
-    const int G2 = (want + 1) / 2;
-    const bool two = G2 <= Gmax && 4 * G2 * ipr >= 3 * ((G2 * ipr + 63) / 64 * 64);
-    const int R = two || want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
-    const int ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
-    int Ge = two ? G2 : (want + R - 1) / R;
+    const int xh = x_f16 ? 1 : 0;
+    auto two_fit = [&](int r, int ri) {
+      const int G2 = (want + 2 * r - 1) / (2 * r);
+      const int thr = (G2 * ipr + 63) / 64 * 64;
+      const int regs = (tables().one_regs[m.fmt][xh][ri] + 7) / 8 * 8;
+      const int waves_per_simd = (thr / 64 + 3) / 4;  // one workgroup's waves on each SIMD
+      return G2 <= Gmax && 4 * G2 * ipr >= 3 * thr && 2 * waves_per_simd * regs <= 512;
+    };
+    int R, ri, Ge;
+    if (two_fit(1, 0) || two_fit(2, 1)) {
+      R = two_fit(1, 0) ? 1 : 2;
+      ri = R - 1;
+      Ge = (want + 2 * R - 1) / (2 * R);
+    } else {
+      R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
+      ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
+      Ge = (want + R - 1) / R;
+    }
     if (Ge > Gmax) Ge = Gmax;
     const int RW = Ge * R;
     const size_t lds = one_lds_floats(nU, RW) * sizeof(float);
@@ -897,7 +921,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
       a.y = y;
       a.N = 1;
       const int threads = (Ge * ipr + 63) / 64 * 64;
-      hipLaunchKernelGGL(tables().one[m.fmt][x_f16 ? 1 : 0][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
+      hipLaunchKernelGGL(tables().one[m.fmt][xh][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
       return hipGetLastError();
     }
   }
