@@ -56,6 +56,8 @@ struct GemvArgs {
   int N;                // tokens (dense)
   const int32_t* ids;   // expert-indexed mode
   int S, x_per_slot, E;
+  int tok_groups;       // multi-token kernel: token groups of threads
+  int tok_pass;         // multi-token kernel: tokens staged per pass
 };
 
 template <int CTRL>
@@ -669,6 +671,173 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   reduce_rows(s_part, rows, 1, nU, RW, a.M, r0, tm, a.y);
 }
 
+// ---------------------------------------------------------------------------------------------
+// A few tokens (2 .. 32).  The one-token layout (thread = item column gi of row
+// group g, R rows g + G k) gains token groups: thread tg of TGN computes tokens
+// tg, tg + TGN, ... of each pass.  A pass stages the activations of TP tokens
+// (the most the LDS budget holds) as images like the one-token kernel's -- fp32
+// values, or the fp16 values themselves when the call's activations are fp16 --
+// then every thread decodes its rows' items once into code pairs and runs them
+// against each of its tokens, the activations of one (token, run) read once
+// from LDS for all R rows.  After the products the pass's outputs are reduced
+// as everywhere else, so the results are the bits of the other paths.  The
+// weight bytes stay in registers across passes.
+constexpr int kXNRounds = 4;   // chunks per thread when staging a pass
+
+// floats per staged unit: 32 values (fp32) or 32 halves in 16 floats (fp16),
+// then the two half sums and a pad
+template <bool XH> struct XImg { static constexpr int U = XH ? 20 : kXU; };
+
+template <int F, int R>
+__device__ __forceinline__ void multi_run(const MixPairs<F> (&pk)[R], const Unit (&o)[R][Item<F>::RUNS], int r,
+                                          const float (&x)[32], float sx0, float sx1, float (&v)[R]) {
+  float s[R][2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32 w = e & 1 ? pk[q].od[r][4 * h + k] : pk[q].ev[r][4 * h + k];
+          const float c = e < 2 ? code_lo(w) : code_hi(w);
+          const float xv = x[16 * h + 4 * k + e];
+          s[q][h] = k == 0 && e == 0 ? c * xv : __builtin_fmaf(c, xv, s[q][h]);
+        }
+  const float sc = static_cast<float>(1u << (24 - MixPairs<F>::sh(r)));
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const Unit& u = o[q][r];
+    v[q] = __builtin_fmaf(u.a0 * sc, s[q][0], __builtin_fmaf(u.b0, sx0, __builtin_fmaf(u.a1 * sc, s[q][1], u.b1 * sx1)));
+  }
+}
+
+template <int F, bool XH, int R>
+__global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
+  using It = Item<F>;
+  constexpr int RUNS = It::RUNS;
+  constexpr int XU = XImg<XH>::U;
+  const int RW = a.rows_per_wg;
+  const int r0 = blockIdx.x * RW;
+  const int rows = min(RW, a.M - r0);
+  const int nU = a.nU;
+  const int ipr = nU / RUNS;
+  const int G = a.chunk_units;
+  const int TGN = a.tok_groups;
+  const int TP = a.tok_pass;
+  const int n = a.N;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int gg = tid / ipr;            // row group + G * token group
+  const bool active = gg < G * TGN;
+  const int gi = active ? tid - gg * ipr : 0;
+  const int g = active ? gg % G : 0;
+  const int tg = active ? gg / G : TGN;  // inactive threads take no token
+  const u8* W = a.W;
+  const u32 rb = static_cast<u32>(a.row_bytes);
+  const int img = XU * nU;               // floats per token image
+  float* s_x = s_dyn;                    // TP images, then one spare unit
+  float* s_part = s_dyn + TP * img + XU;
+  const int spare_part = TP * RW * nU;
+
+  typename It::Raw wr[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int t0 = 0; t0 < n; t0 += TP) {
+    const int tp = min(TP, n - t0);
+    // stage the pass: chunk c = (token c / (2 nU), half unit c % (2 nU))
+    const int chunks = tp * 2 * nU;
+    uint4 xr[kXNRounds][4];
+#pragma unroll
+    for (int j = 0; j < kXNRounds; ++j) {
+      const int c = tid + j * nthr;
+      if (c < chunks) {
+        const int t = c / (2 * nU), cc = c - t * 2 * nU;
+        x1_fetch<XH>(reinterpret_cast<const u8*>(a.x) + static_cast<size_t>(t0 + t) * a.K * (XH ? 2 : 4), cc, xr[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kXNRounds; ++j) {
+      const int c = tid + j * nthr;
+      if (j * nthr < chunks) {
+        const int t = c / (2 * nU), cc = c - t * 2 * nU;
+        float* ub = c < chunks ? s_x + t * img + XU * (cc >> 1) : s_x + TP * img;
+        const int hf = c < chunks ? (cc & 1) : 0;
+        if constexpr (XH) {
+          // 16 halves as they are, and the half sum of their fp32 values
+          *reinterpret_cast<uint4*>(ub + 8 * hf) = xr[j][0];
+          *reinterpret_cast<uint4*>(ub + 8 * hf + 4) = xr[j][1];
+          typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+          float f[16];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const h8 h = __builtin_bit_cast(h8, xr[j][k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[8 * k + e] = static_cast<float>(h[e]);
+          }
+          ub[16 + hf] = half_sum16(f);
+        } else {
+          x1_put<false>(xr[j], ub + 16 * hf, ub + 32 + hf);
+        }
+      }
+    }
+    __syncthreads();
+
+    // decode the rows' items into code pairs once per pass
+    MixPairs<F> pk[R];
+    Unit o[R][RUNS];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      It::unpack(wr[k], o[k]);
+      pk[k].make(wr[k], o[k]);
+    }
+    for (int t = tg; t < tp; t += TGN) {
+#pragma unroll
+      for (int r = 0; r < RUNS; ++r) {
+        const int u = It::unit(gi, r);
+        const float* ub = s_x + t * img + XU * u;
+        float xv[32];
+        if constexpr (XH) {
+          typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const h8 h = __builtin_bit_cast(h8, *reinterpret_cast<const uint4*>(ub + 4 * k));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[8 * k + e] = static_cast<float>(h[e]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float4 f4 = *reinterpret_cast<const float4*>(ub + 4 * k);
+            xv[4 * k] = f4.x; xv[4 * k + 1] = f4.y; xv[4 * k + 2] = f4.z; xv[4 * k + 3] = f4.w;
+          }
+        }
+        const float2 sx = *reinterpret_cast<const float2*>(ub + (XH ? 16 : 32));
+        float v[R];
+        multi_run<F, R>(pk, o, r, xv, sx.x, sx.y, v);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+          const int row = g + G * k;
+          s_part[active && row < rows ? (t * RW + row) * nU + u : spare_part] = v[k];
+        }
+      }
+    }
+    __syncthreads();
+    const TokMap tm{nullptr, 1, 1};
+    reduce_rows(s_part, rows, tp, nU, RW, a.M, r0, tm, a.y + static_cast<size_t>(t0) * a.M);
+  }
+}
+
+// LDS floats of the multi-token kernel: TP token images and a spare unit, then
+// TP * RW * nU partial sums and a spare slot
+inline size_t multi_lds_floats(bool xh, int nU, int RW, int TP) {
+  const size_t U = xh ? XImg<true>::U : XImg<false>::U;
+  return static_cast<size_t>(TP) * U * nU + U + static_cast<size_t>(TP) * RW * nU + 1;
+}
+
 // Expert-indexed: blockIdx.y = rank k of the expert among the distinct valid ids
 // of this call (ascending), blockIdx.x = row slice.  Each workgroup builds, in LDS,
 // the presence bitmap of the ids, finds its expert and the (token, slot) pairs
@@ -793,12 +962,28 @@ constexpr void fill_one(GemvKernel (&t)[2][3]) {
   t[1][0] = k_gemv1<F, true, 1>;  t[1][1] = k_gemv1<F, true, 2>;  t[1][2] = k_gemv1<F, true, 4>;
 }
 
+template <int F>
+constexpr void fill_multi(GemvKernel (&t)[2]) {
+  if constexpr (F == FMT_Q8_0) {  // its codes carry a bias: the general path takes it
+    t[0] = t[1] = nullptr;
+  } else {
+    t[0] = k_gemvn<F, false, 1>;
+    t[1] = k_gemvn<F, true, 1>;
+  }
+}
+
 struct Tables {
   GemvKernel dense[5][kNumBuckets];
   GemvKernel id[5][kIdBuckets];
   GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   int one_regs[5][2][3];    // their VGPRs per lane (512 when unknown)
+  GemvKernel multi[5][2];  // [format][fp16 activations], one row per thread
   Tables() {
+    fill_multi<FMT_Q4_0>(multi[FMT_Q4_0]);
+    fill_multi<FMT_Q8_0>(multi[FMT_Q8_0]);
+    fill_multi<FMT_Q4_K>(multi[FMT_Q4_K]);
+    fill_multi<FMT_Q6_K>(multi[FMT_Q6_K]);
+    fill_multi<FMT_A4G64>(multi[FMT_A4G64]);
     fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
     fill_one<FMT_Q8_0>(one[FMT_Q8_0]);
     fill_one<FMT_Q4_K>(one[FMT_Q4_K]);
@@ -923,6 +1108,50 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
       const int threads = (Ge * ipr + 63) / 64 * 64;
       hipLaunchKernelGGL(tables().one[m.fmt][xh][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
       return hipGetLastError();
+    }
+  }
+  if (N >= 2 && m.fmt != FMT_Q8_0) {
+    // A few tokens: the one-token layout with one row per thread (two would
+    // spill registers with fp32 activations), about one workgroup per CU, TGN
+    // token groups filling up to 512 threads, TP tokens per pass as the LDS
+    // budget and kXNRounds staging rounds allow.
+    const int ipr2 = nU / kRuns[m.fmt];
+    const int Gmax = 512 / ipr2;
+    if (Gmax >= 1) {
+      const int want = (M + kCUs - 1) / kCUs;
+      const int R = 1;
+      int Ge = (want + R - 1) / R;
+      if (Ge > Gmax) Ge = Gmax;
+      const int RW = Ge * R;
+      const bool xh = x_f16 != 0;
+      int TP = N;
+      while (TP > 0 && multi_lds_floats(xh, nU, RW, TP) * sizeof(float) > static_cast<size_t>(kLdsBudget)) --TP;
+      int TGN = TP < 512 / (Ge * ipr2) ? TP : 512 / (Ge * ipr2);
+      if (TGN < 1) TGN = 1;
+      const int threads = (Ge * TGN * ipr2 + 63) / 64 * 64;
+      const int tp_rounds = kXNRounds * threads / (2 * nU);
+      if (TP > tp_rounds) TP = tp_rounds;
+      if (TP >= 1) TP = (N + (N + TP - 1) / TP - 1) / ((N + TP - 1) / TP);  // passes of equal size
+      if (TGN > TP) TGN = TP;
+      if (TP >= 1) {
+        GemvArgs a{};
+        a.W = m.blocks;
+        a.row_bytes = m.row_bytes;
+        a.M = M;
+        a.nU = nU;
+        a.K = static_cast<int>(m.K);
+        a.rows_per_wg = RW;
+        a.chunk_units = Ge;
+        a.x = x;
+        a.x_f16 = x_f16;
+        a.y = y;
+        a.N = N;
+        a.tok_groups = TGN;
+        a.tok_pass = TP;
+        const size_t lds = multi_lds_floats(xh, nU, RW, TP) * sizeof(float);
+        hipLaunchKernelGGL(tables().multi[m.fmt][xh ? 1 : 0], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
+        return hipGetLastError();
+      }
     }
   }
   // about one workgroup per CU

@@ -93,3 +93,27 @@ def test_gemv_deterministic():
     x = to_dev(np.random.default_rng(46).standard_normal((5, K)).astype(np.float32))
     a, b = to_host(qm.gemv(x)), to_host(qm.gemv(x))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("xdtype", [np.float32, np.float16])
+def test_gemv_tokens_long_rows(fmt, xdtype):
+    """Rows long enough that a call's activations are staged a few tokens at a
+    time (several passes, the last one shorter)."""
+    for K, N in ((8192, 3), (9728, 16)):
+        if K % oracle.block_weights(fmt) == 0:
+            _run(fmt, 300, K, N, xdtype, [47, K, N])
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemv_tokens_match_single_token_calls(fmt):
+    """Every path sums the same unit partials in the same order, so a call with N
+    tokens returns, bit for bit, what N one-token calls return."""
+    M, K, N = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048, 11
+    qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [48])), fmt, M, K)
+    for xdtype in (np.float32, np.float16):
+        x = to_dev(np.random.default_rng(48).standard_normal((N, K)).astype(xdtype))
+        full = to_host(qm.gemv(x))
+        for t in range(N):
+            one = to_host(qm.gemv(x[t:t + 1].contiguous()))
+            assert np.array_equal(full[t:t + 1].view(np.uint32), one.view(np.uint32)), (fmt, xdtype, t)
