@@ -306,19 +306,27 @@ def extra_small_decode(torch, q, W, args):
 
 
 def extra_prefill(torch, q, W, mats, args):
-    rot = Rotation(torch, [m["blob"] for m in mats], min_total=0, min_copies=1)
-    hs = [q.QMatrix(rot.slice(0, j), m["fmt"], m["M"], m["K"]) for j, m in enumerate(mats)]
+    # weight copies rotate over >1 GiB, as for the decode layer: at few tokens the
+    # path streams its weights, which must not come from a warm cache
+    rot = Rotation(torch, [m["blob"] for m in mats])
+    hss = [[q.QMatrix(rot.slice(c, j), m["fmt"], m["M"], m["K"]) for j, m in enumerate(mats)]
+           for c in range(rot.copies)]
     flops_tok = 2 * sum(m["M"] * m["K"] for m in mats)
     wbytes = sum(int(m["blob"].size) for m in mats)
     res = []
     for n in W.PREFILL_TOKENS:
         xs = [torch.from_numpy(W.prefill_x(j, n)).to("cuda") for j in range(len(mats))]
         ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
-        calls = max(1, min(args.calls, int(2e10 // (flops_tok * n)) or 1))
+        # the workspace of the K-split few-token calls (QMatrix.gemm's path)
+        wss = []
+        for j in range(len(mats)):
+            nb = q.qmm_gemm_workspace_bytes(hss[0][j].handle, n)
+            wss.append(torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None)
+        calls = max(1, min(args.calls, rot.copies, int(2e10 // (flops_tok * n)) or 1))
         per_tile = {}
         for tile in (32, 64):
-            g = capture(torch, lambda tile=tile: [q.qmm_gemm(hs[j].handle, xs[j], n, ys[j], tile)
-                                                  for _ in range(calls) for j in range(len(mats))])
+            g = capture(torch, lambda tile=tile: [q.qmm_gemm_ws(hss[c][j].handle, xs[j], n, ys[j], tile, wss[j])
+                                                  for c in range(calls) for j in range(len(mats))])
             per_tile[tile] = g
         ts = {32: [], 64: []}
         for r in range(args.rounds):
@@ -327,13 +335,15 @@ def extra_prefill(torch, q, W, mats, args):
                 ts[tile].append(time_graph(torch, per_tile[tile], 1) * 1e3 / calls)
         chosen = q.qmm_tile_for_tokens(n)
         us = {t: float(np.median(v)) for t, v in ts.items()}
-        res.append({"n": n, "chosen_tile": chosen, "us_per_layer": us[chosen],
+        res.append({"n": n, "chosen_tile": chosen, "k_split": any(w is not None for w in wss),
+                    "us_per_layer": us[chosen],
                     "us_tile32": us[32], "us_tile64": us[64], "ratio_64_over_32": us[64] / us[32],
                     "tflops": flops_tok * n / (us[chosen] * 1e-6) / 1e12,
                     "frac_mfma": flops_tok * n / (us[chosen] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
                     "weight_gbs": wbytes / (us[chosen] * 1e-6) / 1e9})
         del per_tile
-    return {"workload": "decode-layer shapes as prefill GEMM, fp16 tokens, auto tile", "results": res}
+    return {"workload": "decode-layer shapes as prefill GEMM, fp16 tokens, auto tile, weights rotated",
+            "copies": rot.copies, "results": res}
 
 
 def extra_moe(torch, q, W, args):

@@ -8,6 +8,7 @@ check tensor metadata, allocate outputs with torch and marshal pointers.
     qm = QMatrix(blocks_u8_cuda, "q4_k", M, K)
     y = qm.gemv(x)               # 1..32 tokens, fp32 accumulation
     y = qm.gemm(x, tile="auto")  # any N, fp16 matrix cores, 32/64-token tile
+                                 # (K split over a torch-allocated workspace for few tokens)
     y = qm_stack.gemm_id(x, ids) # expert-indexed matrix-vector
     w = qm.dequantize()          # exact fp32 weights (or fp16 staging values)
 """
@@ -20,7 +21,8 @@ from ._lib import DTYPES, LIB_PATH, QMM_OK, STATUS, TILES, TYPES, QmmError, chec
 
 __all__ = [
     "QMatrix", "QmmError", "LIB_PATH", "TYPES",
-    "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_id", "qmm_dequantize",
+    "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
+    "qmm_gemm_id", "qmm_dequantize",
     "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_block_weights", "qmm_block_bytes",
 ]
 
@@ -92,6 +94,19 @@ def qmm_gemm(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, stream=None) -
     check(lib.qmm_gemm(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), t, _stream(stream)))
 
 
+def qmm_gemm_workspace_bytes(h, N: int) -> int:
+    return lib.qmm_gemm_workspace_bytes(h, int(N))
+
+
+def qmm_gemm_ws(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, ws: torch.Tensor = None, stream=None) -> None:
+    t = TILES[tile] if tile in TILES else int(tile)
+    if ws is None:
+        wp, wb = ctypes.c_void_p(0), 0
+    else:
+        wp, wb = _dev_ptr(ws, "ws"), ws.numel() * ws.element_size()
+    check(lib.qmm_gemm_ws(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), t, wp, wb, _stream(stream)))
+
+
 def qmm_gemm_id(h, x: torch.Tensor, N: int, S: int, x_per_slot: int, ids: torch.Tensor, y: torch.Tensor,
                 stream=None) -> None:
     check(lib.qmm_gemm_id(h, _dev_ptr(x, "x"), _xt(x), int(N), int(S), int(x_per_slot),
@@ -160,7 +175,9 @@ class QMatrix:
         self._check_x(x, 2)
         N = x.shape[0]
         y = out if out is not None else torch.empty((N, self.M), dtype=torch.float32, device=x.device)
-        qmm_gemm(self._h, x, N, y, tile)
+        nb = qmm_gemm_workspace_bytes(self._h, N)
+        ws = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=x.device) if nb else None
+        qmm_gemm_ws(self._h, x, N, y, tile, ws)
         return y
 
     def gemm_id(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:

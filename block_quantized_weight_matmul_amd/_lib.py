@@ -1,6 +1,6 @@
 """ctypes loader for libqmm.so (the C ABI of include/qmm.h).
 
-The library is built in-tree by ``python -m block_quantized_weight_matmul_amd.build``.
+The library is built in-tree by ``python block_quantized_weight_matmul_amd/build.py``.
 There is no fallback: importing this module without the built library raises.
 """
 
@@ -28,7 +28,7 @@ class QmmError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m block_quantized_weight_matmul_amd.build`")
+            f"{LIB_PATH} is not built; run `python block_quantized_weight_matmul_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     sigs = {
@@ -36,6 +36,8 @@ def _load():
         "qmm_destroy": (c_int, [vp]),
         "qmm_gemv": (c_int, [vp, vp, c_int, i64, vp, vp]),
         "qmm_gemm": (c_int, [vp, vp, c_int, i64, vp, c_int, vp]),
+        "qmm_gemm_ws": (c_int, [vp, vp, c_int, i64, vp, c_int, vp, ctypes.c_size_t, vp]),
+        "qmm_gemm_workspace_bytes": (ctypes.c_size_t, [vp, i64]),
         "qmm_gemm_id": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, vp]),
         "qmm_dequantize": (c_int, [vp, i64, vp, c_int, vp]),
         "qmm_tile_for_tokens": (c_int, [i64]),

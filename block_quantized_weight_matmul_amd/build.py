@@ -1,6 +1,6 @@
 """Build libqmm.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m block_quantized_weight_matmul_amd.build [-v]
+    python block_quantized_weight_matmul_amd/build.py [-v]
 
 Every HIP source under csrc/ is compiled to an object under _build/ (in
 parallel), then linked into block_quantized_weight_matmul_amd/libqmm.so.

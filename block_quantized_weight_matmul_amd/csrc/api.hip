@@ -179,7 +179,41 @@ qmm_status qmm_gemm(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N,
   if (N == 0) return ok();
   if ((s = check_device(h)) != QMM_OK) return s;
   const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
-  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e =
+      qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, nullptr, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return ok();
+}
+
+size_t qmm_gemm_workspace_bytes(const qmm_matrix* h, int64_t N) {
+  if (!h || h->d.n_experts != 1 || N <= 0 || N > (1LL << 24) || h->d.K >= qmm::kMaxGemmK) return 0;
+  return qmm::gemm_workspace_bytes(h->d, N);
+}
+
+qmm_status qmm_gemm_ws(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N, float* y, qmm_tile tile,
+                       void* ws, size_t ws_bytes, qmm_stream_t stream) {
+  if (!h) return fail(QMM_E_ARG, "handle is NULL");
+  if (h->d.n_experts != 1) return fail(QMM_E_ARG, "qmm_gemm_ws needs a handle with n_experts == 1");
+  if (tile != QMM_TILE_AUTO && tile != QMM_TILE_32 && tile != QMM_TILE_64)
+    return fail(QMM_E_ARG, "tile must be QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64 (got %d)", static_cast<int>(tile));
+  if (N < 0 || N > (1LL << 24))
+    return fail(QMM_E_SHAPE, "qmm_gemm_ws takes 0..2^24 tokens (got %lld)", static_cast<long long>(N));
+  if (h->d.K >= qmm::kMaxGemmK)
+    return fail(QMM_E_SHAPE, "qmm_gemm_ws takes K below %lld (handle has K=%lld)",
+                static_cast<long long>(qmm::kMaxGemmK), static_cast<long long>(h->d.K));
+  qmm_status s;
+  if ((s = check_x(x, xt)) != QMM_OK || (s = check_y(y)) != QMM_OK) return s;
+  if (N == 0) return ok();
+  const size_t need = qmm::gemm_workspace_bytes(h->d, N);
+  if (need > 0) {
+    if (!ws) return fail(QMM_E_ARG, "ws is NULL; this call needs %zu bytes", need);
+    if (ws_bytes < need) return fail(QMM_E_ARG, "ws holds %zu bytes; this call needs %zu", ws_bytes, need);
+    if (!aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
+  }
+  if ((s = check_device(h)) != QMM_OK) return s;
+  const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
+  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, need > 0 ? static_cast<float*>(ws) : nullptr,
+                                        reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }

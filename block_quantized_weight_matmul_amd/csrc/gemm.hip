@@ -27,6 +27,7 @@
 // operands over the same 32-deep steps in the same order, whatever T, TT and
 // RB are; T only changes how many padding blocks of the last super-tile are
 // computed (and never stored).
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -48,6 +49,8 @@ struct GemmArgs {
   int y_vec;        // y rows can take 16-byte stores (M % 4 == 0, y 16-byte aligned)
   int T;            // token tile (32 or 64)
   int n_row_tiles;  // blockIdx.x = super_tile * n_row_tiles + row_tile
+  int split_stages; // K stages per split (blockIdx.y = split); all of K when unsplit
+  u64 split_floats; // floats between the splits' partial outputs (0 when unsplit)
 };
 
 constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
@@ -407,8 +410,9 @@ __device__ __forceinline__ void stage_barrier() {
 // without copies.
 template <int F, int RB, int TT, bool XF16, bool FULL>
 __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT * kKS], floatx4 (&acc)[RB][TT / 16],
-                                       const u32 (&row_off)[RB], int tok0, int ntb, int o0, int o1, int tid, int g) {
-  const int nstages = (a.nU + 1) >> 1;
+                                       const u32 (&row_off)[RB], int tok0, int ntb, int o0, int o1, int tid, int g,
+                                       int sb, int nstages) {
+  // stages sb .. sb + nstages - 1 of K; s below counts from 0 within them
   AStage<F> w0[RB], w1[RB];
   XStage<TT, XF16> x0, x1;
   half8 A0[RB][2], A1[RB][2];
@@ -419,18 +423,20 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
 
   // a stage past K (K / 32 odd, last stage) has its activations read clamped and
   // cleared, and its second unit's weights zeroed; LAST: s may be such a stage
-  auto tail = [&](int s) { return kKS * s + kKS > a.K; };
+  auto tail = [&](int s) { return kKS * (sb + s) + kKS > a.K; };
   auto fetch_w = [&](int s, AStage<F>(&w)[RB]) {
 #pragma unroll
-    for (int b = 0; b < RB; ++b) w[b].load(a.W, row_off[b], 2 * s, a.nU, g);
+    for (int b = 0; b < RB; ++b) w[b].load(a.W, row_off[b], 2 * (sb + s), a.nU, g);
   };
-  auto fetch_x = [&](int s, XStage<TT, XF16>& xs, bool last) { xs.load(xb, xl, a.K, kKS * s, tid, last && tail(s)); };
+  auto fetch_x = [&](int s, XStage<TT, XF16>& xs, bool last) {
+    xs.load(xb, xl, a.K, kKS * (sb + s), tid, last && tail(s));
+  };
   auto put = [&](int s, const XStage<TT, XF16>& xs, bool last) {
     xs.store(sX[s & 1], tid);
-    if (last && tail(s)) clear_k_tail<TT>(sX[s & 1], tid, a.K - kKS * s);
+    if (last && tail(s)) clear_k_tail<TT>(sX[s & 1], tid, a.K - kKS * (sb + s));
   };
   auto decode = [&](int s, AStage<F>(&w)[RB], half8(&A)[RB][2], bool last) {
-    if (last && 2 * s + 1 == a.nU) {
+    if (last && 2 * (sb + s) + 1 == a.nU) {
 #pragma unroll
       for (int b = 0; b < RB; ++b) w[b].zero_second(g);
     }
@@ -515,10 +521,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NTB; ++t) acc[b][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // split blockIdx.y takes K stages [sb, sb + ns) and writes its partial products
+  // to its own [N, M] slab of the workspace (y itself when unsplit)
+  const int all = (a.nU + 1) >> 1;
+  const int sb = blockIdx.y * a.split_stages;
+  const int ns = min(a.split_stages, all - sb);
+  float* const yo = a.y + blockIdx.y * a.split_floats;
   if (ntb == NTB)
-    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g);
+    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g, sb, ns);
   else
-    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g);
+    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g, sb, ns);
 
   // D[4*(l/16) + v][l % 16] of block (b, t): row rw0 + 16b + 4g + v, token tok0 + 16t + l % 16
 #pragma unroll
@@ -528,7 +540,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const int r = rw0 + 16 * b + 4 * g;
-        float* yp = a.y + (u64)tok * a.M + r;
+        float* yp = yo + (u64)tok * a.M + r;
         if (a.y_vec && r + 3 < a.M) {
           *reinterpret_cast<float4*>(yp) = make_float4(acc[b][t][0], acc[b][t][1], acc[b][t][2], acc[b][t][3]);
         } else {
@@ -537,6 +549,30 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
             if (r + v < a.M) yp[v] = acc[b][t][v];
         }
       }
+    }
+  }
+}
+
+// y = sum of the S partial slabs of a split call, in split order (so the result
+// does not depend on which workgroup finished first).
+__global__ __launch_bounds__(256) void k_split_sum(const float* ws, int S, u64 stride, u64 count, int vec,
+                                                   float* y) {
+  const u64 i0 = static_cast<u64>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const u64 step = static_cast<u64>(gridDim.x) * blockDim.x;
+  if (vec) {
+    for (u64 i = i0; 4 * i < count; i += step) {
+      float4 v = reinterpret_cast<const float4*>(ws)[i];
+      for (int s = 1; s < S; ++s) {
+        const float4 w = reinterpret_cast<const float4*>(ws + s * stride)[i];
+        v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+      }
+      reinterpret_cast<float4*>(y)[i] = v;
+    }
+  } else {
+    for (u64 i = i0; i < count; i += step) {
+      float v = ws[i];
+      for (int s = 1; s < S; ++s) v += ws[s * stride + i];
+      y[i] = v;
     }
   }
 }
@@ -569,8 +605,33 @@ GemmKernel pick(int RB, int TT, bool xf16) {
 constexpr int64_t kCUs = 256;
 }  // namespace
 
-hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile,
+// K splits for N tokens: few tokens leave too few (row, token) tiles to fill the
+// chip, so the K stages are divided among that many more workgroups, at least
+// two stages each.  A function of the shape and N only (not of the tile), so both
+// tiles split alike and stay bit-identical.
+GemmSplit gemm_split(const MatDesc& m, int64_t N) {
+  GemmSplit sp{1, static_cast<int>((m.K / 32 + 1) / 2)};
+  const int64_t base = ((m.M + 63) / 64) * ((N + 63) / 64);
+  const int64_t want = m.fmt == FMT_Q6_K ? kCUs : 2 * kCUs;
+  if (N <= 0 || 2 * base >= want) return sp;
+  const int64_t nst = sp.stages;
+  int64_t S = (want + base - 1) / base;
+  if (S > nst / 2) S = nst / 2;
+  if (S < 2) return sp;
+  const int64_t per = (nst + S - 1) / S;
+  sp.stages = static_cast<int>(per);
+  sp.splits = static_cast<int>((nst + per - 1) / per);
+  return sp;
+}
+
+size_t gemm_workspace_bytes(const MatDesc& m, int64_t N) {
+  const GemmSplit sp = gemm_split(m, N);
+  return sp.splits > 1 ? static_cast<size_t>(sp.splits) * N * m.M * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t st) {
+  const GemmSplit sp = ws ? gemm_split(m, N) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
   GemmArgs a{};
   a.W = m.blocks;
   a.row_bytes = static_cast<u32>(m.row_bytes);
@@ -582,6 +643,9 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   a.y = y;
   a.y_vec = (m.M % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0);
   a.T = tile;
+  a.split_stages = sp.stages;
+  a.split_floats = sp.splits > 1 ? static_cast<u64>(N) * static_cast<u64>(m.M) : 0;
+  if (sp.splits > 1) a.y = ws;
   // Rows x tokens per workgroup: the first shape, in order of decreasing reuse,
   // that gives two workgroups per CU (one for Q6_K, whose wider decode favours
   // reuse over parallelism), else 64 x 64.  Measured on the decode-layer shapes.
@@ -592,6 +656,7 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   const bool xf16 = x_f16 != 0;
   int RB = 1, TT = 64;
   for (const auto& c : kShapes) {
+    if (sp.splits > 1) break;  // split calls take the 64 x 64 shape
     if (!shape_ok(m.fmt, xf16, c[0], c[1])) continue;
     if (c[1] > 64 && padded <= c[1] / 2) continue;  // a super-tile at most half used
     if (wgs(c[0], c[1]) >= want) {
@@ -613,7 +678,16 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   a.n_row_tiles = static_cast<int>((m.M + 64 * RB - 1) / (64 * RB));
   const int64_t blocks = static_cast<int64_t>(a.n_row_tiles) * ((N + TT - 1) / TT);
   if (blocks > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(blocks), sp.splits), dim3(256), 0, st, a);
+  if (sp.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const u64 count = static_cast<u64>(N) * static_cast<u64>(m.M);
+    const int vec = (count % 4 == 0) && ((reinterpret_cast<uintptr_t>(y) & 15) == 0) ? 1 : 0;
+    const u64 items = vec ? count / 4 : count;
+    const unsigned grid = static_cast<unsigned>(std::min<u64>((items + 255) / 256, 2048));
+    hipLaunchKernelGGL(k_split_sum, dim3(grid), dim3(256), 0, st, ws, sp.splits, a.split_floats, count, vec, y);
+  }
   return hipGetLastError();
 }
 

@@ -26,7 +26,16 @@ hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);
 hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
                           const int32_t* ids, float* y, hipStream_t s);
-hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile,
+// K splits of the matrix-matrix path for N tokens (splits = 1: unsplit)
+struct GemmSplit {
+  int splits;  // workgroups along K
+  int stages;  // 64-deep K stages per split
+};
+GemmSplit gemm_split(const MatDesc& m, int64_t N);
+size_t gemm_workspace_bytes(const MatDesc& m, int64_t N);
+// ws: workspace of gemm_workspace_bytes(m, N) bytes for a split call, or nullptr
+// (unsplit)
+hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t s);
 
 }  // namespace qmm

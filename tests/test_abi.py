@@ -97,3 +97,8 @@ def test_binding_refuses_bad_type_name():
     with pytest.raises(ValueError):
         q.qmm_row_bytes("q5_1", 256)
     assert q.qmm_row_bytes("q6_k", 256) == 210
+
+
+def test_workspace_query_without_handle():
+    L = _lib()
+    assert L.lib.qmm_gemm_workspace_bytes(None, 7) == 0

@@ -114,3 +114,39 @@ def test_gemm_deterministic_and_zero_tokens():
     y = torch.full((1, M), 3.0, device="cuda")
     q.qmm_gemm(qm.handle, xd, 0, y, 0)
     assert np.all(to_host(y) == 3.0)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_split_and_unsplit(fmt):
+    """qmm_gemm runs every K stage in one workgroup; qmm_gemm_ws (what QMatrix.gemm
+    calls) divides K among workgroups for few tokens and sums the partial slabs in
+    split order.  Both meet the bound, both are tile-identical, and the split call
+    is deterministic."""
+    bw = oracle.block_weights(fmt)
+    K = 2560 if 2560 % bw == 0 else 2048
+    M = 200
+    for N in (7, 33, 130):
+        blob, w, x = _data(fmt, N, M, K, np.float16, [56, N])
+        qm = q.QMatrix(to_dev(blob), fmt, M, K)
+        xd = to_dev(x)
+        assert q.qmm_gemm_workspace_bytes(qm.handle, N) > 0, "few tokens should split K"
+        y_ref, S = oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w)
+        outs = {}
+        for t in (32, 64):
+            y = torch.empty((N, M), device="cuda")
+            q.qmm_gemm(qm.handle, xd, N, y, t)
+            outs[("unsplit", t)] = to_host(y)
+            outs[("split", t)] = to_host(qm.gemm(xd, tile=t))
+        for (kind, t), y in outs.items():
+            assert_within(y, y_ref, S, TOL, f"gemm {kind} {fmt} N={N} tile={t}")
+        for kind in ("unsplit", "split"):
+            assert count_differences(outs[(kind, 32)], outs[(kind, 64)]) == 0, (fmt, N, kind)
+        assert count_differences(outs[("split", 64)], to_host(qm.gemm(xd, tile=64))) == 0
+
+
+def test_gemm_workspace_is_zero_for_many_tokens():
+    fmt, M, K = "q4_k", 4096, 2560
+    qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [57])), fmt, M, K)
+    assert q.qmm_gemm_workspace_bytes(qm.handle, 2048) == 0
+    assert q.qmm_gemm_workspace_bytes(qm.handle, 7) > 0
+    assert q.qmm_gemm_workspace_bytes(qm.handle, 0) == 0
