@@ -580,14 +580,14 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* ws, int S, u64 s
 namespace {
 typedef void (*GemmKernel)(GemmArgs);
 
-// Workgroup shapes (RB, TT): 128 rows x 128 tokens, 64 x 128 and 64 x 64.  The
-// first two amortise each decoded weight over 128 tokens; the last gives small
-// problems more workgroups.  Q6_K's raw bytes and fp32 activations (held twice
+// Workgroup shapes (RB, TT): 128 rows x 128 tokens, 64 x 128, 64 x 64 and 64 x 32.
+// The first two amortise each decoded weight over 128 tokens; 64 x 64 gives small
+// problems more workgroups; 64 x 32 serves K-split calls padded to 32 tokens.  Q6_K's raw bytes and fp32 activations (held twice
 // as wide while in flight) leave no room for the 128 x 128 shape within 256
 // registers per lane.
 constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
   if (RB == 2) return TT == 128 && F != FMT_Q6_K && xf16;
-  return TT == 64 || TT == 128;
+  return TT == 32 || TT == 64 || TT == 128;
 }
 
 template <int F, bool XF16, int RB, int TT>
@@ -598,8 +598,13 @@ GemmKernel kernel_if_ok() {
 
 template <int F>
 GemmKernel pick(int RB, int TT, bool xf16) {
-  if (xf16) return RB == 2 ? kernel_if_ok<F, true, 2, 128>() : TT == 128 ? kernel_if_ok<F, true, 1, 128>() : kernel_if_ok<F, true, 1, 64>();
-  return RB == 2 ? kernel_if_ok<F, false, 2, 128>() : TT == 128 ? kernel_if_ok<F, false, 1, 128>() : kernel_if_ok<F, false, 1, 64>();
+  if (xf16)
+    return RB == 2 ? kernel_if_ok<F, true, 2, 128>()
+         : TT == 128 ? kernel_if_ok<F, true, 1, 128>()
+         : TT == 64 ? kernel_if_ok<F, true, 1, 64>() : kernel_if_ok<F, true, 1, 32>();
+  return RB == 2 ? kernel_if_ok<F, false, 2, 128>()
+       : TT == 128 ? kernel_if_ok<F, false, 1, 128>()
+       : TT == 64 ? kernel_if_ok<F, false, 1, 64>() : kernel_if_ok<F, false, 1, 32>();
 }
 
 constexpr int64_t kCUs = 256;
@@ -654,9 +659,11 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   static const int kShapes[3][2] = {{2, 128}, {1, 128}, {1, 64}};
   const int64_t want = m.fmt == FMT_Q6_K ? kCUs : 2 * kCUs;
   const bool xf16 = x_f16 != 0;
-  int RB = 1, TT = 64;
+  // split calls take 64 rows x 64 tokens, or x 32 when the call pads to 32:
+  // activations of absent tokens are not staged then
+  int RB = 1, TT = sp.splits > 1 && padded <= 32 ? 32 : 64;
   for (const auto& c : kShapes) {
-    if (sp.splits > 1) break;  // split calls take the 64 x 64 shape
+    if (sp.splits > 1) break;
     if (!shape_ok(m.fmt, xf16, c[0], c[1])) continue;
     if (c[1] > 64 && padded <= c[1] / 2) continue;  // a super-tile at most half used
     if (wgs(c[0], c[1]) >= want) {
