@@ -713,20 +713,17 @@ __device__ __forceinline__ void multi_run(const MixPairs<F> (&pk)[R], const Unit
   }
 }
 
-template <int F, bool XH, int R>
-__global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
+// Rows [r0, r0 + rows) of the matrix at W against the n tokens of tm (their
+// activation rows tm.x(t), output rows tm.y(t)); G row groups x TGN token groups
+// of ipr threads, R rows per thread, TP tokens per pass.
+template <int F, bool XH, int R, int XRND>
+__device__ __forceinline__ void multi_rows(const GemvArgs& a, const u8* W, int r0, int rows, int RW, int G, int TGN,
+                                           int TP, const TokMap& tm, int n, float* lds) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
   constexpr int XU = XImg<XH>::U;
-  const int RW = a.rows_per_wg;
-  const int r0 = blockIdx.x * RW;
-  const int rows = min(RW, a.M - r0);
   const int nU = a.nU;
   const int ipr = nU / RUNS;
-  const int G = a.chunk_units;
-  const int TGN = a.tok_groups;
-  const int TP = a.tok_pass;
-  const int n = a.N;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int gg = tid / ipr;            // row group + G * token group
@@ -734,11 +731,10 @@ __global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
   const int gi = active ? tid - gg * ipr : 0;
   const int g = active ? gg % G : 0;
   const int tg = active ? gg / G : TGN;  // inactive threads take no token
-  const u8* W = a.W;
   const u32 rb = static_cast<u32>(a.row_bytes);
   const int img = XU * nU;               // floats per token image
-  float* s_x = s_dyn;                    // TP images, then one spare unit
-  float* s_part = s_dyn + TP * img + XU;
+  float* s_x = lds;                      // TP images, then one spare unit
+  float* s_part = lds + TP * img + XU;
   const int spare_part = TP * RW * nU;
 
   typename It::Raw wr[R];
@@ -750,17 +746,18 @@ __global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
     const int tp = min(TP, n - t0);
     // stage the pass: chunk c = (token c / (2 nU), half unit c % (2 nU))
     const int chunks = tp * 2 * nU;
-    uint4 xr[kXNRounds][4];
+    uint4 xr[XRND][4];
 #pragma unroll
-    for (int j = 0; j < kXNRounds; ++j) {
+    for (int j = 0; j < XRND; ++j) {
       const int c = tid + j * nthr;
       if (c < chunks) {
         const int t = c / (2 * nU), cc = c - t * 2 * nU;
-        x1_fetch<XH>(reinterpret_cast<const u8*>(a.x) + static_cast<size_t>(t0 + t) * a.K * (XH ? 2 : 4), cc, xr[j]);
+        const size_t row = static_cast<size_t>(tm.x(t0 + t));
+        x1_fetch<XH>(reinterpret_cast<const u8*>(a.x) + row * a.K * (XH ? 2 : 4), cc, xr[j]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kXNRounds; ++j) {
+    for (int j = 0; j < XRND; ++j) {
       const int c = tid + j * nthr;
       if (j * nthr < chunks) {
         const int t = c / (2 * nU), cc = c - t * 2 * nU;
@@ -795,6 +792,17 @@ __global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
       pk[k].make(wr[k], o[k]);
     }
     for (int t = tg; t < tp; t += TGN) {
+      // the pairs stay fp16 codes widened inside fma_mix: converted once per pass
+      // they would hold 32 registers per run and row
+#pragma unroll
+      for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int r = 0; r < RUNS; ++r)
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            pk[k].ev[r][w] = opaque(pk[k].ev[r][w]);
+            pk[k].od[r][w] = opaque(pk[k].od[r][w]);
+          }
 #pragma unroll
       for (int r = 0; r < RUNS; ++r) {
         const int u = It::unit(gi, r);
@@ -826,9 +834,22 @@ __global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
       }
     }
     __syncthreads();
-    const TokMap tm{nullptr, 1, 1};
-    reduce_rows(s_part, rows, tp, nU, RW, a.M, r0, tm, a.y + static_cast<size_t>(t0) * a.M);
+    if (tm.pairs) {
+      const TokMap pm{tm.pairs + t0, tm.S, tm.per_slot};
+      reduce_rows(s_part, rows, tp, nU, RW, a.M, r0, pm, a.y);
+    } else {
+      reduce_rows(s_part, rows, tp, nU, RW, a.M, r0, tm, a.y + static_cast<size_t>(t0) * a.M);
+    }
   }
+}
+
+template <int F, bool XH, int R>
+__global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
+  const int RW = a.rows_per_wg;
+  const int r0 = blockIdx.x * RW;
+  const TokMap tm{nullptr, 1, 1};
+  multi_rows<F, XH, R, kXNRounds>(a, a.W, r0, min(RW, a.M - r0), RW, a.chunk_units, a.tok_groups, a.tok_pass, tm,
+                                  a.N, s_dyn);
 }
 
 // LDS floats of the multi-token kernel: TP token images and a spare unit, then
@@ -845,28 +866,31 @@ inline size_t multi_lds_floats(bool xh, int nU, int RW, int TP) {
 constexpr int kIdBitmapWords = static_cast<int>(kMaxExperts / 32);
 constexpr int kIdMaxPairs = static_cast<int>(kMaxGemvTokens * kMaxSlots);
 
-template <int F, int NB>
-__global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
-  __shared__ u32 s_bits[kIdBitmapWords];
-  __shared__ int s_pairs[kIdMaxPairs];
-  __shared__ int s_expert, s_npairs, s_bad;
+// The workgroup's expert (rank blockIdx.y among the distinct valid ids of the
+// call, ascending; -1 if there are fewer) and the (token, slot) pairs routed to
+// it, in sh.pairs[0 .. sh.npairs).  Rank-0 workgroups also write the NaN rows of ids
+// outside [0, E) for their row slice.
+struct IdShared {
+  u32 bits[kIdBitmapWords];
+  int pairs[kIdMaxPairs];
+  int expert, npairs, bad;
+};
 
+__device__ __forceinline__ int id_route(const GemvArgs& a, int r0, int rows, IdShared& sh) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int P = a.N * a.S;
   const int nwords = (a.E + 31) >> 5;
-  const int r0 = blockIdx.x * a.rows_per_wg;
-  const int rows = min(a.rows_per_wg, a.M - r0);
 
-  for (int w = tid; w < nwords; w += nthr) s_bits[w] = 0u;
-  if (tid == 0) { s_expert = -1; s_npairs = 0; s_bad = 0; }
+  for (int w = tid; w < nwords; w += nthr) sh.bits[w] = 0u;
+  if (tid == 0) { sh.expert = -1; sh.npairs = 0; sh.bad = 0; }
   __syncthreads();
   for (int p = tid; p < P; p += nthr) {
     const int e = a.ids[p];
     if (e >= 0 && e < a.E)
-      atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+      atomicOr(&sh.bits[e >> 5], 1u << (e & 31));
     else
-      s_bad = 1;
+      sh.bad = 1;
   }
   __syncthreads();
 
@@ -877,7 +901,7 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
     const int wpl = (nwords + 63) >> 6;
     const int w0 = tid * wpl, w1 = min(nwords, w0 + wpl);
     int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(s_bits[w]);
+    for (int w = w0; w < w1; ++w) cnt += __popc(sh.bits[w]);
     int incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -888,10 +912,10 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
     if (k >= excl && k < incl) {
       int seen = excl;
       for (int w = w0; w < w1; ++w) {
-        u32 bits = s_bits[w];
+        u32 bits = sh.bits[w];
         while (bits) {
           const int b = __ffs(bits) - 1;
-          if (seen == k) s_expert = (w << 5) + b;
+          if (seen == k) sh.expert = (w << 5) + b;
           ++seen;
           bits &= bits - 1u;
         }
@@ -899,11 +923,11 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
     }
   }
   __syncthreads();
-  const int e = s_expert;
+  const int e = sh.expert;
 
   // Ids outside [0, E) have no matrix: their output rows are NaN (written by the
   // rank-0 workgroups, which exist for every row slice).
-  if (blockIdx.y == 0 && s_bad) {
+  if (blockIdx.y == 0 && sh.bad) {
     const float qnan = __builtin_nanf("");
     for (int i = tid; i < P * rows; i += nthr) {
       const int p = i / rows, r = i - p * rows;
@@ -911,22 +935,56 @@ __global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
       if (id < 0 || id >= a.E) a.y[(u64)p * a.M + r0 + r] = qnan;
     }
   }
-  if (e < 0) return;  // uniform over the workgroup
+  if (e < 0) return -1;  // uniform over the workgroup
 
+  // (pair order within the list does not matter: each pair's outputs are
+  // computed on their own)
   for (int p = tid; p < P; p += nthr)
-    if (a.ids[p] == e) s_pairs[atomicAdd(&s_npairs, 1)] = p;
+    if (a.ids[p] == e) sh.pairs[atomicAdd(&sh.npairs, 1)] = p;
   __syncthreads();
-  const int np = s_npairs;
+  return e;
+}
 
+// Expert-indexed: blockIdx.y = rank of the expert, blockIdx.x = row slice.  Each
+// workgroup builds, in LDS, the presence bitmap of the ids, finds its expert and
+// the (token, slot) pairs routed to it, and streams that expert's rows of its
+// slice once per NB pairs.
+template <int F, int NB>
+__global__ __launch_bounds__(512) void k_gemv_id(GemvArgs a) {
+  __shared__ IdShared sh;
+  const int r0 = blockIdx.x * a.rows_per_wg;
+  const int rows = min(a.rows_per_wg, a.M - r0);
+  const int e = id_route(a, r0, rows, sh);
+  if (e < 0) return;
+  const int np = sh.npairs;
   const u8* W = a.W + (u64)e * a.expert_bytes;
   for (int c = 0; c < np; c += NB) {
-    const TokMap tm{s_pairs + c, a.S, a.x_per_slot};
+    const TokMap tm{sh.pairs + c, a.S, a.x_per_slot};
     // (the K-quant formats stage activations directly: the pass loop leaves no
     // registers for the activation slots)
     gemv_rows<F, NB, F != FMT_Q4_K && F != FMT_Q6_K>(W, static_cast<u32>(a.row_bytes), a.M, a.nU, a.K, r0, rows,
                                                      a.rows_per_wg, a.chunk_units, a.x, a.x_f16, tm,
                                                      min(NB, np - c), a.y, s_dyn);
   }
+}
+
+// Expert-indexed through the few-token layout (formats whose codes carry no
+// bias): the pairs routed to the workgroup's expert are its tokens.  Rows per
+// thread: 4 for one-run items, 2 for two-run items (more would spill); one
+// staging round per pass.
+template <int F> constexpr int id_rows() { return Item<F>::RUNS == 1 ? 4 : 2; }
+
+template <int F, bool XH>
+__global__ __launch_bounds__(512) void k_gemvn_id(GemvArgs a) {
+  __shared__ IdShared sh;
+  const int RW = a.rows_per_wg;
+  const int r0 = blockIdx.x * RW;
+  const int rows = min(RW, a.M - r0);
+  const int e = id_route(a, r0, rows, sh);
+  if (e < 0) return;
+  const TokMap tm{sh.pairs, a.S, a.x_per_slot};
+  multi_rows<F, XH, id_rows<F>(), 1>(a, a.W + (u64)e * a.expert_bytes, r0, rows, RW, a.chunk_units, a.tok_groups,
+                                     a.tok_pass, tm, sh.npairs, s_dyn);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -963,12 +1021,14 @@ constexpr void fill_one(GemvKernel (&t)[2][3]) {
 }
 
 template <int F>
-constexpr void fill_multi(GemvKernel (&t)[2]) {
+constexpr void fill_multi(GemvKernel (&t)[2], GemvKernel (&ti)[2]) {
   if constexpr (F == FMT_Q8_0) {  // its codes carry a bias: the general path takes it
-    t[0] = t[1] = nullptr;
+    t[0] = t[1] = ti[0] = ti[1] = nullptr;
   } else {
     t[0] = k_gemvn<F, false, 1>;
     t[1] = k_gemvn<F, true, 1>;
+    ti[0] = k_gemvn_id<F, false>;
+    ti[1] = k_gemvn_id<F, true>;
   }
 }
 
@@ -978,12 +1038,13 @@ struct Tables {
   GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   int one_regs[5][2][3];    // their VGPRs per lane (512 when unknown)
   GemvKernel multi[5][2];  // [format][fp16 activations], one row per thread
+  GemvKernel multi_id[5][2];
   Tables() {
-    fill_multi<FMT_Q4_0>(multi[FMT_Q4_0]);
-    fill_multi<FMT_Q8_0>(multi[FMT_Q8_0]);
-    fill_multi<FMT_Q4_K>(multi[FMT_Q4_K]);
-    fill_multi<FMT_Q6_K>(multi[FMT_Q6_K]);
-    fill_multi<FMT_A4G64>(multi[FMT_A4G64]);
+    fill_multi<FMT_Q4_0>(multi[FMT_Q4_0], multi_id[FMT_Q4_0]);
+    fill_multi<FMT_Q8_0>(multi[FMT_Q8_0], multi_id[FMT_Q8_0]);
+    fill_multi<FMT_Q4_K>(multi[FMT_Q4_K], multi_id[FMT_Q4_K]);
+    fill_multi<FMT_Q6_K>(multi[FMT_Q6_K], multi_id[FMT_Q6_K]);
+    fill_multi<FMT_A4G64>(multi[FMT_A4G64], multi_id[FMT_A4G64]);
     fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
     fill_one<FMT_Q8_0>(one[FMT_Q8_0]);
     fill_one<FMT_Q4_K>(one[FMT_Q4_K]);
@@ -1185,6 +1246,57 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   // the grid is ranks x row slices: about two workgroups per CU over all the
   // active experts
   const int M = static_cast<int>(m.M);
+  if (m.fmt != FMT_Q8_0) {
+    // the few-token layout per expert: about two workgroups per CU over the
+    // active experts, each G row groups x id_rows rows per thread, the pairs
+    // staged TP at a time in one round
+    const int ipr = nU / kRuns[m.fmt];
+    const int Rk = kRuns[m.fmt] == 1 ? 4 : 2;
+    const int Gmax = 512 / ipr;
+    if (Gmax >= 1) {
+      const int slices_want = (2 * kCUs + ranks - 1) / ranks;
+      const int rows_want = (M + slices_want - 1) / slices_want;
+      int Ge = (rows_want + Rk - 1) / Rk;
+      if (Ge > Gmax) Ge = Gmax;
+      const int RW = Ge * Rk;
+      const bool xh = x_f16 != 0;
+      const int P = N * S;
+      int TP = P;
+      // (the routing tables take static LDS besides the dynamic budget)
+      const size_t budget = static_cast<size_t>(kLdsBudget) - sizeof(IdShared);
+      while (TP > 0 && multi_lds_floats(xh, nU, RW, TP) * sizeof(float) > budget) --TP;
+      int TGN = TP < 512 / (Ge * ipr) ? TP : 512 / (Ge * ipr);
+      if (TGN < 1) TGN = 1;
+      const int threads = (Ge * TGN * ipr + 63) / 64 * 64;
+      if (TP > threads / (2 * nU)) TP = threads / (2 * nU);
+      if (TGN > TP) TGN = TP;
+      if (TP >= 1) {
+        GemvArgs a{};
+        a.W = m.blocks;
+        a.row_bytes = m.row_bytes;
+        a.expert_bytes = m.row_bytes * static_cast<u64>(m.M);
+        a.M = M;
+        a.nU = nU;
+        a.K = static_cast<int>(m.K);
+        a.rows_per_wg = RW;
+        a.chunk_units = Ge;
+        a.x = x;
+        a.x_f16 = x_f16;
+        a.y = y;
+        a.N = N;
+        a.ids = ids;
+        a.S = S;
+        a.x_per_slot = x_per_slot;
+        a.E = static_cast<int>(m.n_experts);
+        a.tok_groups = TGN;
+        a.tok_pass = TP;
+        const size_t lds = multi_lds_floats(xh, nU, RW, TP) * sizeof(float);
+        hipLaunchKernelGGL(tables().multi_id[m.fmt][xh ? 1 : 0], dim3((M + RW - 1) / RW, ranks), dim3(threads), lds,
+                           st, a);
+        return hipGetLastError();
+      }
+    }
+  }
   const int slices = (2 * kCUs + ranks - 1) / ranks;
   // (256 threads: each workgroup streams a short slice, and two share a CU)
   const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + slices - 1) / slices, 256);
