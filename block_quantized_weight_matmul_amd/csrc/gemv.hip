@@ -36,6 +36,7 @@
 // row's partials in a fixed order (lane l adds units l, l+64, ...; then a
 // butterfly over the wave), so results are deterministic and independent of
 // the launch shape, and the dense and expert-indexed paths agree bit for bit.
+#include <type_traits>
 #include <utility>
 
 #include "decode.hpp"
@@ -738,11 +739,9 @@ __device__ __forceinline__ void multi_rows(const GemvArgs& a, const u8* W, int r
   const int spare_part = TP * RW * nU;
 
   typename It::Raw wr[R];
-#pragma unroll
-  for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  for (int t0 = 0; t0 < n; t0 += TP) {
+  // a pass; the first one issues the weight loads right after its activation
+  // loads, so the staging waits for the activations only
+  auto pass = [&](auto first, int t0) {
     const int tp = min(TP, n - t0);
     // stage the pass: chunk c = (token c / (2 nU), half unit c % (2 nU))
     const int chunks = tp * 2 * nU;
@@ -755,6 +754,11 @@ __device__ __forceinline__ void multi_rows(const GemvArgs& a, const u8* W, int r
         const size_t row = static_cast<size_t>(tm.x(t0 + t));
         x1_fetch<XH>(reinterpret_cast<const u8*>(a.x) + row * a.K * (XH ? 2 : 4), cc, xr[j]);
       }
+    }
+    if constexpr (decltype(first)::value) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < XRND; ++j) {
@@ -840,7 +844,9 @@ __device__ __forceinline__ void multi_rows(const GemvArgs& a, const u8* W, int r
     } else {
       reduce_rows(s_part, rows, tp, nU, RW, a.M, r0, tm, a.y + static_cast<size_t>(t0) * a.M);
     }
-  }
+  };
+  pass(std::true_type{}, 0);
+  for (int t0 = TP; t0 < n; t0 += TP) pass(std::false_type{}, t0);
 }
 
 template <int F, bool XH, int R>
