@@ -10,6 +10,7 @@ check tensor metadata, allocate outputs with torch and marshal pointers.
     y = qm.gemm(x, tile="auto")  # any N, fp16 matrix cores, 32/64-token tile
                                  # (K split over a torch-allocated workspace for few tokens)
     y = qm_stack.gemm_id(x, ids) # expert-indexed matrix-vector
+    y = qm_stack.gemm_id_tiled(x, ids)  # expert-indexed, matrix cores, any N
     w = qm.dequantize()          # exact fp32 weights (or fp16 staging values)
 """
 
@@ -22,7 +23,7 @@ from ._lib import DTYPES, LIB_PATH, QMM_OK, STATUS, TILES, TYPES, QmmError, chec
 __all__ = [
     "QMatrix", "QmmError", "LIB_PATH", "TYPES",
     "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
-    "qmm_gemm_id", "qmm_dequantize",
+    "qmm_gemm_id", "qmm_gemm_id_tiled", "qmm_dequantize",
     "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_block_weights", "qmm_block_bytes",
 ]
 
@@ -107,6 +108,13 @@ def qmm_gemm_ws(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, ws: torch.T
     check(lib.qmm_gemm_ws(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), t, wp, wb, _stream(stream)))
 
 
+def qmm_gemm_id_tiled(h, x: torch.Tensor, N: int, S: int, x_per_slot: int, ids: torch.Tensor, y: torch.Tensor,
+                      tile=0, stream=None) -> None:
+    t = TILES[tile] if tile in TILES else int(tile)
+    check(lib.qmm_gemm_id_tiled(h, _dev_ptr(x, "x"), _xt(x), int(N), int(S), int(x_per_slot),
+                                _dev_ptr(ids, "ids"), _dev_ptr(y, "y"), t, _stream(stream)))
+
+
 def qmm_gemm_id(h, x: torch.Tensor, N: int, S: int, x_per_slot: int, ids: torch.Tensor, y: torch.Tensor,
                 stream=None) -> None:
     check(lib.qmm_gemm_id(h, _dev_ptr(x, "x"), _xt(x), int(N), int(S), int(x_per_slot),
@@ -189,6 +197,18 @@ class QMatrix:
         x_per_slot = 1 if x.dim() == 3 else 0
         y = out if out is not None else torch.empty((N, S, self.M), dtype=torch.float32, device=x.device)
         qmm_gemm_id(self._h, x, N, S, x_per_slot, ids, y)
+        return y
+
+    def gemm_id_tiled(self, x: torch.Tensor, ids: torch.Tensor, tile="auto", out: torch.Tensor = None) -> torch.Tensor:
+        """Prefill-sized expert-indexed product on the matrix cores (any N): ids [N, S]
+        int32; x [N, S, K] or [N, K] -> y [N, S, M] fp32; tile "auto", 32 or 64."""
+        if ids.dtype != torch.int32 or ids.dim() != 2:
+            raise ValueError("ids must be an int32 [N, S] tensor")
+        self._check_x(x, 3)
+        N, S = ids.shape
+        x_per_slot = 1 if x.dim() == 3 else 0
+        y = out if out is not None else torch.empty((N, S, self.M), dtype=torch.float32, device=x.device)
+        qmm_gemm_id_tiled(self._h, x, N, S, x_per_slot, ids, y, tile)
         return y
 
     def dequantize(self, expert: int = 0, dtype=torch.float32) -> torch.Tensor:

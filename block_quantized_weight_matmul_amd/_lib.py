@@ -39,6 +39,7 @@ def _load():
         "qmm_gemm_ws": (c_int, [vp, vp, c_int, i64, vp, c_int, vp, ctypes.c_size_t, vp]),
         "qmm_gemm_workspace_bytes": (ctypes.c_size_t, [vp, i64]),
         "qmm_gemm_id": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, vp]),
+        "qmm_gemm_id_tiled": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, c_int, vp]),
         "qmm_dequantize": (c_int, [vp, i64, vp, c_int, vp]),
         "qmm_tile_for_tokens": (c_int, [i64]),
         "qmm_row_bytes": (ctypes.c_size_t, [c_int, i64]),

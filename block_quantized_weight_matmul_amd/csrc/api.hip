@@ -243,6 +243,39 @@ qmm_status qmm_gemm_id(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t
   return ok();
 }
 
+qmm_status qmm_gemm_id_tiled(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N, int64_t S,
+                             int x_per_slot, const int32_t* ids, float* y, qmm_tile tile, qmm_stream_t stream) {
+  if (!h) return fail(QMM_E_ARG, "handle is NULL");
+  if (h->d.n_experts > qmm::kMaxExperts)
+    return fail(QMM_E_SHAPE, "qmm_gemm_id_tiled takes at most %lld experts (handle has %lld)",
+                static_cast<long long>(qmm::kMaxExperts), static_cast<long long>(h->d.n_experts));
+  if (tile != QMM_TILE_AUTO && tile != QMM_TILE_32 && tile != QMM_TILE_64)
+    return fail(QMM_E_ARG, "tile must be QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64 (got %d)", static_cast<int>(tile));
+  if (S < 1 || S > qmm::kMaxSlots)
+    return fail(QMM_E_SHAPE, "qmm_gemm_id_tiled takes 1..%lld slots per token (got %lld)",
+                static_cast<long long>(qmm::kMaxSlots), static_cast<long long>(S));
+  if (N < 0 || N * S > qmm::kMaxGemmIdPairs)
+    return fail(QMM_E_SHAPE, "qmm_gemm_id_tiled takes 0..%lld (token, slot) pairs (got %lld x %lld)",
+                static_cast<long long>(qmm::kMaxGemmIdPairs), static_cast<long long>(N), static_cast<long long>(S));
+  if (h->d.K >= qmm::kMaxGemmK)
+    return fail(QMM_E_SHAPE, "qmm_gemm_id_tiled takes K below %lld (handle has K=%lld)",
+                static_cast<long long>(qmm::kMaxGemmK), static_cast<long long>(h->d.K));
+  if (x_per_slot != 0 && x_per_slot != 1) return fail(QMM_E_ARG, "x_per_slot must be 0 or 1");
+  const int64_t xrows = x_per_slot ? N * S : N;
+  if (xrows * h->d.K * (xt == QMM_F16 ? 2 : 4) >= (int64_t(1) << 32))
+    return fail(QMM_E_SHAPE, "qmm_gemm_id_tiled takes activations below 4 GiB");
+  qmm_status s;
+  if ((s = check_x(x, xt)) != QMM_OK || (s = check_y(y)) != QMM_OK) return s;
+  if (!ids) return fail(QMM_E_ARG, "ids is NULL");
+  if (!aligned(ids, 4)) return fail(QMM_E_ALIGN, "ids must be 4-byte aligned");
+  if (N == 0) return ok();
+  if ((s = check_device(h)) != QMM_OK) return s;
+  const hipError_t e = qmm::launch_gemm_id(h->d, x, xt == QMM_F16, N, S, x_per_slot, ids, y, static_cast<int>(tile),
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_id_tiled launch");
+  return ok();
+}
+
 qmm_status qmm_dequantize(const qmm_matrix* h, int64_t expert, void* out, qmm_dtype ot, qmm_stream_t stream) {
   if (!h) return fail(QMM_E_ARG, "handle is NULL");
   if (expert < 0 || expert >= h->d.n_experts)

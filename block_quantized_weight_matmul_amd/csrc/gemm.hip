@@ -51,6 +51,10 @@ struct GemmArgs {
   int n_row_tiles;  // blockIdx.x = super_tile * n_row_tiles + row_tile
   int split_stages; // K stages per split (blockIdx.y = split); all of K when unsplit
   u64 split_floats; // floats between the splits' partial outputs (0 when unsplit)
+  // expert-indexed (k_gemm_id): ids [N, S], E experts of expert_bytes each
+  const int32_t* ids;
+  int S, x_per_slot, E;
+  u64 expert_bytes;
 };
 
 constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
@@ -305,6 +309,16 @@ struct XLanes {
       off[c] = (static_cast<u32>(row) * static_cast<u32>(K) + 8u * (idx & 7)) * ES;
     }
   }
+  // gathered rows: token row i of the super-tile is activation row rows[i] (rows
+  // past nvalid repeat the last valid one); offsets from the activations' start
+  __device__ __forceinline__ void init_rows(int K, const int* rows, int nvalid, int tid) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int idx = tid + c * 256;
+      const int row = rows[min(idx >> 3, nvalid - 1)];
+      off[c] = (static_cast<u32>(row) * static_cast<u32>(K) + 8u * (idx & 7)) * ES;
+    }
+  }
   // byte offset of chunk c for stage base k0, with the K clamp of a tail stage
   __device__ __forceinline__ u32 at(int c, int K, int k0, int tid, bool tail) const {
     if (!tail) return off[c];
@@ -410,16 +424,12 @@ __device__ __forceinline__ void stage_barrier() {
 // without copies.
 template <int F, int RB, int TT, bool XF16, bool FULL>
 __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT * kKS], floatx4 (&acc)[RB][TT / 16],
-                                       const u32 (&row_off)[RB], int tok0, int ntb, int o0, int o1, int tid, int g,
-                                       int sb, int nstages) {
+                                       const u32 (&row_off)[RB], const XLanes<TT, XF16 ? 2 : 4>& xl, const u8* xb,
+                                       int ntb, int o0, int o1, int tid, int g, int sb, int nstages) {
   // stages sb .. sb + nstages - 1 of K; s below counts from 0 within them
   AStage<F> w0[RB], w1[RB];
   XStage<TT, XF16> x0, x1;
   half8 A0[RB][2], A1[RB][2];
-  constexpr int ES = XF16 ? 2 : 4;
-  XLanes<TT, ES> xl;
-  xl.init(a.K, a.N, tok0, tid);
-  const u8* xb = reinterpret_cast<const u8*>(a.x) + static_cast<u64>(tok0) * static_cast<u64>(a.K) * ES;
 
   // a stage past K (K / 32 odd, last stage) has its activations read clamped and
   // cleared, and its second unit's weights zeroed; LAST: s may be such a stage
@@ -527,10 +537,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
   const int sb = blockIdx.y * a.split_stages;
   const int ns = min(a.split_stages, all - sb);
   float* const yo = a.y + blockIdx.y * a.split_floats;
+  constexpr int ES = XF16 ? 2 : 4;
+  XLanes<TT, ES> xl;
+  xl.init(a.K, a.N, tok0, tid);
+  const u8* xb = reinterpret_cast<const u8*>(a.x) + static_cast<u64>(tok0) * static_cast<u64>(a.K) * ES;
   if (ntb == NTB)
-    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g, sb, ns);
+    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, sb, ns);
   else
-    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, tok0, ntb, o0, o1, tid, g, sb, ns);
+    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, sb, ns);
 
   // D[4*(l/16) + v][l % 16] of block (b, t): row rw0 + 16b + 4g + v, token tok0 + 16t + l % 16
 #pragma unroll
@@ -550,6 +564,185 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Expert-indexed matrix-matrix path (any number of tokens).  Grid = (64*RB-row
+// tiles) x (rank of the expert among the call's distinct valid ids).  A
+// workgroup finds its expert as the expert-indexed matrix-vector path does (id
+// bitmap in LDS, single-wave prefix scan), counts the (token, slot) pairs routed
+// to it in ascending pair order (each thread counts a contiguous segment of the
+// ids, then one exclusive scan), and runs the matrix-core loop over that
+// expert's rows for each super-tile of its pairs: the pairs' activation rows are
+// gathered into the staged tile, and output row p (the pair index) receives
+// the results.  The pairs are padded to the token tile per expert (the tile
+// rule applied to the expert's own pair count under QMM_TILE_AUTO).  Every
+// output is accumulated as in the dense path, so each output row is, bit for
+// bit, qmm_gemm of its expert on its activation row.
+constexpr int kMmIdBitmapWords = static_cast<int>(kMaxExperts / 32);
+
+struct MmIdShared {
+  u32 bits[kMmIdBitmapWords];
+  int base[256];       // exclusive prefix of the threads' segment counts
+  int pair[128];       // pair index of each token of the current super-tile
+  int xrow[128];       // its activation row
+  int expert, count, bad;
+};
+
+__device__ __forceinline__ int tile_for_count(int n) {
+  const int p64 = (n + 63) / 64 * 64 - n, p32 = (n + 31) / 32 * 32 - n;
+  return p64 <= p32 ? 64 : 32;
+}
+
+template <int F, int RB, int TT, bool XF16>
+__global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
+  constexpr int NTB = TT / 16;
+  __shared__ __attribute__((aligned(16))) _Float16 sX[2][TT * kKS];
+  __shared__ MmIdShared sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int P = a.N * a.S;
+  const int nwords = (a.E + 31) >> 5;
+
+  // presence bitmap of the valid ids
+  for (int w = tid; w < nwords; w += 256) sh.bits[w] = 0u;
+  if (tid == 0) { sh.expert = -1; sh.bad = 0; }
+  __syncthreads();
+  for (int p = tid; p < P; p += 256) {
+    const int e = a.ids[p];
+    if (e >= 0 && e < a.E)
+      atomicOr(&sh.bits[e >> 5], 1u << (e & 31));
+    else
+      sh.bad = 1;
+  }
+  __syncthreads();
+  // the blockIdx.y-th set bit (first wave)
+  if (tid < 64) {
+    const int wpl = (nwords + 63) >> 6;
+    const int w0 = tid * wpl, w1 = min(nwords, w0 + wpl);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sh.bits[w]);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (tid >= off) incl += v;
+    }
+    const int excl = incl - cnt;
+    const int k = blockIdx.y;
+    if (k >= excl && k < incl) {
+      int seen = excl;
+      for (int w = w0; w < w1; ++w) {
+        u32 bits = sh.bits[w];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          if (seen == k) sh.expert = (w << 5) + b;
+          ++seen;
+          bits &= bits - 1u;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int e = sh.expert;
+  const int r_lo = blockIdx.x * 64 * RB;
+  const int r_hi = min(a.M, r_lo + 64 * RB);
+  // ids outside [0, E): NaN rows, written by the rank-0 workgroup of each row tile
+  if (blockIdx.y == 0 && sh.bad) {
+    const float qnan = __builtin_nanf("");
+    const int nr = r_hi - r_lo;
+    for (int i = tid; i < P * nr; i += 256) {
+      const int p = i / nr, r = r_lo + (i - p * nr);
+      const int id = a.ids[p];
+      if (id < 0 || id >= a.E) a.y[(u64)p * a.M + r] = qnan;
+    }
+  }
+  if (e < 0) return;  // uniform over the workgroup
+
+  // pairs routed to e, in ascending order: thread segments, then an exclusive scan
+  const int L = (P + 255) / 256;
+  const int s0 = min(P, tid * L), s1 = min(P, s0 + L);
+  int mine = 0;
+  for (int p = s0; p < s1; ++p) mine += a.ids[p] == e;
+  {
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) sh.base[tid >> 6] = incl;  // wave totals
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < (tid >> 6); ++w) before += sh.base[w];
+    const int total = sh.base[0] + sh.base[1] + sh.base[2] + sh.base[3];
+    __syncthreads();
+    sh.base[tid] = before + incl - mine;
+    if (tid == 0) sh.count = total;
+    __syncthreads();
+  }
+  const int count = sh.count;
+  const int T = a.T ? a.T : tile_for_count(count);
+
+  GemmArgs ae = a;
+  ae.W = a.W + static_cast<u64>(e) * a.expert_bytes;
+  const int rw0 = r_lo + (tid >> 6) * (16 * RB);  // this wave's first row
+  u32 row_off[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int r = rw0 + 16 * b + (lane & 15);
+    row_off[b] = static_cast<u32>(r < a.M ? r : a.M - 1) * a.row_bytes;
+  }
+  const int o0 = x_slot(lane & 15, 2 * g);
+  const int o1 = x_slot(lane & 15, 2 * g + 1);
+  const int all = (a.nU + 1) >> 1;
+  constexpr int ES = XF16 ? 2 : 4;
+
+  for (int tok0 = 0; tok0 < count; tok0 += TT) {
+    // this super-tile's pairs and activation rows
+    int pos = sh.base[tid];
+    for (int p = s0; p < s1; ++p)
+      if (a.ids[p] == e) {
+        if (pos >= tok0 && pos < tok0 + TT) {
+          sh.pair[pos - tok0] = p;
+          sh.xrow[pos - tok0] = a.x_per_slot ? p : p / a.S;
+        }
+        ++pos;
+      }
+    __syncthreads();
+    const int rem = count - tok0;
+    const int ntb = rem >= TT ? NTB : ((rem + T - 1) / T) * (T / 16);
+    XLanes<TT, ES> xl;
+    xl.init_rows(a.K, sh.xrow, min(rem, TT), tid);
+    floatx4 acc[RB][NTB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int t = 0; t < NTB; ++t) acc[b][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const u8* xb = reinterpret_cast<const u8*>(a.x);
+    if (ntb == NTB)
+      k_loop<F, RB, TT, XF16, true>(ae, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, 0, all);
+    else
+      k_loop<F, RB, TT, XF16, false>(ae, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, 0, all);
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) {
+      const int i = 16 * t + (lane & 15);
+      if (t < ntb && i < rem) {
+        const int p = sh.pair[i];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const int r = rw0 + 16 * b + 4 * g;
+          float* yp = a.y + (u64)p * a.M + r;
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (r + v < a.M) yp[v] = acc[b][t][v];
+        }
+      }
+    }
+    __syncthreads();  // sX, pair and xrow are refilled for the next super-tile
   }
 }
 
@@ -607,6 +800,12 @@ GemmKernel pick(int RB, int TT, bool xf16) {
        : TT == 64 ? kernel_if_ok<F, false, 1, 64>() : kernel_if_ok<F, false, 1, 32>();
 }
 
+template <int F, int TT>
+GemmKernel pick_id(bool xf16) {
+  if (xf16) return k_gemm_id<F, 1, TT, true>;
+  return k_gemm_id<F, 1, TT, false>;
+}
+
 constexpr int64_t kCUs = 256;
 }  // namespace
 
@@ -632,6 +831,44 @@ GemmSplit gemm_split(const MatDesc& m, int64_t N) {
 size_t gemm_workspace_bytes(const MatDesc& m, int64_t N) {
   const GemmSplit sp = gemm_split(m, N);
   return sp.splits > 1 ? static_cast<size_t>(sp.splits) * N * m.M * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N, int64_t S, int x_per_slot,
+                          const int32_t* ids, float* y, int tile, hipStream_t st) {
+  GemmArgs a{};
+  a.W = m.blocks;
+  a.row_bytes = static_cast<u32>(m.row_bytes);
+  a.M = static_cast<int>(m.M);
+  a.nU = static_cast<int>(m.K / 32);
+  a.K = static_cast<int>(m.K);
+  a.x = x;
+  a.N = static_cast<int>(N);
+  a.y = y;
+  a.T = tile;  // 0: the tile rule on each expert's pair count
+  a.ids = ids;
+  a.S = static_cast<int>(S);
+  a.x_per_slot = x_per_slot;
+  a.E = static_cast<int>(m.n_experts);
+  a.expert_bytes = m.row_bytes * static_cast<u64>(m.M);
+  const int64_t P = N * S;
+  const int64_t ranks = P < m.n_experts ? P : m.n_experts;
+  // 64 rows x 64 tokens; 128 tokens when an expert averages that many pairs
+  const bool xf16 = x_f16 != 0;
+  const int TT = P >= 128 * m.n_experts && m.fmt != FMT_Q6_K ? 128 : 64;  // (Q6_K x 128 spills)
+  GemmKernel k = nullptr;
+  switch (m.fmt) {
+    case FMT_Q4_0: k = TT == 128 ? pick_id<FMT_Q4_0, 128>(xf16) : pick_id<FMT_Q4_0, 64>(xf16); break;
+    case FMT_Q8_0: k = TT == 128 ? pick_id<FMT_Q8_0, 128>(xf16) : pick_id<FMT_Q8_0, 64>(xf16); break;
+    case FMT_Q4_K: k = TT == 128 ? pick_id<FMT_Q4_K, 128>(xf16) : pick_id<FMT_Q4_K, 64>(xf16); break;
+    case FMT_Q6_K: k = pick_id<FMT_Q6_K, 64>(xf16); break;
+    case FMT_A4G64: k = TT == 128 ? pick_id<FMT_A4G64, 128>(xf16) : pick_id<FMT_A4G64, 64>(xf16); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (!k) return hipErrorInvalidValue;
+  const int64_t row_tiles = (m.M + 63) / 64;
+  if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(row_tiles), static_cast<unsigned>(ranks)), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,

@@ -21,6 +21,9 @@ constexpr int64_t kMaxSlots = 64;
 // The matrix-matrix path addresses a 256-token slab of fp32 activations with
 // 32-bit offsets: K * 4 bytes * 256 must stay below 4 GiB.
 constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+// The expert-indexed matrix-matrix path scans every (token, slot) id in each
+// workgroup's routing prologue: at most this many pairs per call.
+constexpr int64_t kMaxGemmIdPairs = int64_t(1) << 18;
 
 hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f16, hipStream_t s);
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);
@@ -37,5 +40,8 @@ size_t gemm_workspace_bytes(const MatDesc& m, int64_t N);
 // (unsplit)
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t s);
+// tile: 32 or 64, or 0 for the tile rule on each expert's pair count
+hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N, int64_t S, int x_per_slot,
+                          const int32_t* ids, float* y, int tile, hipStream_t s);
 
 }  // namespace qmm

@@ -187,6 +187,25 @@ qmm_status qmm_gemm_id(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t
                        qmm_stream_t stream);
 
 /*
+ * qmm_gemm_id_tiled -- expert-indexed matrix-matrix path for prefill-sized calls
+ * (MUL_MAT_ID in the llama.cpp pull request above, on the token-tiled matrix
+ * cores of the candle pull request): the same operation, arguments and NaN rule
+ * as qmm_gemm_id, with qmm_gemm's arithmetic (weights staged as fp16, fp32
+ * activations rounded to fp16, fp32 accumulation; bound 2e-3 * S).  Each
+ * workgroup finds its expert, gathers the pairs routed to it in ascending pair
+ * order, and multiplies that expert's rows by them tile by tile; each expert's
+ * pairs are padded to the token tile on their own.
+ *   N, S   N * S <= 2^18 (token, slot) pairs; S 1..64.  Any N >= 0.
+ *   x      activation rows below 4 GiB in all.
+ *   tile   QMM_TILE_AUTO (the tile rule on each expert's pair count), 32 or 64.
+ *          Results are bit-identical for either tile, and every output row equals,
+ *          bit for bit, qmm_gemm of its expert on its activation row.
+ */
+qmm_status qmm_gemm_id_tiled(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
+                             int64_t S, int x_per_slot, const int32_t *ids, float *y,
+                             qmm_tile tile, qmm_stream_t stream);
+
+/*
  * qmm_dequantize -- decode one expert's matrix (expert 0 for a plain matrix).
  *   out  DEVICE [M, K] of type ot, 16-byte aligned.  QMM_F32: the exact dequantized
  *        weights.  QMM_F16: the fp16 values the matrix-matrix path stages in LDS.
