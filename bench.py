@@ -369,8 +369,25 @@ def extra_moe(torch, q, W, args):
         gbs = distinct * ebytes / (us * 1e-6) / 1e9
         res.append({"n": n, "us_per_call": us, "distinct_experts": distinct,
                     "distinct_weight_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS})
+    # prefill-sized calls on the matrix cores (qmm_gemm_id_tiled), fp16 activations
+    pre = []
+    C = 8
+    for n in W.MOE_PREFILL_TOKENS:
+        ids_h = [W.moe_ids(n, c) for c in range(C)]
+        ids = [torch.from_numpy(i).to("cuda") for i in ids_h]
+        x = torch.from_numpy(W.moe_prefill_x(n)).to("cuda")
+        y = torch.empty((n, S, M), device="cuda")
+        g = capture(torch, lambda: [q.qmm_gemm_id_tiled(hs[c % rot.copies].handle, x, n, S, 1, ids[c], y)
+                                    for c in range(C)])
+        us = time_graph(torch, g, args.rounds) * 1e3 / C
+        distinct = float(np.mean([len(np.unique(i)) for i in ids_h]))
+        tflops = 2.0 * M * K * n * S / (us * 1e-6) / 1e12
+        pre.append({"n": n, "us_per_call": us, "distinct_experts": distinct, "tflops": tflops,
+                    "frac_mfma": tflops / MFMA_F16_PEAK_TFLOPS,
+                    "distinct_weight_gbs": distinct * ebytes / (us * 1e-6) / 1e9})
     return {"workload": "128 experts x Q4_0 4096x512, 8 ids per token, ids re-drawn per call",
-            "copies": rot.copies, "results": res}
+            "copies": rot.copies, "results": res,
+            "prefill_tiled": {"workload": "same experts, fp16 tokens, qmm_gemm_id_tiled, auto tile", "results": pre}}
 
 
 # ------------------------------------------------------------------------------------------------

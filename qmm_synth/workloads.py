@@ -124,6 +124,14 @@ def moe_x(n):
     return draw_x(rng([4, n]), (n, MOE_SLOTS, MOE_K), np.float32)
 
 
+MOE_PREFILL_TOKENS = [64, 256, 1024]
+
+
+def moe_prefill_x(n):
+    """[n, slots, K] fp16 activations of a prefill-sized expert-indexed call."""
+    return draw_x(rng([4, n, 7]), (n, MOE_SLOTS, MOE_K), np.float16)
+
+
 def moe_ids(n, call, n_experts=MOE_EXPERTS, slots=MOE_SLOTS):
     """[n, slots] int32: per token, ``slots`` distinct experts drawn uniformly."""
     g = rng([4, n, call])
