@@ -14,6 +14,8 @@ Contents
              over blocks with NumPy).
 ``matmul``   the dense product ``y = x . W^T`` and the expert-indexed product
              in fp64, plus the tolerance scale ``S = |x| . |W|^T``.
+``quantize`` reference quantizers fp32 -> blocks (``quantize_blocks``), the
+             check for the library's GPU quantizer.
 ``tile``     the 32/64-token tile rule of the candle pull request
              "Metal: 64-token tile for the quantized matrix-matrix kernel",
              section "Where the 64-token tile is used".
@@ -33,3 +35,4 @@ from .formats import (  # noqa: F401
 )
 from .matmul import matmul_ref, matmul_id_ref, tolerance_scale, tolerance_scale_id  # noqa: F401
 from .tile import tile_for_tokens, pad_tokens  # noqa: F401
+from .quantize import quantize_blocks  # noqa: F401
