@@ -23,7 +23,7 @@ from ._lib import DTYPES, LIB_PATH, QMM_OK, STATUS, TILES, TYPES, QmmError, chec
 __all__ = [
     "QMatrix", "QmmError", "LIB_PATH", "TYPES",
     "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
-    "qmm_gemm_id", "qmm_gemm_id_tiled", "qmm_dequantize",
+    "qmm_gemm_id", "qmm_gemm_id_tiled", "qmm_dequantize", "qmm_quantize", "quantize",
     "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_block_weights", "qmm_block_bytes",
 ]
 
@@ -73,6 +73,24 @@ def qmm_block_weights(qtype) -> int:
 
 def qmm_block_bytes(qtype) -> int:
     return lib.qmm_block_bytes(_type_id(qtype))
+
+
+def qmm_quantize(qtype, w: torch.Tensor, M: int, K: int, blocks: torch.Tensor, stream=None) -> None:
+    check(lib.qmm_quantize(_type_id(qtype), _dev_ptr(w, "w"), int(M), int(K), _dev_ptr(blocks, "blocks"),
+                           _stream(stream)))
+
+
+def quantize(w: torch.Tensor, qtype) -> torch.Tensor:
+    """fp32 [M, K] device tensor -> uint8 device tensor of M rows of blocks."""
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a float32 [M, K] tensor")
+    M, K = w.shape
+    nbytes = qmm_row_bytes(qtype, K) * M
+    if nbytes == 0 and M:
+        raise ValueError(f"K={K} is not a multiple of the block of {qtype!r}")
+    blocks = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)[:nbytes]
+    qmm_quantize(qtype, w, M, K, blocks)
+    return blocks
 
 
 def qmm_create(blocks: torch.Tensor, qtype, M: int, K: int, n_experts: int = 1) -> ctypes.c_void_p:

@@ -41,6 +41,7 @@ def _load():
         "qmm_gemm_id": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, vp]),
         "qmm_gemm_id_tiled": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, c_int, vp]),
         "qmm_dequantize": (c_int, [vp, i64, vp, c_int, vp]),
+        "qmm_quantize": (c_int, [c_int, vp, i64, i64, vp, vp]),
         "qmm_tile_for_tokens": (c_int, [i64]),
         "qmm_row_bytes": (ctypes.c_size_t, [c_int, i64]),
         "qmm_block_weights": (c_int, [c_int]),

@@ -276,6 +276,24 @@ qmm_status qmm_gemm_id_tiled(const qmm_matrix* h, const void* x, qmm_dtype xt, i
   return ok();
 }
 
+qmm_status qmm_quantize(qmm_type type, const float* w, int64_t M, int64_t K, void* blocks, qmm_stream_t stream) {
+  if (!valid_type(type)) return fail(QMM_E_TYPE, "unknown block type %d", static_cast<int>(type));
+  if (M < 0 || M > INT_MAX / 2) return fail(QMM_E_SHAPE, "M=%lld out of range", static_cast<long long>(M));
+  const size_t rb = qmm_row_bytes(type, K);
+  if (rb == 0 || K > INT_MAX / 2)
+    return fail(QMM_E_SHAPE, "K=%lld is not a positive multiple of %d (or too large)",
+                static_cast<long long>(K), kBW[type]);
+  if (!w) return fail(QMM_E_ARG, "w is NULL");
+  if (!blocks) return fail(QMM_E_ARG, "blocks is NULL");
+  if (!aligned(w, 4)) return fail(QMM_E_ALIGN, "w must be 4-byte aligned");
+  if (!aligned(blocks, 16)) return fail(QMM_E_ALIGN, "blocks must be 16-byte aligned");
+  if (M == 0) return ok();
+  const hipError_t e = qmm::launch_quantize(static_cast<int>(type), w, M, K, blocks,
+                                            reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return ok();
+}
+
 qmm_status qmm_dequantize(const qmm_matrix* h, int64_t expert, void* out, qmm_dtype ot, qmm_stream_t stream) {
   if (!h) return fail(QMM_E_ARG, "handle is NULL");
   if (expert < 0 || expert >= h->d.n_experts)

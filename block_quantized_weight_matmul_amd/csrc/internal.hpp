@@ -26,6 +26,7 @@ constexpr int64_t kMaxGemmK = int64_t(1) << 22;
 constexpr int64_t kMaxGemmIdPairs = int64_t(1) << 18;
 
 hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f16, hipStream_t s);
+hipError_t launch_quantize(int fmt, const float* w, int64_t M, int64_t K, void* out, hipStream_t s);
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);
 hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
                           const int32_t* ids, float* y, hipStream_t s);

@@ -213,6 +213,37 @@ qmm_status qmm_gemm_id_tiled(const qmm_matrix *h, const void *x, qmm_dtype xt, i
 qmm_status qmm_dequantize(const qmm_matrix *h, int64_t expert, void *out, qmm_dtype ot,
                           qmm_stream_t stream);
 
+/*
+ * qmm_quantize -- encode fp32 weights into blocks of `type` on the GPU (the step
+ * before the path).  The pages quantize random weights to each type before
+ * timing (candle pull request above, section "Numbers") but print no quantizer;
+ * these are this library's closed forms, evaluated in fp64 on the exact fp32
+ * inputs in the order written.  rne/up/down round to the nearest fp16 (ties to
+ * even), the least fp16 >= the value, the greatest fp16 <= it; rha rounds half
+ * away from zero:
+ *   Q4_0   w* = element of largest |w| (first on a tie), d = rne(w* / -8),
+ *          q = min(15, floor(w / d + 8.5)) (8 when d = 0).
+ *   Q8_0   d = rne(max|w| / 127), q = clamp(rha(w / d), -127, 127) (0 when d = 0).
+ *   Q4_K   per 32-weight sub-block j: lo_j = min(0, min w), hi_j = max w;
+ *          dmin = up(max_j(-lo_j) / 63), m_j = clamp(ceil(-lo_j / dmin), 0, 63),
+ *          span_j = hi_j + dmin * m_j, d = up(max_j(span_j / 15) / 63),
+ *          sc_j = clamp(ceil(span_j / (15 d)), 0, 63),
+ *          q = clamp(rha((w + dmin m_j) / (d sc_j)), 0, 15) (0 when d sc_j = 0);
+ *          a zero divisor gives 0 before a ceil.
+ *   Q6_K   a_j = max|w| per 16-weight sub-block, d = up(max_j a_j / 3937),
+ *          sc_j = clamp(ceil(a_j / (31 d)), 0, 127),
+ *          q = clamp(rha(w / (d sc_j)) + 32, 0, 63) (32 when d sc_j = 0).
+ *   A4G64  bias = down(min w), scale = up((max w - bias) / 15),
+ *          q = clamp(rha((w - bias) / scale), 0, 15) (0 when scale = 0).
+ *   w       DEVICE fp32 [M, K] contiguous, 4-byte aligned; finite values whose
+ *           scales fit fp16.
+ *   blocks  DEVICE, 16-byte aligned, M * qmm_row_bytes(type, K) bytes, written in
+ *           the block layout above (rows back to back).  M = 0: no launch.
+ * Deterministic: the bytes depend only on w.
+ */
+qmm_status qmm_quantize(qmm_type type, const float *w, int64_t M, int64_t K, void *blocks,
+                        qmm_stream_t stream);
+
 /* qmm_tile_for_tokens -- 64 when a 64-token tile pads no more tokens than a
  * 32-token tile, else 32 (candle pull request, section "Where the 64-token tile
  * is used").  Host-only and pure; N < 0 returns 0. */

@@ -1,0 +1,80 @@
+"""GPU quantizer (qmm_quantize) against the oracle's reference quantizers: the
+same bytes, block for block, on several distributions, zero blocks, signed
+zeros and exact ties."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_matmul_amd as q
+from tests.gpu_helpers import FORMATS, oracle, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(fmt, dist, M, K, seed):
+    g = np.random.default_rng(seed)
+    if dist == "normal":
+        w = g.normal(0, 0.02, (M, K))
+    elif dist == "wide":
+        w = g.normal(0, 1.0, (M, K)) * np.exp(g.uniform(-6, 6, (M, 1)))
+    elif dist == "spiky":
+        w = g.normal(0, 1e-3, (M, K))
+        w[:, ::37] = -5.0
+    else:  # "edges": zero blocks, signed zeros, exact ties, constant groups
+        w = g.normal(0, 0.5, (M, K))
+        bw = oracle.block_weights(fmt)
+        w[0, :bw] = 0.0
+        w[1, :bw] = -0.0
+        w[2, :bw] = 0.75
+        w[3, 3], w[3, 9] = 4.0, -4.0
+        w[4, ::2] = 0.0
+        w[5, : 2 * bw] = -0.0
+        w[5, 7] = 0.0
+    return w.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("dist", ["normal", "wide", "spiky", "edges"])
+def test_quantize_matches_oracle(fmt, dist):
+    bw = oracle.block_weights(fmt)
+    M, K = 7, 2 * 256 if bw == 256 else 6 * bw
+    w = _weights(fmt, dist, M, K, [91, len(dist)])
+    got = to_host(q.quantize(to_dev(w), fmt))
+    ref = oracle.quantize_blocks(fmt, w)
+    assert got.shape == ref.shape
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{fmt} {dist}: {bad.size} bytes differ, first at byte {bad[:1]} (block {bad[:1] // oracle.block_bytes(fmt)})"
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantized_blocks_feed_the_path(fmt):
+    """Blocks made on the GPU go straight into a handle; the matrix-vector result
+    matches the oracle on the oracle's own encoding of the same weights."""
+    bw = oracle.block_weights(fmt)
+    M, K = 300, 2560 if 2560 % bw == 0 else 2048
+    w = np.random.default_rng(92).normal(0, 0.02, (M, K)).astype(np.float32)
+    blocks = q.quantize(to_dev(w), fmt)
+    rb = oracle.row_bytes(fmt, K)
+    assert np.array_equal(to_host(blocks)[:4 * rb], oracle.quantize_blocks(fmt, w[:4]))
+    wq = oracle.dequantize(fmt, to_host(blocks), M, K)
+    qm = q.QMatrix(blocks, fmt, M, K)
+    x = np.random.default_rng(93).standard_normal((3, K)).astype(np.float32)
+    y = to_host(qm.gemv(to_dev(x)))
+    S = oracle.tolerance_scale(x, wq)
+    assert np.all(np.abs(y - oracle.matmul_ref(x, wq)) <= 1e-5 * S)
+    assert np.array_equal(to_host(qm.dequantize()), wq)
+
+
+def test_quantize_errors_and_empty():
+    import ctypes
+    from block_quantized_weight_matmul_amd import _lib as L
+    w = torch.zeros((2, 64), device="cuda")
+    b = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    wp, bp = ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(b.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.lib.qmm_quantize(7, wp, 2, 64, bp, s) == -2                 # bad type
+    assert L.lib.qmm_quantize(2, wp, 2, 64, bp, s) == -3                 # K not a multiple of 256
+    assert L.lib.qmm_quantize(0, None, 2, 64, bp, s) == -1
+    assert L.lib.qmm_quantize(0, wp, 2, 64, ctypes.c_void_p(b.data_ptr() + 2), s) == -4
+    assert L.lib.qmm_quantize(0, wp, 0, 64, bp, s) == 0                  # M = 0: nothing to do
