@@ -390,6 +390,24 @@ def extra_moe(torch, q, W, args):
             "prefill_tiled": {"workload": "same experts, fp16 tokens, qmm_gemm_id_tiled, auto tile", "results": pre}}
 
 
+def extra_quantize(torch, q, W, mats, args):
+    """The GPU quantizer on the decode layer's fp32 weights (regenerated from the
+    same seeds), fp32 bytes read per second."""
+    res = []
+    for j, m in enumerate(mats):
+        if m["name"] not in ("ffn_gate", "ffn_down"):
+            continue
+        w = torch.from_numpy(W.decode_weights_fp32(j)).to("cuda")
+        out = torch.empty(m["blob"].size, dtype=torch.uint8, device="cuda")
+        g = capture(torch, lambda: [q.qmm_quantize(m["fmt"], w, m["M"], m["K"], out) for _ in range(5)])
+        us = time_graph(torch, g, args.rounds) * 1e3 / 5
+        res.append({"proj": m["name"], "fmt": m["fmt"], "M": m["M"], "K": m["K"], "us": us,
+                    "fp32_gbs": w.numel() * 4 / (us * 1e-6) / 1e9,
+                    "same_bytes_as_data": bool(np.array_equal(out.cpu().numpy(), m["blob"]))})
+        del w, out
+    return {"workload": "qmm_quantize of decode-layer weights (fp32 in, blocks out)", "results": res}
+
+
 # ------------------------------------------------------------------------------------------------
 
 def copy_probe(torch):
@@ -475,7 +493,8 @@ def main():
         for name, fn in (("single_matvec", lambda: extra_single_matvec(torch, q, W, args)),
                          ("small_decode_a4g64", lambda: extra_small_decode(torch, q, W, args)),
                          ("prefill_gemm", lambda: extra_prefill(torch, q, W, mats, args)),
-                         ("expert_matvec", lambda: extra_moe(torch, q, W, args))):
+                         ("expert_matvec", lambda: extra_moe(torch, q, W, args)),
+                         ("quantize", lambda: extra_quantize(torch, q, W, mats, args))):
             t0 = time.time()
             extras[name] = fn()
             log(f"[bench] extra {name} done in {time.time() - t0:.1f}s")

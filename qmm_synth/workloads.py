@@ -77,6 +77,12 @@ def decode_weights(i):
     return {"name": name, "fmt": fmt, "M": M, "K": K, "blob": quantize(fmt, w)}
 
 
+def decode_weights_fp32(i):
+    """The fp32 weights decode_weights(i) encodes (same seed)."""
+    _, M, K, _ = DECODE_SHAPES[i]
+    return draw_weights(rng([1, i]), M, K)
+
+
 def decode_x(i, n=1):
     _, _, K, _ = DECODE_SHAPES[i]
     return draw_x(rng([1, i, n]), (n, K), np.float32)
