@@ -471,6 +471,10 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
       put(s + 1, xo, !STEADY);
       stage_barrier();
     }
+    // keep the next step's decode below this point: hoisted above the barrier it
+    // waits for the weight loads this step just issued (the load counter retires
+    // in order), which serialises the stage behind a full memory latency
+    __builtin_amdgcn_sched_barrier(0);
   };
   using steady_t = std::integral_constant<bool, true>;
   using edge_t = std::integral_constant<bool, false>;
