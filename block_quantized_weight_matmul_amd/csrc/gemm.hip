@@ -893,12 +893,14 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   a.split_floats = sp.splits > 1 ? static_cast<u64>(N) * static_cast<u64>(m.M) : 0;
   if (sp.splits > 1) a.y = ws;
   // Rows x tokens per workgroup: the first shape, in order of decreasing reuse,
-  // that gives two workgroups per CU (one for Q6_K, whose wider decode favours
-  // reuse over parallelism), else 64 x 64.  Measured on the decode-layer shapes.
+  // that gives two workgroups per CU (one per two CUs for Q6_K, whose wider
+  // decode favours reuse over parallelism: ffn_down at 512 tokens takes 122 us
+  // at 64 x 128 on 160 workgroups against 189 at 64 x 64 on 320), else 64 x 64.
+  // Measured on the decode-layer shapes.
   const int64_t padded = (N + tile - 1) / tile * tile;
   auto wgs = [&](int rb, int tt) { return ((m.M + 64 * rb - 1) / (64 * rb)) * ((padded + tt - 1) / tt); };
   static const int kShapes[3][2] = {{2, 128}, {1, 128}, {1, 64}};
-  const int64_t want = m.fmt == FMT_Q6_K ? kCUs : 2 * kCUs;
+  const int64_t want = m.fmt == FMT_Q6_K ? kCUs / 2 : 2 * kCUs;
   const bool xf16 = x_f16 != 0;
   // split calls take 64 rows x 64 tokens, or x 32 when the call pads to 32:
   // activations of absent tokens are not staged then
