@@ -67,10 +67,13 @@ def log(*a):
 
 
 def source_digest():
+    """Digest of what the one-token GEMV kernel is built from (its source, the headers it
+    includes and the build flags): the committed counter summaries hold for that kernel only."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "block_quantized_weight_matmul_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    pkg = os.path.join(ROOT, "block_quantized_weight_matmul_amd")
+    for f in ["csrc/gemv.hip", "csrc/decode.hpp", "csrc/internal.hpp", "build.py"]:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
