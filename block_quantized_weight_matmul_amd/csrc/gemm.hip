@@ -60,9 +60,12 @@ struct GemmArgs {
 constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
 
 // LDS slot (in halves) of k-chunk c (8 values) of token row r of a stage buffer:
-// 128-byte rows, chunk index XOR-swizzled by r % 8 so the 16 rows a B-operand
-// read touches fall in distinct bank groups.
-__device__ __forceinline__ int x_slot(int r, int c) { return r * kKS + 8 * (c ^ (r & 7)); }
+// 128-byte rows, so rows 2i and 2i+1 share one 256-byte line of the 64 four-byte
+// banks, in its lower and upper half.  The chunk index is XOR-swizzled by
+// (r / 2) % 8: the 16 rows a B-operand read touches (one chunk each) then cover
+// all 64 banks once.  Swizzling by r % 8 would put rows r and r + 8 on the same
+// banks, a two-way conflict on every B read.
+__device__ __forceinline__ int x_slot(int r, int c) { return r * kKS + 8 * (c ^ ((r >> 1) & 7)); }
 
 // ---------------------------------------------------------------------------------------------
 // A operands.  The K order inside a 64-deep stage is permuted so that each lane
@@ -413,6 +416,10 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// sched_barrier mask: every instruction class but global memory may be moved
+// across (ALU, VALU, SALU, MFMA, LDS, transcendental)
+constexpr int kNoVmemCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
+
 // One workgroup's K loop for token blocks [0, NTB) (FULL) or [0, ntb).  The
 // products of stage s run while the wave decodes the A operands of stage s+1,
 // so the matrix cores and the VALU work side by side within one wave.  Weight
@@ -464,8 +471,12 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
     const bool fetch2 = STEADY || s + 2 < nstages;
     const bool fetch3 = STEADY || s + 3 < nstages;
     if (next) decode(s + 1, wn, An, !STEADY);
-    if (fetch3) fetch_w(s + 3, wn);
+    // activations before weights: the load counter retires in order, so the wait
+    // for these activations (next step, before they are written to LDS) must not
+    // also wait for the weight bytes of stage s+3, which have two more steps
     if (fetch2) fetch_x(s + 2, xs, !STEADY);
+    __builtin_amdgcn_sched_barrier(kNoVmemCross);
+    if (fetch3) fetch_w(s + 3, wn);
     stage_products<FULL>(sX[s & 1], o0, o1, Ac, acc, ntb);
     if (next) {
       put(s + 1, xo, !STEADY);
@@ -815,10 +826,57 @@ constexpr int64_t kCUs = 256;
 
 // K splits for N tokens: few tokens leave too few (row, token) tiles to fill the
 // chip, so the K stages are divided among that many more workgroups, at least
-// two stages each.  A function of the shape and N only (not of the tile), so both
+// two stages each (above 64 tokens, the plan above).  A function of the shape and N only (not of the tile), so both
 // tiles split alike and stay bit-identical.
+namespace {
+
+// Calls of more than 64 tokens: the split count (1 .. 3, at least 8 stages per
+// split) and token super-tile (128 or 64, one row block) that minimise a cost
+// fitted to the decode-layer shapes at 130 .. 2048 tokens.  A workgroup runs
+// about as fast alone on a CU as beside a second one, so a launch takes
+// ceil(workgroups / CUs) rounds of (stages per split) x (time of one stage of
+// that super-tile); a split adds a fixed 4 us plus the partial outputs written
+// and summed at ~4 TB/s.  Stage times (us): 0.55 (128 tokens) and 0.38 (64) for
+// the formats decoded in one multiply-add per weight, 0.73 and 0.58 for Q6_K.
+// The plan does not depend on the token tile or the activation type (the
+// workspace query knows neither): more than 64 tokens pad to more than 64
+// under both tiles.
+struct WidePlan {
+  int splits, stages, TT;
+};
+
+WidePlan wide_plan(const MatDesc& m, int64_t N) {
+  const int nst = static_cast<int>((m.K / 32 + 1) / 2);
+  const bool q6 = m.fmt == FMT_Q6_K;
+  WidePlan best{1, nst, 64};
+  double best_cost = 1e300;
+  for (const int tt : {128, 64}) {
+    const double stage_us = q6 ? (tt == 128 ? 0.73 : 0.58) : (tt == 128 ? 0.55 : 0.38);
+    const int64_t wgs = ((m.M + 63) / 64) * ((N + tt - 1) / tt);
+    for (int S = 1; S <= 3; ++S) {
+      const int per = (nst + S - 1) / S;
+      if (S > 1 && per < 8) break;
+      const int splits = (nst + per - 1) / per;
+      const int64_t rounds = (wgs * splits + kCUs - 1) / kCUs;
+      double cost = static_cast<double>(rounds) * per * stage_us;
+      if (splits > 1) cost += 4.0 + static_cast<double>(N) * static_cast<double>(m.M) * 4.0 * (splits + 1) / 4e6;
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = WidePlan{splits, per, tt};
+      }
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
 GemmSplit gemm_split(const MatDesc& m, int64_t N) {
   GemmSplit sp{1, static_cast<int>((m.K / 32 + 1) / 2)};
+  if (N > 64) {
+    const WidePlan p = wide_plan(m, N);
+    return GemmSplit{p.splits, p.stages};
+  }
   const int64_t base = ((m.M + 63) / 64) * ((N + 63) / 64);
   const int64_t want = m.fmt == FMT_Q6_K ? kCUs : 2 * kCUs;
   if (N <= 0 || 2 * base >= want) return sp;
@@ -902,9 +960,11 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   static const int kShapes[3][2] = {{2, 128}, {1, 128}, {1, 64}};
   const int64_t want = m.fmt == FMT_Q6_K ? kCUs / 2 : 2 * kCUs;
   const bool xf16 = x_f16 != 0;
-  // split calls take 64 rows x 64 tokens, or x 32 when the call pads to 32:
-  // activations of absent tokens are not staged then
+  // split calls take 64 rows x the planned super-tile above 64 tokens, else x 64,
+  // or x 32 when the call pads to 32: activations of absent tokens are not
+  // staged then
   int RB = 1, TT = sp.splits > 1 && padded <= 32 ? 32 : 64;
+  if (sp.splits > 1 && N > 64) TT = wide_plan(m, N).TT;
   for (const auto& c : kShapes) {
     if (sp.splits > 1) break;
     if (!shape_ok(m.fmt, xf16, c[0], c[1])) continue;
