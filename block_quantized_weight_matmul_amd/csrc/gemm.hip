@@ -420,6 +420,28 @@ __device__ __forceinline__ void stage_barrier() {
 // across (ALU, VALU, SALU, MFMA, LDS, transcendental)
 constexpr int kNoVmemCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
 
+// Approximate VALU instructions of one row block's A-operand decode per stage.
+template <int F> constexpr int kDecodeValu = F == FMT_Q6_K ? 90 : (F == FMT_Q4_K ? 64 : 48);
+
+// Instruction order asked of the scheduler for a steady full stage: the first
+// two token blocks' B operands read from LDS up front, then each MFMA followed
+// by its share of the next stage's decode and by the LDS read of a later
+// block's B operand, so the matrix core, the VALU and LDS latency overlap within
+// one wave instead of running as three serial phases.
+template <int F, int RB, int NTB>
+__device__ __forceinline__ void interleave_stage() {
+  constexpr int kMfma = 2 * RB * NTB;
+  constexpr int kValu = (kDecodeValu<F> * RB + kMfma - 1) / kMfma;
+  constexpr int kAheadReads = 4 < 2 * NTB ? 4 : 2 * NTB;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAheadReads, 0);
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    if (i % RB == RB - 1 && i / RB < 2 * NTB - kAheadReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // One workgroup's K loop for token blocks [0, NTB) (FULL) or [0, ntb).  The
 // products of stage s run while the wave decodes the A operands of stage s+1,
 // so the matrix cores and the VALU work side by side within one wave.  Weight
@@ -478,10 +500,9 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
     __builtin_amdgcn_sched_barrier(kNoVmemCross);
     if (fetch3) fetch_w(s + 3, wn);
     stage_products<FULL>(sX[s & 1], o0, o1, Ac, acc, ntb);
-    if (next) {
-      put(s + 1, xo, !STEADY);
-      stage_barrier();
-    }
+    if (next) put(s + 1, xo, !STEADY);
+    if constexpr (STEADY && FULL) interleave_stage<F, RB, TT / 16>();
+    if (next) stage_barrier();
     // keep the next step's decode below this point: hoisted above the barrier it
     // waits for the weight loads this step just issued (the load counter retires
     // in order), which serialises the stage behind a full memory latency
