@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--calls", type=int, default=20, help="calls per timed sample in the extras")
     p.add_argument("--rounds", type=int, default=6, help="timed samples per extra case (median)")
     p.add_argument("--copy-probe", action="store_true", help="only run a 256 MiB device copy (counter calibration)")
+    p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
+                   help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
     return p.parse_args()
 
 
@@ -317,7 +319,8 @@ def extra_prefill(torch, q, W, mats, args):
     flops_tok = 2 * sum(m["M"] * m["K"] for m in mats)
     wbytes = sum(int(m["blob"].size) for m in mats)
     res = []
-    for n in W.PREFILL_TOKENS:
+    tokens = [int(t) for t in args.prefill_only.split(",")] if args.prefill_only else W.PREFILL_TOKENS
+    for n in tokens:
         xs = [torch.from_numpy(W.prefill_x(j, n)).to("cuda") for j in range(len(mats))]
         ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
         # the workspace of the K-split few-token calls (QMatrix.gemm's path)
@@ -441,6 +444,10 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.prefill_only:
+        mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
+        print(json.dumps({"prefill_gemm": extra_prefill(torch, q, W, mats, args)}), flush=True)
         return
 
     head, mats = decode_layer(torch, q, W, args)
