@@ -130,3 +130,38 @@ def test_gemm_id_experts_not_dword_aligned(fmt):
     for e in range(E):
         got = to_host(qm.dequantize(e))
         assert np.array_equal(got, ws[e]), f"expert {e}"
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q4_k", "q6_k", "a4g64"])
+def test_gemm_id_tall_experts(fmt):
+    """Tall experts and many distinct ones: every expert's rows span many row
+    slices of the launch."""
+    E, M, K, N, S = 32, 2048, 512, 8, 8
+    blob, ws = _stack(fmt, E, M, K, 69)
+    g = np.random.default_rng(69)
+    ids = _ids(g, N, S, E)
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL,
+                  f"slices {fmt}")
+
+
+def test_gemm_id_tall_experts_many_pairs_and_bad_ids():
+    """All pairs on two tall experts: several passes of pairs per row slice, many
+    row slices, with ids outside [0, E) among them (NaN rows)."""
+    fmt, E, M, K, N, S = "q4_0", 32, 2048, 512, 8, 8
+    blob, ws = _stack(fmt, E, M, K, 70)
+    g = np.random.default_rng(70)
+    ids = g.integers(3, 5, size=(N, S)).astype(np.int32)
+    ids[1, 2] = -3
+    ids[5, 7] = E
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(np.isnan(y[bad]))
+    ids_ok = np.where(bad, 3, ids)
+    ref = oracle.matmul_id_ref(x, ids_ok, ws)
+    sc = oracle.tolerance_scale_id(x, ids_ok, ws)
+    assert_within(y[~bad], ref[~bad], sc[~bad], TOL, "slices and passes")
