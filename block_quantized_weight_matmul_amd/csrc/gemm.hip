@@ -534,8 +534,10 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
   }
 }
 
+// (the 256-token super-tile takes one workgroup per CU: its accumulators need
+// the register file's accumulation half)
 template <int F, int RB, int TT, bool XF16>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(256, TT >= 256 ? 1 : 2) void k_gemm(GemmArgs a) {
   constexpr int NTB = TT / 16;  // 16-token blocks of the super-tile
   __shared__ __attribute__((aligned(16))) _Float16 sX[2][TT * kKS];
 
@@ -813,8 +815,10 @@ typedef void (*GemmKernel)(GemmArgs);
 // The first two amortise each decoded weight over 128 tokens; 64 x 64 gives small
 // problems more workgroups; 64 x 32 serves K-split calls padded to 32 tokens.  Q6_K's raw bytes and fp32 activations (held twice
 // as wide while in flight) leave no room for the 128 x 128 shape within 256
-// registers per lane.
+// registers per lane.  Q6_K, whose decode costs the most per weight, also has
+// 64 x 256 and 128 x 256 with fp16 activations, one workgroup per CU.
 constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
+  if (TT == 256) return F == FMT_Q6_K && xf16 && (RB == 1 || RB == 2);
   if (RB == 2) return TT == 128 && F != FMT_Q6_K && xf16;
   return TT == 32 || TT == 64 || TT == 128;
 }
@@ -827,6 +831,7 @@ GemmKernel kernel_if_ok() {
 
 template <int F>
 GemmKernel pick(int RB, int TT, bool xf16) {
+  if (xf16 && TT == 256) return RB == 2 ? kernel_if_ok<F, true, 2, 256>() : kernel_if_ok<F, true, 1, 256>();
   if (xf16)
     return RB == 2 ? kernel_if_ok<F, true, 2, 128>()
          : TT == 128 ? kernel_if_ok<F, true, 1, 128>()
@@ -852,28 +857,32 @@ constexpr int64_t kCUs = 256;
 namespace {
 
 // Calls of more than 64 tokens: the split count (1 .. 3, at least 8 stages per
-// split) and token super-tile (128 or 64, one row block) that minimise a cost
-// fitted to the decode-layer shapes at 130 .. 2048 tokens.  A workgroup runs
-// about as fast alone on a CU as beside a second one, so a launch takes
-// ceil(workgroups / CUs) rounds of (stages per split) x (time of one stage of
-// that super-tile); a split adds a fixed 4 us plus the partial outputs written
-// and summed at ~4 TB/s.  Stage times (us): 0.55 (128 tokens) and 0.38 (64) for
-// the formats decoded in one multiply-add per weight, 0.73 and 0.58 for Q6_K.
-// The plan does not depend on the token tile or the activation type (the
-// workspace query knows neither): more than 64 tokens pad to more than 64
-// under both tiles.
+// split) and workgroup shape (64 rows x 128 or 64 tokens; for Q6_K with fp16
+// activations also 64 or 128 rows x 256 tokens) that minimise a cost fitted to
+// the decode-layer shapes at 130 .. 2048 tokens.  A workgroup runs about as fast
+// alone on a CU as beside a second one, so a launch takes ceil(workgroups / CUs)
+// rounds of (stages per split) x (time of one stage of that shape); a split adds
+// a fixed 4 us plus the partial outputs written and summed at ~4 TB/s.  Stage
+// times (us): 0.55 (64 x 128) and 0.38 (64 x 64) for the formats decoded in one
+// multiply-add per weight; 0.73, 0.58, 1.15 (64 x 256) and 2.15 (128 x 256) for
+// Q6_K.  The plan does not depend on the token tile (more than 64 tokens pad to
+// more than 64 under both tiles), so both tiles split alike.
 struct WidePlan {
-  int splits, stages, TT;
+  int splits, stages, RB, TT;
 };
 
-WidePlan wide_plan(const MatDesc& m, int64_t N) {
+WidePlan wide_plan(const MatDesc& m, int64_t N, bool xf16) {
   const int nst = static_cast<int>((m.K / 32 + 1) / 2);
   const bool q6 = m.fmt == FMT_Q6_K;
-  WidePlan best{1, nst, 64};
+  WidePlan best{1, nst, 1, 64};
   double best_cost = 1e300;
-  for (const int tt : {128, 64}) {
-    const double stage_us = q6 ? (tt == 128 ? 0.73 : 0.58) : (tt == 128 ? 0.55 : 0.38);
-    const int64_t wgs = ((m.M + 63) / 64) * ((N + tt - 1) / tt);
+  static const int kWide[4][2] = {{1, 128}, {1, 64}, {1, 256}, {2, 256}};
+  for (const auto& c : kWide) {
+    const int rb = c[0], tt = c[1];
+    if (!shape_ok(m.fmt, xf16, rb, tt)) continue;
+    const double stage_us = q6 ? (tt == 256 ? (rb == 2 ? 2.15 : 1.15) : (tt == 128 ? 0.73 : 0.58))
+                               : (tt == 128 ? 0.55 : 0.38);
+    const int64_t wgs = ((m.M + 64 * rb - 1) / (64 * rb)) * ((N + tt - 1) / tt);
     for (int S = 1; S <= 3; ++S) {
       const int per = (nst + S - 1) / S;
       if (S > 1 && per < 8) break;
@@ -883,7 +892,7 @@ WidePlan wide_plan(const MatDesc& m, int64_t N) {
       if (splits > 1) cost += 4.0 + static_cast<double>(N) * static_cast<double>(m.M) * 4.0 * (splits + 1) / 4e6;
       if (cost < best_cost) {
         best_cost = cost;
-        best = WidePlan{splits, per, tt};
+        best = WidePlan{splits, per, rb, tt};
       }
     }
   }
@@ -892,10 +901,11 @@ WidePlan wide_plan(const MatDesc& m, int64_t N) {
 
 }  // namespace
 
-GemmSplit gemm_split(const MatDesc& m, int64_t N) {
+namespace {
+GemmSplit split_for(const MatDesc& m, int64_t N, bool xf16) {
   GemmSplit sp{1, static_cast<int>((m.K / 32 + 1) / 2)};
   if (N > 64) {
-    const WidePlan p = wide_plan(m, N);
+    const WidePlan p = wide_plan(m, N, xf16);
     return GemmSplit{p.splits, p.stages};
   }
   const int64_t base = ((m.M + 63) / 64) * ((N + 63) / 64);
@@ -909,6 +919,14 @@ GemmSplit gemm_split(const MatDesc& m, int64_t N) {
   sp.stages = static_cast<int>(per);
   sp.splits = static_cast<int>((nst + per - 1) / per);
   return sp;
+}
+}  // namespace
+
+// The split of a call with either activation type that needs the larger
+// workspace (the workspace query does not know the type).
+GemmSplit gemm_split(const MatDesc& m, int64_t N) {
+  const GemmSplit a = split_for(m, N, false), b = split_for(m, N, true);
+  return b.splits > a.splits ? b : a;
 }
 
 size_t gemm_workspace_bytes(const MatDesc& m, int64_t N) {
@@ -956,7 +974,7 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
 
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t st) {
-  const GemmSplit sp = ws ? gemm_split(m, N) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
+  const GemmSplit sp = ws ? split_for(m, N, x_f16 != 0) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
   GemmArgs a{};
   a.W = m.blocks;
   a.row_bytes = static_cast<u32>(m.row_bytes);
@@ -985,9 +1003,16 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   // or x 32 when the call pads to 32: activations of absent tokens are not
   // staged then
   int RB = 1, TT = sp.splits > 1 && padded <= 32 ? 32 : 64;
-  if (sp.splits > 1 && N > 64) TT = wide_plan(m, N).TT;
+  if (N > 64 && ws) {
+    // the planned shape, split or not, when it is one of the 256-token ones
+    const WidePlan p = wide_plan(m, N, xf16);
+    if (sp.splits > 1 || p.TT == 256) {
+      RB = p.RB;
+      TT = p.TT;
+    }
+  }
   for (const auto& c : kShapes) {
-    if (sp.splits > 1) break;
+    if (sp.splits > 1 || TT == 256) break;
     if (!shape_ok(m.fmt, xf16, c[0], c[1])) continue;
     if (c[1] > 64 && padded <= c[1] / 2) continue;  // a super-tile at most half used
     if (wgs(c[0], c[1]) >= want) {

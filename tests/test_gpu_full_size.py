@@ -1,0 +1,150 @@
+"""Parity at the full benchmark sizes, in the launch configurations bench.py times.
+
+The seeded workloads of the benchmark (the seven decode-layer projections, the
+4-bit-group layer, the prefill GEMM at 7 .. 2048 tokens, the 128-expert matvec
+and its prefill-sized tiled form) run through the same entry points and launch
+shapes as bench.py.  The oracle cannot take whole outputs at these sizes, so it
+computes sampled outputs one by one: the sampled rows' blocks are dequantized by
+the oracle and multiplied by the given activations in fp64.  Tolerances are
+those of the smaller tests: 1e-5 * S on the fp32-accumulating matrix-vector
+paths, 2e-3 * S on the fp16-staged matrix-core paths.  The two token tiles are
+compared bit for bit over the whole output on the device.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_matmul_amd as q
+from qmm_synth import workloads as W
+from tests.gpu_helpers import assert_within, oracle, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL_GEMV = 1e-5
+TOL_GEMM = 2e-3
+
+
+@functools.lru_cache(maxsize=None)
+def decode_matrix(i):
+    return W.decode_weights(i)
+
+
+@functools.lru_cache(maxsize=None)
+def small_matrix(i):
+    return W.small_decode_weights(i)
+
+
+@functools.lru_cache(maxsize=1)
+def moe_stack():
+    return W.moe_stack()
+
+
+def sample_rows(M, seed, k=48):
+    g = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], g.choice(M, size=min(k, M), replace=False)]))
+
+
+def rows_ref(m, rows):
+    """Oracle weights of the sampled rows, [len(rows), K] fp32."""
+    rb = oracle.row_bytes(m["fmt"], m["K"])
+    blob = m["blob"]
+    return np.concatenate([oracle.dequantize(m["fmt"], blob[r * rb:(r + 1) * rb], 1, m["K"]) for r in rows])
+
+
+def check_rows(y, x, m, rows, tol, label):
+    """y [N, M] (host) against the oracle on the sampled rows."""
+    w = rows_ref(m, rows)
+    assert_within(y[:, rows], oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), tol, label)
+
+
+@pytest.mark.parametrize("j", range(len(W.DECODE_SHAPES)), ids=[s[0] for s in W.DECODE_SHAPES])
+def test_decode_gemv_one_token(j):
+    """The headline's launches: qmm_gemv of one fp32 token on each projection."""
+    m = decode_matrix(j)
+    x = W.decode_x(j)
+    qm = q.QMatrix(to_dev(m["blob"]), m["fmt"], m["M"], m["K"])
+    y = torch.empty((1, m["M"]), device="cuda")
+    q.qmm_gemv(qm.handle, to_dev(x), 1, y)
+    check_rows(to_host(y), x, m, sample_rows(m["M"], [80, j]), TOL_GEMV, f"decode {m['name']}")
+
+
+@pytest.mark.parametrize("n", W.SMALL_DECODE_TOKENS)
+def test_small_decode_layer(n):
+    """The 4-bit-group layer at 1 .. 16 fp16 tokens, every projection."""
+    for i in range(len(W.SMALL_DECODE_SHAPES)):
+        m = small_matrix(i)
+        x = W.small_decode_x(i, n)
+        qm = q.QMatrix(to_dev(m["blob"]), m["fmt"], m["M"], m["K"])
+        y = torch.empty((n, m["M"]), device="cuda")
+        q.qmm_gemv(qm.handle, to_dev(x), n, y)
+        check_rows(to_host(y), x.astype(np.float32), m, sample_rows(m["M"], [81, i, n]), TOL_GEMV,
+                   f"a4g64 {m['name']} n={n}")
+
+
+@pytest.mark.parametrize("n", W.PREFILL_TOKENS)
+def test_prefill_gemm(n):
+    """qmm_gemm_ws with the workspace the benchmark passes, both tiles and the
+    rule's choice, on every projection: tiles bit-identical over the whole
+    output, sampled outputs against the oracle."""
+    for j in range(len(W.DECODE_SHAPES)):
+        m = decode_matrix(j)
+        x = W.prefill_x(j, n)
+        qm = q.QMatrix(to_dev(m["blob"]), m["fmt"], m["M"], m["K"])
+        nb = q.qmm_gemm_workspace_bytes(qm.handle, n)
+        ws = torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None
+        xd = to_dev(x)
+        ys = {}
+        for t in (32, 64):
+            y = torch.empty((n, m["M"]), device="cuda")
+            q.qmm_gemm_ws(qm.handle, xd, n, y, t, ws)
+            ys[t] = y
+        assert torch.equal(ys[32].view(torch.int32), ys[64].view(torch.int32)), f"{m['name']} n={n}: tiles differ"
+        rows = sample_rows(m["M"], [82, j, n], k=24)
+        check_rows(to_host(ys[64]), x.astype(np.float32), m, rows, TOL_GEMM, f"prefill {m['name']} n={n}")
+
+
+def _moe_rows_check(y, x, ids, rows, tol, label):
+    """y [N, S, M] (host) on the sampled rows of every (token, slot) pair."""
+    stack = moe_stack()
+    eb = stack.size // W.MOE_EXPERTS
+    rb = oracle.row_bytes("q4_0", W.MOE_K)
+    N, S = ids.shape
+    for t in range(N):
+        for s in range(S):
+            e = int(ids[t, s])
+            blob = stack[e * eb:(e + 1) * eb]
+            w = np.concatenate([oracle.dequantize("q4_0", blob[r * rb:(r + 1) * rb], 1, W.MOE_K) for r in rows])
+            xs = x[t, s][None, :].astype(np.float32)
+            assert_within(y[t, s][None, rows], oracle.matmul_ref(xs, w), oracle.tolerance_scale(xs, w), tol,
+                          f"{label} t={t} s={s} e={e}")
+
+
+@pytest.mark.parametrize("n", W.MOE_TOKENS)
+def test_expert_matvec(n):
+    """qmm_gemm_id on the 128-expert stack with per-slot fp32 activations."""
+    stack = moe_stack()
+    qm = q.QMatrix(to_dev(stack), "q4_0", W.MOE_M, W.MOE_K, W.MOE_EXPERTS)
+    ids = W.moe_ids(n, 0)
+    x = W.moe_x(n)
+    y = torch.empty((n, W.MOE_SLOTS, W.MOE_M), device="cuda")
+    q.qmm_gemm_id(qm.handle, to_dev(x), n, W.MOE_SLOTS, 1, to_dev(ids), y)
+    _moe_rows_check(to_host(y), x, ids, sample_rows(W.MOE_M, [83, n], k=16), TOL_GEMV, f"moe n={n}")
+
+
+@pytest.mark.parametrize("n", W.MOE_PREFILL_TOKENS)
+def test_expert_tiled(n):
+    """qmm_gemm_id_tiled at prefill sizes (fp16 activations): sampled pairs."""
+    stack = moe_stack()
+    qm = q.QMatrix(to_dev(stack), "q4_0", W.MOE_M, W.MOE_K, W.MOE_EXPERTS)
+    ids = W.moe_ids(n, 0)
+    x = W.moe_prefill_x(n)
+    y = torch.empty((n, W.MOE_SLOTS, W.MOE_M), device="cuda")
+    q.qmm_gemm_id_tiled(qm.handle, to_dev(x), n, W.MOE_SLOTS, 1, to_dev(ids), y)
+    yh = to_host(y)
+    g = np.random.default_rng([84, n])
+    toks = np.unique(np.concatenate([[0, n - 1], g.choice(n, size=min(6, n), replace=False)]))
+    _moe_rows_check(yh[toks], x[toks], ids[toks], sample_rows(W.MOE_M, [85, n], k=16), TOL_GEMM,
+                    f"moe tiled n={n}")
