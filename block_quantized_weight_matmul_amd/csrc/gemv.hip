@@ -993,6 +993,110 @@ __global__ __launch_bounds__(512) void k_gemvn_id(GemvArgs a) {
                                      a.tok_pass, tm, sh.npairs, s_dyn);
 }
 
+// Expert-indexed, narrow rows: Q4_0 at K = 512, the shape of p2's case (its
+// section "Additional information"), where a row is 16 one-block items.  Lane l
+// of a wave takes item l % 16 of one of the wave's four rows per step, so the 16
+// lanes of a row sum their partials with the same butterfly as every other path
+// (and in the same order as reduce_rows: 0 + the unit's partial, then sum16):
+// results are the bits of the dense paths.  There are no partials in LDS, so a
+// workgroup streams a long slice of its expert's rows with kNarrowAhead items in
+// flight per lane, routing once; each lane holds its unit's activations of up to
+// two pairs in registers (loaded from global memory with their half sums formed
+// as everywhere else), and further pairs take another sweep of the rows.
+constexpr int kNarrowAhead = 8;
+
+template <bool XH>
+__global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
+  using It = Item<FMT_Q4_0>;
+  constexpr int D = kNarrowAhead;
+  constexpr int TPM = 2;
+  __shared__ IdShared sh;
+  const int RW = a.rows_per_wg;
+  const int r0 = blockIdx.x * RW;
+  const int rows = min(RW, a.M - r0);
+  const int e = id_route(a, r0, rows, sh);
+  if (e < 0) return;
+  const TokMap tm{sh.pairs, a.S, a.x_per_slot};
+  const int np = sh.npairs;
+  const int lane = threadIdx.x & 63;
+  const int gi = lane & 15;
+  const int per_step = 4 * (blockDim.x >> 6);             // rows per step of the workgroup
+  const int rsub = 4 * (threadIdx.x >> 6) + (lane >> 4);  // this lane's row within a step
+  const int steps = (rows + per_step - 1) / per_step;
+  const int steps_pad = (steps + D - 1) / D * D;
+  const u8* W = a.W + (u64)e * a.expert_bytes;
+  const u32 rb = static_cast<u32>(a.row_bytes);
+  auto load = [&](int st, typename It::Raw& w) {
+    It::load(W, (u32)(r0 + min(st * per_step + rsub, rows - 1)) * rb, gi, w);
+  };
+
+  for (int t0 = 0; t0 < np; t0 += TPM) {
+    const int tp = min(TPM, np - t0);
+    // this lane's unit of each pair's activations, and its two half sums
+    float xv[TPM][32], sx[TPM][2];
+#pragma unroll
+    for (int t = 0; t < TPM; ++t) {
+      const size_t xrow = static_cast<size_t>(tm.x(t0 + min(t, tp - 1)));
+      if constexpr (XH) {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(a.x) + xrow * a.K + 32 * gi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const h8 h = __builtin_bit_cast(h8, p[k]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xv[t][8 * k + q] = static_cast<float>(h[q]);
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + xrow * a.K + 32 * gi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 f = p[k];
+          xv[t][4 * k] = f.x; xv[t][4 * k + 1] = f.y; xv[t][4 * k + 2] = f.z; xv[t][4 * k + 3] = f.w;
+        }
+      }
+      sx[t][0] = half_sum16(xv[t]);
+      sx[t][1] = half_sum16(xv[t] + 16);
+    }
+
+    // one sweep of the rows for TP_ pairs: no branch in the steady loop, and
+    // every lane stores (rows past the slice repeat its last row, with the
+    // same bits, to the same place; the 16 lanes of a row hold the same sum), so
+    // the load counter's waits stay those of the ring
+    auto sweep = [&](auto tpc) {
+      constexpr int TP_ = decltype(tpc)::value;
+      typename It::Raw wr[D];
+      // step st from ring slot k, then (RELOAD) the slot refilled with step st + D
+      auto step = [&](auto reload, int k, int st) {
+        Unit o[1][1];
+        MixPairs<FMT_Q4_0> pk[1];
+        It::unpack(wr[k], o[0]);
+        pk[0].make(wr[k], o[0]);
+        if constexpr (decltype(reload)::value) load(st + D, wr[k]);
+        const int row = min(st * per_step + rsub, rows - 1);
+#pragma unroll
+        for (int t = 0; t < TP_; ++t) {
+          float v[1];
+          multi_run<FMT_Q4_0, 1>(pk, o, 0, xv[t], sx[t][0], sx[t][1], v);
+          a.y[(u64)tm.y(t0 + t) * a.M + r0 + row] = sum16(0.0f + v[0]);
+        }
+      };
+#pragma unroll
+      for (int k = 0; k < D; ++k) load(k, wr[k]);
+      int s0 = 0;
+      for (; s0 + D < steps_pad; s0 += D) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) step(std::true_type{}, k, s0 + k);
+      }
+#pragma unroll
+      for (int k = 0; k < D; ++k) step(std::false_type{}, k, s0 + k);
+    };
+    if (tp == 2)
+      sweep(std::integral_constant<int, 2>{});
+    else
+      sweep(std::integral_constant<int, 1>{});
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Host side: instance tables and launch-shape choice.
 
@@ -1045,7 +1149,10 @@ struct Tables {
   int one_regs[5][2][3];    // their VGPRs per lane (512 when unknown)
   GemvKernel multi[5][2];  // [format][fp16 activations], one row per thread
   GemvKernel multi_id[5][2];
+  GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
   Tables() {
+    narrow_id[0] = k_gemv_id_narrow<false>;
+    narrow_id[1] = k_gemv_id_narrow<true>;
     fill_multi<FMT_Q4_0>(multi[FMT_Q4_0], multi_id[FMT_Q4_0]);
     fill_multi<FMT_Q8_0>(multi[FMT_Q8_0], multi_id[FMT_Q8_0]);
     fill_multi<FMT_Q4_K>(multi[FMT_Q4_K], multi_id[FMT_Q4_K]);
@@ -1252,6 +1359,32 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   // the grid is ranks x row slices: about two workgroups per CU over all the
   // active experts
   const int M = static_cast<int>(m.M);
+  if (m.fmt == FMT_Q4_0 && nU == 16) {
+    // narrow rows: about two 256-thread workgroups per CU (as many as its
+    // registers let a CU hold) over the active experts, each streaming a slice of
+    // its expert's rows (a multiple of the 16 rows of a step)
+    const int slices = (2 * kCUs + ranks - 1) / ranks;
+    int RW = (M + slices - 1) / slices;
+    RW = (RW + 15) / 16 * 16;
+    GemvArgs a{};
+    a.W = m.blocks;
+    a.row_bytes = m.row_bytes;
+    a.expert_bytes = m.row_bytes * static_cast<u64>(m.M);
+    a.M = M;
+    a.nU = nU;
+    a.K = static_cast<int>(m.K);
+    a.rows_per_wg = RW;
+    a.x = x;
+    a.x_f16 = x_f16;
+    a.y = y;
+    a.N = N;
+    a.ids = ids;
+    a.S = S;
+    a.x_per_slot = x_per_slot;
+    a.E = static_cast<int>(m.n_experts);
+    hipLaunchKernelGGL(tables().narrow_id[x_f16 ? 1 : 0], dim3((M + RW - 1) / RW, ranks), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (m.fmt != FMT_Q8_0) {
     // the few-token layout per expert: about two workgroups per CU over the
     // active experts, each G row groups x id_rows rows per thread, the pairs

@@ -54,11 +54,12 @@ def test_gemm_id_shared_x(xdtype):
                   "gemm_id shared x")
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
-def test_gemm_id_equals_dense_for_one_expert(fmt):
-    """Every slot routed to expert e: identical bits to the dense path on expert e."""
+@pytest.mark.parametrize("fmt,K", [(f, 1024 if 1024 % oracle.block_weights(f) == 0 else 4 * oracle.block_weights(f))
+                                   for f in FORMATS] + [("q4_0", 512)])
+def test_gemm_id_equals_dense_for_one_expert(fmt, K):
+    """Every slot routed to expert e: identical bits to the dense path on expert e
+    (Q4_0 at K = 512 takes the narrow-row kernel)."""
     E, M, N, S = 4, 70, 3, 2
-    K = 1024 if 1024 % oracle.block_weights(fmt) == 0 else 4 * oracle.block_weights(fmt)
     blob, ws = _stack(fmt, E, M, K, 64)
     rb = oracle.row_bytes(fmt, K)
     g = np.random.default_rng(64)
