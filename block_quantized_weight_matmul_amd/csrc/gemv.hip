@@ -1003,7 +1003,7 @@ __global__ __launch_bounds__(512) void k_gemvn_id(GemvArgs a) {
 // flight per lane, routing once; each lane holds its unit's activations of up to
 // two pairs in registers (loaded from global memory with their half sums formed
 // as everywhere else), and further pairs take another sweep of the rows.
-constexpr int kNarrowAhead = 8;
+constexpr int kNarrowAhead = 4;
 
 template <bool XH>
 __global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
@@ -1360,12 +1360,15 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   // active experts
   const int M = static_cast<int>(m.M);
   if (m.fmt == FMT_Q4_0 && nU == 16) {
-    // narrow rows: about two 256-thread workgroups per CU (as many as its
-    // registers let a CU hold) over the active experts, each streaming a slice of
-    // its expert's rows (a multiple of the 16 rows of a step)
-    const int slices = (2 * kCUs + ranks - 1) / ranks;
+    // narrow rows: about four 256-thread workgroups per CU over the ranks, each
+    // streaming a slice of its expert's rows (a multiple of the 16 rows of a
+    // step), at least 128 rows so that the routing stays a small part of it.
+    // Measured on 128 experts of 4096 rows at 2, 8 and 24 tokens (slices of
+    // 128-1024 rows, rings of 4-16 items).
+    const int slices = (4 * kCUs + ranks - 1) / ranks;
     int RW = (M + slices - 1) / slices;
     RW = (RW + 15) / 16 * 16;
+    if (RW < 128) RW = 128;
     GemvArgs a{};
     a.W = m.blocks;
     a.row_bytes = m.row_bytes;
