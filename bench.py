@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--copy-probe", action="store_true", help="only run a 256 MiB device copy (counter calibration)")
     p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
                    help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
+    p.add_argument("--moe-only", default=None, metavar="N[,N...]",
+                   help="only time the expert-indexed matvec at these token counts (for profiling)")
     return p.parse_args()
 
 
@@ -362,7 +364,7 @@ def extra_moe(torch, q, W, args):
     ebytes = stack.size // E
     res = []
     C = 64
-    for n in W.MOE_TOKENS:
+    for n in ([int(t) for t in args.moe_only.split(",")] if args.moe_only else W.MOE_TOKENS):
         ids_h = [W.moe_ids(n, c) for c in range(C)]
         ids = [torch.from_numpy(i).to("cuda") for i in ids_h]
         x = torch.from_numpy(W.moe_x(n)).to("cuda")
@@ -378,7 +380,7 @@ def extra_moe(torch, q, W, args):
     # prefill-sized calls on the matrix cores (qmm_gemm_id_tiled), fp16 activations
     pre = []
     C = 8
-    for n in W.MOE_PREFILL_TOKENS:
+    for n in ([] if args.moe_only else W.MOE_PREFILL_TOKENS):
         ids_h = [W.moe_ids(n, c) for c in range(C)]
         ids = [torch.from_numpy(i).to("cuda") for i in ids_h]
         x = torch.from_numpy(W.moe_prefill_x(n)).to("cuda")
@@ -444,6 +446,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.moe_only:
+        print(json.dumps({"expert_matvec": extra_moe(torch, q, W, args)}), flush=True)
         return
     if args.prefill_only:
         mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
