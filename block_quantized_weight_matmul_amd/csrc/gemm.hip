@@ -90,6 +90,10 @@ __device__ __forceinline__ half2v bits_h2(u32 v) { return __builtin_bit_cast(hal
 // fp16 pairs (1024 + byte0, 1024 + byte1) and (1024 + byte2, 1024 + byte3) of c
 __device__ __forceinline__ half2v code_pair_lo(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0x64646464u, 0x00050004u)); }
 __device__ __forceinline__ half2v code_pair_hi(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0x64646464u, 0x00070006u)); }
+// fp16 pairs (byte0, byte1) * 2^-24 and (byte2, byte3) * 2^-24 of c: the bytes
+// as fp16 subnormals, exact, which the fp32 widening inside v_fma_mix keeps
+__device__ __forceinline__ half2v code_pair_lo_sub(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0u, 0x0C050C04u)); }
+__device__ __forceinline__ half2v code_pair_hi_sub(u32 c) { return bits_h2(__builtin_amdgcn_perm(c, 0u, 0x0C070C06u)); }
 
 // 8 weights from two code words (4 codes each, in bytes), packed fp16 path:
 // w = (code - zero) * d, with 1024 + zero subtracted exactly first.
@@ -99,6 +103,21 @@ __device__ __forceinline__ half8 weights_pk(u32 c0, u32 c1, half2v off, half2v d
   const half2v p2 = (code_pair_lo(c1) - off) * d;
   const half2v p3 = (code_pair_hi(c1) - off) * d;
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 8 weights from code bytes, fp32-coefficient path, codes as fp16 subnormals:
+// w = fp16(fma(code * 2^-24, a24, b)) with a24 = a * 2^24 (exact), so the fma
+// forms the same exact code * a + b, rounded once to fp32 then to fp16, as
+// fma(code, a, b) -- with no subtraction of an offset per pair.
+__device__ __forceinline__ half8 weights_sub(u32 c0, u32 c1, float a24, float b) {
+  const half2v p[4] = {code_pair_lo_sub(c0), code_pair_hi_sub(c0), code_pair_lo_sub(c1), code_pair_hi_sub(c1)};
+  half8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(p[i][0]), a24, b));
+    h[2 * i + 1] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(p[i][1]), a24, b));
+  }
+  return h;
 }
 
 // 8 weights, fp32-coefficient path: w = fp16(fma(code - off, a, b)); off is
@@ -222,12 +241,12 @@ template <> struct AStage<FMT_Q4_K> {
     const u32 m0 = __builtin_amdgcn_alignbit(h[3], h[2], bm & 31u);
     const u32 m1 = h[3] >> (bm & 31u);
     const u32 m = (bm < 64 ? m0 : m1) & 63u;
-    const float a = h2f(h[0]) * static_cast<float>(sc) * (hi ? 0.0625f : 1.0f);  // exact
-    const float b = -(h2f(h[0] >> 16) * static_cast<float>(m));                     // exact
+    // a * 2^24, exact: the codes enter as fp16 subnormals (code * 2^-24)
+    const float a24 = h2f(h[0]) * static_cast<float>(sc) * (hi ? 1048576.0f : 16777216.0f);
+    const float b = -(h2f(h[0] >> 16) * static_cast<float>(m));  // exact
     const u32 mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-    const half2v off = half2v{1024, 1024};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) A[j] = weights_mix<true>(q[2 * j] & mask, q[2 * j + 1] & mask, off, a, b);
+    for (int j = 0; j < 2; ++j) A[j] = weights_sub(q[2 * j] & mask, q[2 * j + 1] & mask, a24, b);
   }
 };
 
@@ -277,12 +296,11 @@ template <> struct AStage<FMT_A4G64> {
   }
   __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
     const bool hi = (g >> 1) != 0;
-    const float a = h2f(hdr) * (hi ? 0.0625f : 1.0f);  // exact
+    const float a24 = h2f(hdr) * (hi ? 1048576.0f : 16777216.0f);  // scale * 2^24 (/16 high), exact
     const float b = h2f(hdr >> 16);
     const u32 mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-    const half2v off = half2v{1024, 1024};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) A[j] = weights_mix<true>(q[2 * j] & mask, q[2 * j + 1] & mask, off, a, b);
+    for (int j = 0; j < 2; ++j) A[j] = weights_sub(q[2 * j] & mask, q[2 * j + 1] & mask, a24, b);
   }
 };
 
