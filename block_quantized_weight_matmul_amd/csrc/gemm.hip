@@ -718,11 +718,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   }
   if (e < 0) return;  // uniform over the workgroup
 
-  // pairs routed to e, in ascending order: thread segments, then an exclusive scan
-  const int L = (P + 255) / 256;
+  // pairs routed to e, in ascending order: thread segments (a multiple of 4 ids,
+  // read 16 bytes at a time when the ids are 16-byte aligned), then an
+  // exclusive scan
+  const int L = ((P + 255) / 256 + 3) & ~3;
   const int s0 = min(P, tid * L), s1 = min(P, s0 + L);
+  const bool vec = (reinterpret_cast<uintptr_t>(a.ids) & 15) == 0;
+  auto visit = [&](auto fn) {
+    int p = s0;
+    if (vec)
+      for (; p + 4 <= s1; p += 4) {
+        const int4 v = *reinterpret_cast<const int4*>(a.ids + p);
+        fn(p, v.x); fn(p + 1, v.y); fn(p + 2, v.z); fn(p + 3, v.w);
+      }
+    for (; p < s1; ++p) fn(p, a.ids[p]);
+  };
   int mine = 0;
-  for (int p = s0; p < s1; ++p) mine += a.ids[p] == e;
+  visit([&](int, int id) { mine += id == e; });
   {
     int incl = mine;
 #pragma unroll
@@ -760,14 +772,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   for (int tok0 = 0; tok0 < count; tok0 += TT) {
     // this super-tile's pairs and activation rows
     int pos = sh.base[tid];
-    for (int p = s0; p < s1; ++p)
-      if (a.ids[p] == e) {
+    visit([&](int p, int id) {
+      if (id == e) {
         if (pos >= tok0 && pos < tok0 + TT) {
           sh.pair[pos - tok0] = p;
           sh.xrow[pos - tok0] = a.x_per_slot ? p : p / a.S;
         }
         ++pos;
       }
+    });
     __syncthreads();
     const int rem = count - tok0;
     const int ntb = rem >= TT ? NTB : ((rem + T - 1) / T) * (T / 16);
