@@ -704,16 +704,21 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   }
   __syncthreads();
   const int e = sh.expert;
-  const int r_lo = blockIdx.x * 64 * RB;
-  const int r_hi = min(a.M, r_lo + 64 * RB);
-  // ids outside [0, E): NaN rows, written by the rank-0 workgroup of each row tile
+  // the workgroup takes row tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
+  // its expert, routing once for all of them
+  const int n_tiles = (a.M + 64 * RB - 1) / (64 * RB);
+  // ids outside [0, E): NaN rows, written by the rank-0 workgroups (which cover
+  // every row tile)
   if (blockIdx.y == 0 && sh.bad) {
     const float qnan = __builtin_nanf("");
-    const int nr = r_hi - r_lo;
-    for (int i = tid; i < P * nr; i += 256) {
-      const int p = i / nr, r = r_lo + (i - p * nr);
-      const int id = a.ids[p];
-      if (id < 0 || id >= a.E) a.y[(u64)p * a.M + r] = qnan;
+    for (int rt = blockIdx.x; rt < n_tiles; rt += gridDim.x) {
+      const int r_lo = rt * 64 * RB;
+      const int nr = min(a.M, r_lo + 64 * RB) - r_lo;
+      for (int i = tid; i < P * nr; i += 256) {
+        const int p = i / nr, r = r_lo + (i - p * nr);
+        const int id = a.ids[p];
+        if (id < 0 || id >= a.E) a.y[(u64)p * a.M + r] = qnan;
+      }
     }
   }
   if (e < 0) return;  // uniform over the workgroup
@@ -757,6 +762,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
 
   GemmArgs ae = a;
   ae.W = a.W + static_cast<u64>(e) * a.expert_bytes;
+  const int o0 = x_slot(lane & 15, 2 * g);
+  const int o1 = x_slot(lane & 15, 2 * g + 1);
+  const int all = (a.nU + 1) >> 1;
+  constexpr int ES = XF16 ? 2 : 4;
+
+  for (int rt = blockIdx.x; rt < n_tiles; rt += gridDim.x) {
+  const int r_lo = rt * 64 * RB;
   const int rw0 = r_lo + (tid >> 6) * (16 * RB);  // this wave's first row
   u32 row_off[RB];
 #pragma unroll
@@ -764,11 +776,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
     const int r = rw0 + 16 * b + (lane & 15);
     row_off[b] = static_cast<u32>(r < a.M ? r : a.M - 1) * a.row_bytes;
   }
-  const int o0 = x_slot(lane & 15, 2 * g);
-  const int o1 = x_slot(lane & 15, 2 * g + 1);
-  const int all = (a.nU + 1) >> 1;
-  constexpr int ES = XF16 ? 2 : 4;
-
   for (int tok0 = 0; tok0 < count; tok0 += TT) {
     // this super-tile's pairs and activation rows
     int pos = sh.base[tid];
@@ -812,6 +819,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
       }
     }
     __syncthreads();  // sX, pair and xrow are refilled for the next super-tile
+  }
   }
 }
 
@@ -1001,9 +1009,13 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
+  // about two workgroups per CU over the ranks, each taking every
+  // gridDim.x-th row tile of its expert (the routing is done once per workgroup)
   const int64_t row_tiles = (m.M + 63) / 64;
   if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(row_tiles), static_cast<unsigned>(ranks)), dim3(256), 0, st, a);
+  int64_t groups = (2 * kCUs + ranks - 1) / ranks;
+  if (groups > row_tiles) groups = row_tiles;
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(groups), static_cast<unsigned>(ranks)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
