@@ -51,10 +51,12 @@ struct GemmArgs {
   int n_row_tiles;  // blockIdx.x = super_tile * n_row_tiles + row_tile
   int split_stages; // K stages per split (blockIdx.y = split); all of K when unsplit
   u64 split_floats; // floats between the splits' partial outputs (0 when unsplit)
-  // expert-indexed (k_gemm_id): ids [N, S], E experts of expert_bytes each
+  // expert-indexed (k_gemm_id): ids [N, S], E experts of expert_bytes each;
+  // id_groups row-tile groups per expert rank, ranks padded to a multiple of 8
   const int32_t* ids;
   int S, x_per_slot, E;
   u64 expert_bytes;
+  int id_groups, id_ranks;
 };
 
 constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
@@ -657,6 +659,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 sX[2][TT * kKS];
   __shared__ MmIdShared sh;
 
+  // workgroup i runs on XCD i mod 8: the row-tile groups of one expert rank get
+  // ids that are equal mod 8, so they share that XCD's L2 for the expert's
+  // activation rows (read once per row tile)
+  const int wid = blockIdx.x;
+  const int xcd = wid & 7, q = wid >> 3;
+  const int grp = q % a.id_groups;
+  const int rank = (q / a.id_groups) * 8 + xcd;
+  if (rank >= a.id_ranks) return;  // padding of the rank count (uniform)
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int g = lane >> 4;
@@ -675,7 +686,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
       sh.bad = 1;
   }
   __syncthreads();
-  // the blockIdx.y-th set bit (first wave)
+  // the rank-th set bit (first wave)
   if (tid < 64) {
     const int wpl = (nwords + 63) >> 6;
     const int w0 = tid * wpl, w1 = min(nwords, w0 + wpl);
@@ -688,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
       if (tid >= off) incl += v;
     }
     const int excl = incl - cnt;
-    const int k = blockIdx.y;
+    const int k = rank;
     if (k >= excl && k < incl) {
       int seen = excl;
       for (int w = w0; w < w1; ++w) {
@@ -704,14 +715,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   }
   __syncthreads();
   const int e = sh.expert;
-  // the workgroup takes row tiles blockIdx.x, blockIdx.x + gridDim.x, ... of
-  // its expert, routing once for all of them
+  // the workgroup takes row tiles grp, grp + id_groups, ... of its expert,
+  // routing once for all of them
   const int n_tiles = (a.M + 64 * RB - 1) / (64 * RB);
   // ids outside [0, E): NaN rows, written by the rank-0 workgroups (which cover
   // every row tile)
-  if (blockIdx.y == 0 && sh.bad) {
+  if (rank == 0 && sh.bad) {
     const float qnan = __builtin_nanf("");
-    for (int rt = blockIdx.x; rt < n_tiles; rt += gridDim.x) {
+    for (int rt = grp; rt < n_tiles; rt += a.id_groups) {
       const int r_lo = rt * 64 * RB;
       const int nr = min(a.M, r_lo + 64 * RB) - r_lo;
       for (int i = tid; i < P * nr; i += 256) {
@@ -767,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   const int all = (a.nU + 1) >> 1;
   constexpr int ES = XF16 ? 2 : 4;
 
-  for (int rt = blockIdx.x; rt < n_tiles; rt += gridDim.x) {
+  for (int rt = grp; rt < n_tiles; rt += a.id_groups) {
   const int r_lo = rt * 64 * RB;
   const int rw0 = r_lo + (tid >> 6) * (16 * RB);  // this wave's first row
   u32 row_off[RB];
@@ -1015,7 +1026,10 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
   if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
   int64_t groups = (2 * kCUs + ranks - 1) / ranks;
   if (groups > row_tiles) groups = row_tiles;
-  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(groups), static_cast<unsigned>(ranks)), dim3(256), 0, st, a);
+  const int64_t ranks8 = (ranks + 7) / 8 * 8;
+  a.id_groups = static_cast<int>(groups);
+  a.id_ranks = static_cast<int>(ranks);
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(groups * ranks8)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
