@@ -740,14 +740,43 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   const int L = ((P + 255) / 256 + 3) & ~3;
   const int s0 = min(P, tid * L), s1 = min(P, s0 + L);
   const bool vec = (reinterpret_cast<uintptr_t>(a.ids) & 15) == 0;
+  // 16-byte output stores: rows r .. r+3 of a pair's output row (M % 4 == 0, y
+  // 16-byte aligned)
+  const bool y_vec = (a.M % 4 == 0) && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
   auto visit = [&](auto fn) {
     int p = s0;
-    if (vec)
+    if (vec) {
+      // 16 ids per round, their four loads issued before any is examined
+      for (; p + 16 <= s1; p += 16) {
+        int4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const int4*>(a.ids + p + 4 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          fn(p + 4 * j, v[j].x); fn(p + 4 * j + 1, v[j].y); fn(p + 4 * j + 2, v[j].z); fn(p + 4 * j + 3, v[j].w);
+        }
+      }
       for (; p + 4 <= s1; p += 4) {
         const int4 v = *reinterpret_cast<const int4*>(a.ids + p);
         fn(p, v.x); fn(p + 1, v.y); fn(p + 2, v.z); fn(p + 3, v.w);
       }
+    }
     for (; p < s1; ++p) fn(p, a.ids[p]);
+  };
+  // the pairs of super-tile tok0 (positions tok0 .. tok0 + TT - 1 of the
+  // ascending list) into sh.pair / sh.xrow
+  auto gather = [&](int tok0) {
+    int pos = sh.base[tid];
+    visit([&](int p, int id) {
+      if (id == e) {
+        if (pos >= tok0 && pos < tok0 + TT) {
+          sh.pair[pos - tok0] = p;
+          sh.xrow[pos - tok0] = a.x_per_slot ? p : p / a.S;
+        }
+        ++pos;
+      }
+    });
+    __syncthreads();
   };
   int mine = 0;
   visit([&](int, int id) { mine += id == e; });
@@ -778,6 +807,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   const int all = (a.nU + 1) >> 1;
   constexpr int ES = XF16 ? 2 : 4;
 
+  // one super-tile of pairs: gathered once for all the row tiles
+  const bool one_tile = count <= TT;
+  if (one_tile) gather(0);
   for (int rt = grp; rt < n_tiles; rt += a.id_groups) {
   const int r_lo = rt * 64 * RB;
   const int rw0 = r_lo + (tid >> 6) * (16 * RB);  // this wave's first row
@@ -789,17 +821,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   }
   for (int tok0 = 0; tok0 < count; tok0 += TT) {
     // this super-tile's pairs and activation rows
-    int pos = sh.base[tid];
-    visit([&](int p, int id) {
-      if (id == e) {
-        if (pos >= tok0 && pos < tok0 + TT) {
-          sh.pair[pos - tok0] = p;
-          sh.xrow[pos - tok0] = a.x_per_slot ? p : p / a.S;
-        }
-        ++pos;
-      }
-    });
-    __syncthreads();
+    if (!one_tile) gather(tok0);
     const int rem = count - tok0;
     const int ntb = rem >= TT ? NTB : ((rem + T - 1) / T) * (T / 16);
     XLanes<TT, ES> xl;
@@ -823,13 +845,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
         for (int b = 0; b < RB; ++b) {
           const int r = rw0 + 16 * b + 4 * g;
           float* yp = a.y + (u64)p * a.M + r;
+          if (y_vec && r + 3 < a.M) {
+            *reinterpret_cast<float4*>(yp) = make_float4(acc[b][t][0], acc[b][t][1], acc[b][t][2], acc[b][t][3]);
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (r + v < a.M) yp[v] = acc[b][t][v];
+            for (int v = 0; v < 4; ++v)
+              if (r + v < a.M) yp[v] = acc[b][t][v];
+          }
         }
       }
     }
-    __syncthreads();  // sX, pair and xrow are refilled for the next super-tile
+    __syncthreads();  // sX (and pair, xrow) are refilled for the next super-tile
   }
   }
 }
