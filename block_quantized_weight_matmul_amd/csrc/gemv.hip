@@ -1023,7 +1023,8 @@ __global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
   const int per_step = 4 * (blockDim.x >> 6);             // rows per step of the workgroup
   const int rsub = 4 * (threadIdx.x >> 6) + (lane >> 4);  // this lane's row within a step
   const int steps = (rows + per_step - 1) / per_step;
-  const int steps_pad = (steps + D - 1) / D * D;
+  static_assert(8 % D == 0, "the ring divides a block of 8 steps");
+  const int steps_pad = (steps + 7) / 8 * 8;  // whole blocks of 8 steps
   const u8* W = a.W + (u64)e * a.expert_bytes;
   const u32 rb = static_cast<u32>(a.row_bytes);
   auto load = [&](int st, typename It::Raw& w) {
@@ -1058,37 +1059,51 @@ __global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
       sx[t][1] = half_sum16(xv[t] + 16);
     }
 
-    // one sweep of the rows for TP_ pairs: no branch in the steady loop, and
-    // every lane stores (rows past the slice repeat its last row, with the
-    // same bits, to the same place; the 16 lanes of a row hold the same sum), so
-    // the load counter's waits stay those of the ring
+    // one sweep of the rows for TP_ pairs: no branch in the steady loop, so the
+    // load counter's waits stay those of the ring
     auto sweep = [&](auto tpc) {
       constexpr int TP_ = decltype(tpc)::value;
       typename It::Raw wr[D];
-      // step st from ring slot k, then (RELOAD) the slot refilled with step st + D
+      // lane gi keeps the sum of step 8 b + gi % 8 of each block b of 8 steps
+      // (the 16 lanes of a row all hold each step's sum) and stores it once per
+      // block: two lanes per output instead of sixteen
+      float outv[TP_];
+      // step st (slot k % D of the ring, step k of the block), then (RELOAD) the
+      // slot refilled with step st + D
       auto step = [&](auto reload, int k, int st) {
         Unit o[1][1];
         MixPairs<FMT_Q4_0> pk[1];
-        It::unpack(wr[k], o[0]);
-        pk[0].make(wr[k], o[0]);
-        if constexpr (decltype(reload)::value) load(st + D, wr[k]);
-        const int row = min(st * per_step + rsub, rows - 1);
+        It::unpack(wr[k % D], o[0]);
+        pk[0].make(wr[k % D], o[0]);
+        if constexpr (decltype(reload)::value) load(st + D, wr[k % D]);
 #pragma unroll
         for (int t = 0; t < TP_; ++t) {
           float v[1];
           multi_run<FMT_Q4_0, 1>(pk, o, 0, xv[t], sx[t][0], sx[t][1], v);
-          a.y[(u64)tm.y(t0 + t) * a.M + r0 + row] = sum16(0.0f + v[0]);
+          const float sum = sum16(0.0f + v[0]);
+          outv[t] = (gi & 7) == k ? sum : outv[t];
         }
+      };
+      // the block's stores: step s0 + gi % 8's row (rows past the slice repeat
+      // its last row, with the same bits)
+      auto store = [&](int s0) {
+        const int row = min((s0 + (gi & 7)) * per_step + rsub, rows - 1);
+#pragma unroll
+        for (int t = 0; t < TP_; ++t) a.y[(u64)tm.y(t0 + t) * a.M + r0 + row] = outv[t];
       };
 #pragma unroll
       for (int k = 0; k < D; ++k) load(k, wr[k]);
       int s0 = 0;
-      for (; s0 + D < steps_pad; s0 += D) {
+      for (; s0 + 8 < steps_pad; s0 += 8) {
 #pragma unroll
-        for (int k = 0; k < D; ++k) step(std::true_type{}, k, s0 + k);
+        for (int k = 0; k < 8; ++k) step(std::true_type{}, k, s0 + k);
+        store(s0);
       }
 #pragma unroll
-      for (int k = 0; k < D; ++k) step(std::false_type{}, k, s0 + k);
+      for (int k = 0; k < 8 - D; ++k) step(std::true_type{}, k, s0 + k);
+#pragma unroll
+      for (int k = 8 - D; k < 8; ++k) step(std::false_type{}, k, s0 + k);
+      store(s0);
     };
     if (tp == 2)
       sweep(std::integral_constant<int, 2>{});
