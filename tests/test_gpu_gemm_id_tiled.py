@@ -40,8 +40,10 @@ def _check(fmt, y, x, ids, ws, label):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("N,S", [(33, 8), (100, 4)])
+@pytest.mark.parametrize("N,S", [(33, 8), (100, 4), (64, 8)])
 def test_gemm_id_tiled_parity_and_tiles(fmt, N, S):
+    """(64, 8): 51 pairs per expert on average, past the 48 that selects the
+    128-token super-tile, and each expert's pairs within one super-tile."""
     E, M = 10, 96
     K = 512 if 512 % oracle.block_weights(fmt) == 0 else 2 * oracle.block_weights(fmt)
     blob, ws = _stack(fmt, E, M, K, 81)
