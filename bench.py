@@ -62,7 +62,8 @@ def parse():
     p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
                    help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
     p.add_argument("--moe-only", default=None, metavar="N[,N...]",
-                   help="only time the expert-indexed matvec at these token counts (for profiling)")
+                   help="only time the expert-indexed paths at these token counts: the matvec up to 32 "
+                        "tokens, the matrix-core path above (for profiling)")
     return p.parse_args()
 
 
@@ -364,7 +365,8 @@ def extra_moe(torch, q, W, args):
     ebytes = stack.size // E
     res = []
     C = 64
-    for n in ([int(t) for t in args.moe_only.split(",")] if args.moe_only else W.MOE_TOKENS):
+    only = [int(t) for t in args.moe_only.split(",")] if args.moe_only else None
+    for n in ([t for t in only if t <= 32] if only else W.MOE_TOKENS):
         ids_h = [W.moe_ids(n, c) for c in range(C)]
         ids = [torch.from_numpy(i).to("cuda") for i in ids_h]
         x = torch.from_numpy(W.moe_x(n)).to("cuda")
@@ -380,7 +382,7 @@ def extra_moe(torch, q, W, args):
     # prefill-sized calls on the matrix cores (qmm_gemm_id_tiled), fp16 activations
     pre = []
     C = 8
-    for n in ([] if args.moe_only else W.MOE_PREFILL_TOKENS):
+    for n in ([t for t in only if t > 32] if only else W.MOE_PREFILL_TOKENS):
         ids_h = [W.moe_ids(n, c) for c in range(C)]
         ids = [torch.from_numpy(i).to("cuda") for i in ids_h]
         x = torch.from_numpy(W.moe_prefill_x(n)).to("cuda")

@@ -28,6 +28,7 @@
 // RB are; T only changes how many padding blocks of the last super-tile are
 // computed (and never stored).
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <type_traits>
 
@@ -923,6 +924,29 @@ GemmKernel pick_id(bool xf16) {
   return k_gemm_id<F, 1, TT, false>;
 }
 
+// Workgroups of 256 threads (one wave per SIMD each) of kernel k that one CU
+// holds at once: 512 registers per SIMD lane over the kernel's register count,
+// and 160 KB of LDS over its LDS size; 2 when the attributes are unavailable,
+// at most 3.  Memoised per (format, super-tile, activation type).
+int id_resident_per_cu(int fmt, int TT, bool xf16, GemmKernel k) {
+  static std::atomic<int> memo[5][2][2];
+  std::atomic<int>& slot = memo[fmt][TT == 128 ? 1 : 0][xf16 ? 1 : 0];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  hipFuncAttributes at{};
+  n = 2;
+  if (hipFuncGetAttributes(&at, reinterpret_cast<const void*>(k)) == hipSuccess && at.numRegs > 0) {
+    const int by_regs = 512 / ((at.numRegs + 7) / 8 * 8);
+    const int by_lds = at.sharedSizeBytes > 0 ? static_cast<int>(163840 / at.sharedSizeBytes) : by_regs;
+    n = std::min(by_regs, by_lds);
+    n = std::max(2, std::min(3, n));
+  } else {
+    (void)hipGetLastError();
+  }
+  slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
 constexpr int64_t kCUs = 256;
 }  // namespace
 
@@ -1049,11 +1073,15 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
-  // about two workgroups per CU over the ranks, each taking every
-  // gridDim.x-th row tile of its expert (the routing is done once per workgroup)
+  // as many workgroups over the ranks as the CUs hold at once (3 per CU for the
+  // 64-token super-tile's registers, 2 for the 128-token one), each taking
+  // every groups-th row tile of its expert (the routing is done once per
+  // workgroup); a second round of workgroups measured slower than fewer,
+  // longer ones
   const int64_t row_tiles = (m.M + 63) / 64;
   if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
-  int64_t groups = (2 * kCUs + ranks - 1) / ranks;
+  const int64_t per_cu = id_resident_per_cu(m.fmt, TT, xf16, k);
+  int64_t groups = (per_cu * kCUs + ranks - 1) / ranks;
   if (groups > row_tiles) groups = row_tiles;
   const int64_t ranks8 = (ranks + 7) / 8 * 8;
   a.id_groups = static_cast<int>(groups);
