@@ -3,7 +3,7 @@
 The seeded workloads of the benchmark (the seven decode-layer projections, the
 4-bit-group layer, the prefill GEMM at 7 .. 2048 tokens, the 128-expert matvec
 and its prefill-sized tiled form) run through the same entry points and launch
-shapes as bench.py.  The oracle cannot take whole outputs at these sizes, so it
+shapes as bench.py; so do one-eighth row shards of three projections.  The oracle cannot take whole outputs at these sizes, so it
 computes sampled outputs one by one: the sampled rows' blocks are dequantized by
 the oracle and multiplied by the given activations in fp64.  Tolerances are
 those of the smaller tests: 1e-5 * S on the fp32-accumulating matrix-vector
@@ -104,6 +104,41 @@ def test_prefill_gemm(n):
         assert torch.equal(ys[32].view(torch.int32), ys[64].view(torch.int32)), f"{m['name']} n={n}: tiles differ"
         rows = sample_rows(m["M"], [82, j, n], k=24)
         check_rows(to_host(ys[64]), x.astype(np.float32), m, rows, TOL_GEMM, f"prefill {m['name']} n={n}")
+
+
+SHARDS = 8  # row shards of one GPU's share when a layer is split over eight
+
+
+@pytest.mark.parametrize("j", [0, 4, 6], ids=["attn_q", "ffn_gate", "ffn_down"])
+@pytest.mark.parametrize("n", [1, 512])
+def test_row_shard(j, n):
+    """One GPU's row shard of a projection (rows [3M/8, 4M/8): 512x2560,
+    1216x2560, 320x9728) is an ordinary matrix of M/8 rows: the one-token GEMV
+    and the 512-token GEMM on it, sampled outputs against the oracle on the
+    shard's own rows, tiles bit-identical."""
+    m = decode_matrix(j)
+    rb = oracle.row_bytes(m["fmt"], m["K"])
+    Ms = m["M"] // SHARDS
+    r0 = 3 * Ms
+    shard = dict(m, M=Ms, blob=m["blob"][r0 * rb:(r0 + Ms) * rb])
+    qm = q.QMatrix(to_dev(shard["blob"]), m["fmt"], Ms, m["K"])
+    rows = sample_rows(Ms, [86, j, n], k=24)
+    if n == 1:
+        x = W.decode_x(j)
+        y = torch.empty((1, Ms), device="cuda")
+        q.qmm_gemv(qm.handle, to_dev(x), 1, y)
+        check_rows(to_host(y), x, shard, rows, TOL_GEMV, f"shard {m['name']} n=1")
+        return
+    x = W.prefill_x(j, n)
+    nb = q.qmm_gemm_workspace_bytes(qm.handle, n)
+    ws = torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None
+    xd = to_dev(x)
+    ys = {}
+    for t in (32, 64):
+        ys[t] = torch.empty((n, Ms), device="cuda")
+        q.qmm_gemm_ws(qm.handle, xd, n, ys[t], t, ws)
+    assert torch.equal(ys[32].view(torch.int32), ys[64].view(torch.int32)), f"shard {m['name']}: tiles differ"
+    check_rows(to_host(ys[64]), x.astype(np.float32), shard, rows, TOL_GEMM, f"shard {m['name']} n={n}")
 
 
 def _moe_rows_check(y, x, ids, rows, tol, label):
