@@ -918,10 +918,17 @@ GemmKernel pick(int RB, int TT, bool xf16) {
        : TT == 64 ? kernel_if_ok<F, false, 1, 64>() : kernel_if_ok<F, false, 1, 32>();
 }
 
+// 128-row workgroups at the 64-token super-tile (twice the weight bytes in
+// flight per workgroup; Q6_K's decode would not fit the registers), 64 rows at
+// the 128-token one
+template <int F, int TT>
+constexpr int id_rows_blocks() { return TT == 64 && F != FMT_Q6_K ? 2 : 1; }
+
 template <int F, int TT>
 GemmKernel pick_id(bool xf16) {
-  if (xf16) return k_gemm_id<F, 1, TT, true>;
-  return k_gemm_id<F, 1, TT, false>;
+  constexpr int RB = id_rows_blocks<F, TT>();
+  if (xf16) return k_gemm_id<F, RB, TT, true>;
+  return k_gemm_id<F, RB, TT, false>;
 }
 
 // Workgroups of 256 threads (one wave per SIMD each) of kernel k that one CU
@@ -1073,12 +1080,13 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
-  // as many workgroups over the ranks as the CUs hold at once (3 per CU for the
-  // 64-token super-tile's registers, 2 for the 128-token one), each taking
+  const int RB = TT == 64 && m.fmt != FMT_Q6_K ? 2 : 1;  // as id_rows_blocks
+  // as many workgroups over the ranks as the CUs hold at once (from the
+  // kernel's registers and LDS: two for each of these kernels), each taking
   // every groups-th row tile of its expert (the routing is done once per
   // workgroup); a second round of workgroups measured slower than fewer,
   // longer ones
-  const int64_t row_tiles = (m.M + 63) / 64;
+  const int64_t row_tiles = (m.M + 64 * RB - 1) / (64 * RB);
   if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
   const int64_t per_cu = id_resident_per_cu(m.fmt, TT, xf16, k);
   int64_t groups = (per_cu * kCUs + ranks - 1) / ranks;
