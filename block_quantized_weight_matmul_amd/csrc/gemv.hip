@@ -1301,13 +1301,16 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
   }
   if (N >= 2 && m.fmt != FMT_Q8_0) {
     // A few tokens: the one-token layout with one row per thread (two would
-    // spill registers with fp32 activations), about one workgroup per CU, TGN
-    // token groups filling up to 512 threads, TP tokens per pass as the LDS
-    // budget and kXNRounds staging rounds allow.
+    // spill registers with fp32 activations), about one workgroup per CU (two
+    // above 8 tokens, where the products outweigh staging the activations once
+    // more: the 4-bit-group layer at 16 tokens 53.6 -> 50.5 us, while 2 and 4
+    // tokens lose 4-5%), TGN token groups filling up to 512 threads, TP tokens
+    // per pass as the LDS budget and kXNRounds staging rounds allow.
     const int ipr2 = nU / kRuns[m.fmt];
     const int Gmax = 512 / ipr2;
     if (Gmax >= 1) {
-      const int want = (M + kCUs - 1) / kCUs;
+      const int per_cu = N > 8 ? 2 : 1;
+      const int want = (M + kCUs * per_cu - 1) / (kCUs * per_cu);
       const int R = 1;
       int Ge = (want + R - 1) / R;
       if (Ge > Gmax) Ge = Gmax;
