@@ -181,5 +181,11 @@ def dequantize(fmt: str, blob: np.ndarray, M: int, K: int) -> np.ndarray:
 
 def staged_fp16(w: np.ndarray) -> np.ndarray:
     """The fp16 value a weight takes when staged for the fp16 matrix-core product:
-    round-to-nearest-even of the fp32 dequantized value (NumPy's cast is RNE)."""
-    return np.asarray(w, dtype=np.float32).astype(np.float16)
+    round-to-nearest-even of the fp32 dequantized value (NumPy's cast is RNE; a
+    magnitude at or above the overflow tie 65520 becomes an infinity, as IEEE
+    rounding defines).  The candle pull request "Metal: 64-token tile for the
+    quantized matrix-matrix kernel" (section "Why the tile sets the weight reuse")
+    decodes each weight tile into threadgroup memory for the matrix product; read
+    here as the fp32 weight rounded once more, to fp16."""
+    with np.errstate(over="ignore"):
+        return np.asarray(w, dtype=np.float32).astype(np.float16)

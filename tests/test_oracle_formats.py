@@ -10,6 +10,7 @@
 * structural invariants on random bytes.
 """
 
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -17,7 +18,7 @@ import pytest
 
 import oracle
 from qmm_synth import quantize
-from tests.golden_io import read_blocks
+from tests.golden_io import GOLDEN, read_blocks
 
 CASES = read_blocks()
 
@@ -157,3 +158,62 @@ def test_random_bytes_structure(fmt):
     elif fmt == "q6_k":
         r = w[nz] / d[nz]
         assert np.all(r == np.round(r)) and np.abs(r).max() <= 4096
+
+
+# --- the fp16 staging value of the matrix-matrix path -----------------------------------------
+# staged_fp16 is the fp16 round-to-nearest-even (ties to even) of the fp32 dequantized weight.
+# Pins from the IEEE binary16 grid: ulp 2^-10 in [1, 2), 2^-9 in [2, 4), subnormal step 2^-24,
+# largest finite 65504 (the next value up would be 65536, so 65520 is the overflow tie).
+
+STAGING_PINS = [
+    (1.0 + 2.0 ** -11, 1.0),                  # tie below an even significand -> down
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),  # tie above an odd significand -> up (to even)
+    (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),  # just above the tie -> up
+    (2.0 + 2.0 ** -10, 2.0),                  # the staging tie of the double-rounding golden blocks
+    (-(2.0 + 3 * 2.0 ** -10), -(2.0 + 2.0 ** -8)),
+    (2.0 ** -25, 0.0),                        # half the smallest subnormal: tie to even zero
+    (3 * 2.0 ** -25, 2.0 ** -23),             # 1.5 subnormal steps -> 2 steps
+    (2.0 ** -24, 2.0 ** -24),                 # subnormals are kept, not flushed
+    (1023 * 2.0 ** -24, 1023 * 2.0 ** -24),
+    (65504.0, 65504.0),
+    (65519.0, 65504.0),                       # below the overflow tie
+    (65520.0, float("inf")),                  # the overflow tie rounds to infinity
+    (-65520.0, float("-inf")),
+]
+
+
+@pytest.mark.parametrize("w,expect", STAGING_PINS)
+def test_staged_fp16_pins(w, expect):
+    w32 = np.float32(w)
+    assert float(w32) == w  # every input above is an fp32 value
+    got = oracle.staged_fp16(np.array([w32]))
+    assert got.dtype == np.float16
+    assert float(got[0]) == expect
+
+
+def test_staged_fp16_keeps_signed_zero():
+    got = oracle.staged_fp16(np.array([-0.0, 0.0, -2.0 ** -26], np.float32))
+    assert np.signbit(got).tolist() == [True, False, True]
+    assert got.tolist() == [0.0, 0.0, 0.0]
+
+
+def test_staged_fp16_of_double_rounding_blocks():
+    # the golden blocks built so that rounding the exact weight once to fp16 would give
+    # 2+2^-9: staging rounds the fp32 weight, so weight 0 stages as 2.0
+    for case in CASES:
+        if case["name"].endswith("_fp16_staging_double_rounding"):
+            w = oracle.dequantize_blocks(case["fmt"], np.frombuffer(case["data"], np.uint8))[0]
+            assert float(w[0]) == 2.0 + 2.0 ** -10
+            exact = case["expect"][0]
+            assert float(oracle.staged_fp16(w)[0]) == 2.0
+            # and the tie is a real one: the exact value lies strictly above the fp16 midpoint
+            assert exact == Fraction(2) + Fraction(1, 1024)
+            assert float(np.float16(float(Fraction(2) + Fraction(1, 1024) + Fraction(1, 2 ** 24)))) == 2.0 + 2.0 ** -9
+
+
+def test_golden_file_matches_its_packer():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(GOLDEN, "pack_blocks.py"), "--check"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -127,3 +127,34 @@ def test_matmul_id_invalid_ids_are_nan():
     assert np.all(np.isfinite(y[0, 0])) and np.all(np.isfinite(y[1, 1]))
     s = oracle.tolerance_scale_id(x, ids, experts)
     assert np.all(np.isnan(s[0, 1])) and np.all(s[1, 1] >= 0)
+
+
+def test_tolerance_scale_id_against_exact_rationals():
+    """S[t, s, r] = sum_k |x_ts[k] * w_e[r, k]| with e = ids[t, s], as exact fractions.  The
+    activations and weights take both signs, so a missing absolute value on either operand, a
+    sum over the wrong expert, or the wrong slot's activations changes S by far more than fp64
+    rounding."""
+    g = np.random.default_rng(27)
+    E, M, K, N, S = 3, 4, 64, 2, 3
+    experts = [oracle.dequantize("q4_0", quantize("q4_0", g.normal(0, 0.02, (M, K)).astype(np.float32)), M, K)
+               for _ in range(E)]
+    assert all((w < 0).any() and (w > 0).any() for w in experts)
+    ids = np.array([[2, 0, 2], [1, 5, 0]], np.int32)
+    for per_slot in (True, False):
+        x = g.standard_normal((N, S, K) if per_slot else (N, K)).astype(np.float32)
+        got = oracle.tolerance_scale_id(x, ids, experts)
+        assert got.shape == (N, S, M)
+        for t in range(N):
+            for s in range(S):
+                e = int(ids[t, s])
+                if not 0 <= e < E:
+                    assert np.all(np.isnan(got[t, s]))
+                    continue
+                xs = x[t, s] if per_slot else x[t]
+                for r in range(M):
+                    exact = sum(abs(Fraction(float(xs[k])) * Fraction(float(experts[e][r, k]))) for k in range(K))
+                    assert abs(Fraction(float(got[t, s, r])) - exact) <= Fraction(1e-14) * exact
+                    # and it bounds the product itself
+                    prod = sum(Fraction(float(xs[k])) * Fraction(float(experts[e][r, k])) for k in range(K))
+                    assert abs(prod) <= exact
+                    assert abs(prod) < exact  # both signs occur, so the bound is strict
