@@ -43,18 +43,68 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev_ptr(t, name):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
-
-
 def _xt(x):
     if x.dtype not in _XT:
         raise ValueError("activations must be float32 or float16")
     return _XT[x.dtype]
+
+
+# --- argument checks ---------------------------------------------------------------------------
+# Every tensor is checked against the handle's shape before a pointer reaches the library: the
+# kernels trust N, S, M and K, so a mis-shaped tensor would be read or written past its end on
+# the device.  Shape and dtype are checked first, then device placement and layout.
+
+class _Meta:
+    __slots__ = ("qtype", "M", "K", "n_experts", "device")
+
+    def __init__(self, qtype, M, K, n_experts, device):
+        self.qtype, self.M, self.K, self.n_experts, self.device = qtype, M, K, n_experts, device
+
+
+# handle value -> _Meta of the matrix it describes (filled by qmm_create)
+_HANDLES = {}
+
+
+def _meta(h):
+    key = h.value if isinstance(h, ctypes.c_void_p) else int(h or 0)
+    m = _HANDLES.get(key)
+    if m is None:
+        raise ValueError("unknown handle: create it with qmm_create (or QMatrix)")
+    return m
+
+
+def _need(device, *specs):
+    """specs: (tensor, name, shape or None, dtypes or None).  All shapes and dtypes are
+    checked before any placement, then each tensor must be a contiguous tensor on
+    `device` (the matrix's device; None: any device).  Returns their pointers."""
+    for t, name, shape, dtypes in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}; expected one of {[str(d) for d in dtypes]}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    ptrs = []
+    for t, name, _, _ in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if device is not None and t.device.index != device:
+            raise ValueError(f"{name} is on cuda:{t.device.index}; the matrix is on cuda:{device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        ptrs.append(ctypes.c_void_p(t.data_ptr()))
+    return ptrs if len(ptrs) > 1 else ptrs[0]
+
+
+_ACT = (torch.float32, torch.float16)
+_F32 = (torch.float32,)
+
+
+def _count(v, name, lo, hi=None):
+    v = int(v)
+    if v < lo or (hi is not None and v > hi):
+        raise ValueError(f"{name}={v} outside [{lo}, {hi if hi is not None else 'inf'})")
+    return v
 
 
 # --- functions with the C names --------------------------------------------------------------
@@ -76,8 +126,14 @@ def qmm_block_bytes(qtype) -> int:
 
 
 def qmm_quantize(qtype, w: torch.Tensor, M: int, K: int, blocks: torch.Tensor, stream=None) -> None:
-    check(lib.qmm_quantize(_type_id(qtype), _dev_ptr(w, "w"), int(M), int(K), _dev_ptr(blocks, "blocks"),
-                           _stream(stream)))
+    M, K = _count(M, "M", 0), _count(K, "K", 1)
+    rb = qmm_row_bytes(qtype, K)
+    if rb == 0:
+        raise ValueError(f"K={K} is not a positive multiple of the {qtype!r} block")
+    wp, bp = _need(None, (w, "w", (M, K), _F32), (blocks, "blocks", (M * rb,), (torch.uint8,)))
+    if w.device != blocks.device:
+        raise ValueError("w and blocks must be on the same device")
+    check(lib.qmm_quantize(_type_id(qtype), wp, M, K, bp, _stream(stream)))
 
 
 def quantize(w: torch.Tensor, qtype) -> torch.Tensor:
@@ -94,23 +150,37 @@ def quantize(w: torch.Tensor, qtype) -> torch.Tensor:
 
 
 def qmm_create(blocks: torch.Tensor, qtype, M: int, K: int, n_experts: int = 1) -> ctypes.c_void_p:
+    t = _type_id(qtype)
+    M, K, E = _count(M, "M", 1), _count(K, "K", 1), _count(n_experts, "n_experts", 1)
+    rb = lib.qmm_row_bytes(t, K)
+    if rb == 0:
+        raise ValueError(f"K={K} is not a positive multiple of the {qtype!r} block")
+    bp = _need(None, (blocks, "blocks", (E * M * rb,), (torch.uint8,)))
     h = ctypes.c_void_p()
-    check(lib.qmm_create(ctypes.byref(h), _type_id(qtype), _dev_ptr(blocks, "blocks"),
-                         int(n_experts), int(M), int(K)))
+    check(lib.qmm_create(ctypes.byref(h), t, bp, E, M, K))
+    _HANDLES[h.value] = _Meta(t, M, K, E, blocks.device.index)
     return h
 
 
 def qmm_destroy(h) -> None:
+    key = h.value if isinstance(h, ctypes.c_void_p) else h
+    _HANDLES.pop(key, None)
     check(lib.qmm_destroy(h))
 
 
 def qmm_gemv(h, x: torch.Tensor, N: int, y: torch.Tensor, stream=None) -> None:
-    check(lib.qmm_gemv(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), _stream(stream)))
+    m = _meta(h)
+    N = _count(N, "N", 0)
+    xp, yp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32))
+    check(lib.qmm_gemv(h, xp, _xt(x), N, yp, _stream(stream)))
 
 
 def qmm_gemm(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, stream=None) -> None:
+    m = _meta(h)
+    N = _count(N, "N", 0)
     t = TILES[tile] if tile in TILES else int(tile)
-    check(lib.qmm_gemm(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), t, _stream(stream)))
+    xp, yp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32))
+    check(lib.qmm_gemm(h, xp, _xt(x), N, yp, t, _stream(stream)))
 
 
 def qmm_gemm_workspace_bytes(h, N: int) -> int:
@@ -118,32 +188,47 @@ def qmm_gemm_workspace_bytes(h, N: int) -> int:
 
 
 def qmm_gemm_ws(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, ws: torch.Tensor = None, stream=None) -> None:
+    m = _meta(h)
+    N = _count(N, "N", 0)
     t = TILES[tile] if tile in TILES else int(tile)
     if ws is None:
+        xp, yp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32))
         wp, wb = ctypes.c_void_p(0), 0
     else:
-        wp, wb = _dev_ptr(ws, "ws"), ws.numel() * ws.element_size()
-    check(lib.qmm_gemm_ws(h, _dev_ptr(x, "x"), _xt(x), int(N), _dev_ptr(y, "y"), t, wp, wb, _stream(stream)))
+        xp, yp, wp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32), (ws, "ws", None, None))
+        wb = ws.numel() * ws.element_size()
+    check(lib.qmm_gemm_ws(h, xp, _xt(x), N, yp, t, wp, wb, _stream(stream)))
+
+
+def _id_args(m, x, N, S, x_per_slot, ids, y):
+    N, S = _count(N, "N", 0), _count(S, "S", 1)
+    if x_per_slot not in (0, 1):
+        raise ValueError("x_per_slot must be 0 or 1")
+    xp, ip, yp = _need(m.device, (x, "x", (N, S, m.K) if x_per_slot else (N, m.K), _ACT),
+                       (ids, "ids", (N, S), (torch.int32,)), (y, "y", (N, S, m.M), _F32))
+    return N, S, xp, ip, yp
 
 
 def qmm_gemm_id_tiled(h, x: torch.Tensor, N: int, S: int, x_per_slot: int, ids: torch.Tensor, y: torch.Tensor,
                       tile=0, stream=None) -> None:
+    m = _meta(h)
     t = TILES[tile] if tile in TILES else int(tile)
-    check(lib.qmm_gemm_id_tiled(h, _dev_ptr(x, "x"), _xt(x), int(N), int(S), int(x_per_slot),
-                                _dev_ptr(ids, "ids"), _dev_ptr(y, "y"), t, _stream(stream)))
+    N, S, xp, ip, yp = _id_args(m, x, N, S, x_per_slot, ids, y)
+    check(lib.qmm_gemm_id_tiled(h, xp, _xt(x), N, S, int(x_per_slot), ip, yp, t, _stream(stream)))
 
 
 def qmm_gemm_id(h, x: torch.Tensor, N: int, S: int, x_per_slot: int, ids: torch.Tensor, y: torch.Tensor,
                 stream=None) -> None:
-    check(lib.qmm_gemm_id(h, _dev_ptr(x, "x"), _xt(x), int(N), int(S), int(x_per_slot),
-                          _dev_ptr(ids, "ids"), _dev_ptr(y, "y"), _stream(stream)))
+    m = _meta(h)
+    N, S, xp, ip, yp = _id_args(m, x, N, S, x_per_slot, ids, y)
+    check(lib.qmm_gemm_id(h, xp, _xt(x), N, S, int(x_per_slot), ip, yp, _stream(stream)))
 
 
 def qmm_dequantize(h, expert: int, out: torch.Tensor, stream=None) -> None:
-    ot = _XT.get(out.dtype)
-    if ot is None:
-        raise ValueError("out must be float32 or float16")
-    check(lib.qmm_dequantize(h, int(expert), _dev_ptr(out, "out"), ot, _stream(stream)))
+    m = _meta(h)
+    expert = _count(expert, "expert", 0, m.n_experts - 1)
+    op = _need(m.device, (out, "out", (m.M, m.K), _ACT))
+    check(lib.qmm_dequantize(h, expert, op, _XT[out.dtype], _stream(stream)))
 
 
 # --- convenience object -------------------------------------------------------------------------
@@ -169,7 +254,7 @@ class QMatrix:
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value is not None:
-            lib.qmm_destroy(self._h)
+            qmm_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -182,24 +267,33 @@ class QMatrix:
     def handle(self):
         return self._h
 
-    def _check_x(self, x, rows_shape):
+    def _rows(self, x, dims):
+        """Leading dimensions of x ([N, K] when dims == 2); x must end in K."""
+        if not isinstance(x, torch.Tensor) or x.dim() not in dims:
+            raise ValueError(f"x must be a tensor of {' or '.join(str(d) for d in dims)} dimensions")
         if x.shape[-1] != self.K:
             raise ValueError(f"x has K={x.shape[-1]}, matrix has K={self.K}")
-        if x.device.type != "cuda":
-            raise ValueError("x must be a device tensor")
+        return tuple(x.shape[:-1])
+
+    def _ids(self, x, ids):
+        if not isinstance(ids, torch.Tensor) or ids.dtype != torch.int32 or ids.dim() != 2:
+            raise ValueError("ids must be an int32 [N, S] tensor")
+        N, S = ids.shape
+        lead = self._rows(x, (2, 3))
+        if lead != ((N, S) if x.dim() == 3 else (N,)):
+            raise ValueError(f"x has leading shape {lead}; ids [N, S] = {(N, S)} needs [N, S, K] or [N, K]")
+        return N, S, 1 if x.dim() == 3 else 0
 
     def gemv(self, x: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
         """x [N, K] (N <= 32) -> y [N, M] fp32."""
-        self._check_x(x, 2)
-        N = x.shape[0]
+        (N,) = self._rows(x, (2,))
         y = out if out is not None else torch.empty((N, self.M), dtype=torch.float32, device=x.device)
         qmm_gemv(self._h, x, N, y)
         return y
 
     def gemm(self, x: torch.Tensor, tile="auto", out: torch.Tensor = None) -> torch.Tensor:
         """x [N, K] -> y [N, M] fp32 through the fp16 matrix-core path; tile "auto", 32 or 64."""
-        self._check_x(x, 2)
-        N = x.shape[0]
+        (N,) = self._rows(x, (2,))
         y = out if out is not None else torch.empty((N, self.M), dtype=torch.float32, device=x.device)
         nb = qmm_gemm_workspace_bytes(self._h, N)
         ws = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=x.device) if nb else None
@@ -208,11 +302,7 @@ class QMatrix:
 
     def gemm_id(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
         """ids [N, S] int32; x [N, S, K] (one row per slot) or [N, K] -> y [N, S, M] fp32."""
-        if ids.dtype != torch.int32 or ids.dim() != 2:
-            raise ValueError("ids must be an int32 [N, S] tensor")
-        self._check_x(x, 3)
-        N, S = ids.shape
-        x_per_slot = 1 if x.dim() == 3 else 0
+        N, S, x_per_slot = self._ids(x, ids)
         y = out if out is not None else torch.empty((N, S, self.M), dtype=torch.float32, device=x.device)
         qmm_gemm_id(self._h, x, N, S, x_per_slot, ids, y)
         return y
@@ -220,11 +310,7 @@ class QMatrix:
     def gemm_id_tiled(self, x: torch.Tensor, ids: torch.Tensor, tile="auto", out: torch.Tensor = None) -> torch.Tensor:
         """Prefill-sized expert-indexed product on the matrix cores (any N): ids [N, S]
         int32; x [N, S, K] or [N, K] -> y [N, S, M] fp32; tile "auto", 32 or 64."""
-        if ids.dtype != torch.int32 or ids.dim() != 2:
-            raise ValueError("ids must be an int32 [N, S] tensor")
-        self._check_x(x, 3)
-        N, S = ids.shape
-        x_per_slot = 1 if x.dim() == 3 else 0
+        N, S, x_per_slot = self._ids(x, ids)
         y = out if out is not None else torch.empty((N, S, self.M), dtype=torch.float32, device=x.device)
         qmm_gemm_id_tiled(self._h, x, N, S, x_per_slot, ids, y, tile)
         return y

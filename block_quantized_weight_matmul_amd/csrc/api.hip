@@ -136,6 +136,7 @@ qmm_status qmm_create(qmm_matrix** out, qmm_type type, const void* blocks, int64
   h->d.M = M;
   h->d.K = K;
   h->d.row_bytes = rb;
+  h->d.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->device = dev;
   *out = h;
   return ok();

@@ -954,7 +954,6 @@ int id_resident_per_cu(int fmt, int TT, bool xf16, GemmKernel k) {
   return n;
 }
 
-constexpr int64_t kCUs = 256;
 }  // namespace
 
 // K splits for N tokens: few tokens leave too few (row, token) tiles to fill the
@@ -979,6 +978,7 @@ struct WidePlan {
 };
 
 WidePlan wide_plan(const MatDesc& m, int64_t N, bool xf16) {
+  const int64_t cus = m.cus;
   const int nst = static_cast<int>((m.K / 32 + 1) / 2);
   const bool q6 = m.fmt == FMT_Q6_K;
   WidePlan best{1, nst, 1, 64};
@@ -994,7 +994,7 @@ WidePlan wide_plan(const MatDesc& m, int64_t N, bool xf16) {
       const int per = (nst + S - 1) / S;
       if (S > 1 && per < 8) break;
       const int splits = (nst + per - 1) / per;
-      const int64_t rounds = (wgs * splits + kCUs - 1) / kCUs;
+      const int64_t rounds = (wgs * splits + cus - 1) / cus;
       double cost = static_cast<double>(rounds) * per * stage_us;
       if (splits > 1) cost += 4.0 + static_cast<double>(N) * static_cast<double>(m.M) * 4.0 * (splits + 1) / 4e6;
       if (cost < best_cost) {
@@ -1010,6 +1010,7 @@ WidePlan wide_plan(const MatDesc& m, int64_t N, bool xf16) {
 
 namespace {
 GemmSplit split_for(const MatDesc& m, int64_t N, bool xf16) {
+  const int64_t cus = m.cus;
   GemmSplit sp{1, static_cast<int>((m.K / 32 + 1) / 2)};
   if (N > 64) {
     const WidePlan p = wide_plan(m, N, xf16);
@@ -1020,7 +1021,7 @@ GemmSplit split_for(const MatDesc& m, int64_t N, bool xf16) {
   // sweep of 1..16 splits on the decode-layer shapes at 7, 33 and 64 tokens
   // came within 2% of its best per projection with this count)
   const int64_t base = ((m.M + 63) / 64) * ((N + 63) / 64);
-  const int64_t want = m.fmt == FMT_Q6_K ? kCUs / 2 : kCUs;
+  const int64_t want = m.fmt == FMT_Q6_K ? cus / 2 : cus;
   if (N <= 0 || base >= want) return sp;
   const int64_t nst = sp.stages;
   int64_t S = (want + base - 1) / base;
@@ -1047,6 +1048,7 @@ size_t gemm_workspace_bytes(const MatDesc& m, int64_t N) {
 
 hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N, int64_t S, int x_per_slot,
                           const int32_t* ids, float* y, int tile, hipStream_t st) {
+  const int64_t cus = m.cus;
   GemmArgs a{};
   a.W = m.blocks;
   a.row_bytes = static_cast<u32>(m.row_bytes);
@@ -1089,7 +1091,7 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
   const int64_t row_tiles = (m.M + 64 * RB - 1) / (64 * RB);
   if (ranks > 65535 || row_tiles > INT_MAX) return hipErrorInvalidValue;
   const int64_t per_cu = id_resident_per_cu(m.fmt, TT, xf16, k);
-  int64_t groups = (per_cu * kCUs + ranks - 1) / ranks;
+  int64_t groups = (per_cu * cus + ranks - 1) / ranks;
   if (groups > row_tiles) groups = row_tiles;
   const int64_t ranks8 = (ranks + 7) / 8 * 8;
   a.id_groups = static_cast<int>(groups);
@@ -1100,6 +1102,7 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
 
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t st) {
+  const int64_t cus = m.cus;
   const GemmSplit sp = ws ? split_for(m, N, x_f16 != 0) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
   GemmArgs a{};
   a.W = m.blocks;
@@ -1123,7 +1126,7 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
   const int64_t padded = (N + tile - 1) / tile * tile;
   auto wgs = [&](int rb, int tt) { return ((m.M + 64 * rb - 1) / (64 * rb)) * ((padded + tt - 1) / tt); };
   static const int kShapes[3][2] = {{2, 128}, {1, 128}, {1, 64}};
-  const int64_t want = m.fmt == FMT_Q6_K ? kCUs / 2 : 2 * kCUs;
+  const int64_t want = m.fmt == FMT_Q6_K ? cus / 2 : 2 * cus;
   const bool xf16 = x_f16 != 0;
   // split calls take 64 rows x the planned super-tile above 64 tokens, else x 64,
   // or x 32 when the call pads to 32: activations of absent tokens are not

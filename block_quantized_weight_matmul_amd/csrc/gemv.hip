@@ -1205,7 +1205,6 @@ const Tables& tables() {
   return t;
 }
 
-constexpr int kCUs = 256;
 constexpr int kLdsBudget = 64 * 1024;  // bytes of dynamic LDS per workgroup
 
 struct Shape {
@@ -1244,6 +1243,7 @@ Shape make_shape(int M, int nU, int runs, int NB, int RW, int max_threads = 512)
 constexpr int kRuns[5] = {1, 1, 2, 2, 2};
 
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t st) {
+  const int cus = m.cus;
   const int bi = bucket_index(N);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
@@ -1259,7 +1259,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     // covers M / 256 rows.  Shapes whose activation image and partials do not
     // fit the LDS budget take the general path below.
     const int Gmax = 512 / ipr;
-    const int want = (M + kCUs - 1) / kCUs;
+    const int want = (M + cus - 1) / cus;
     const int xh = x_f16 ? 1 : 0;
     auto two_fit = [&](int r, int ri) {
       const int G2 = (want + 2 * r - 1) / (2 * r);
@@ -1310,7 +1310,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     const int Gmax = 512 / ipr2;
     if (Gmax >= 1) {
       const int per_cu = N > 8 ? 2 : 1;
-      const int want = (M + kCUs * per_cu - 1) / (kCUs * per_cu);
+      const int want = (M + cus * per_cu - 1) / (cus * per_cu);
       const int R = 1;
       int Ge = (want + R - 1) / R;
       if (Ge > Gmax) Ge = Gmax;
@@ -1347,7 +1347,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     }
   }
   // about one workgroup per CU
-  const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + kCUs - 1) / kCUs);
+  const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + cus - 1) / cus);
   GemvArgs a{};
   a.W = m.blocks;
   a.row_bytes = m.row_bytes;
@@ -1367,6 +1367,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
 
 hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
                           const int32_t* ids, float* y, hipStream_t st) {
+  const int cus = m.cus;
   // pairs per expert: at most N when a token's ids are distinct, and about
   // N * S / E in a routed batch; a workgroup takes them NB <= 4 at a time
   const int bi = bucket_index(N < 4 ? N : 4);
@@ -1383,7 +1384,7 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
     // step), at least 128 rows so that the routing stays a small part of it.
     // Measured on 128 experts of 4096 rows at 2, 8 and 24 tokens (slices of
     // 128-1024 rows, rings of 4-16 items).
-    const int slices = (4 * kCUs + ranks - 1) / ranks;
+    const int slices = (4 * cus + ranks - 1) / ranks;
     int RW = (M + slices - 1) / slices;
     RW = (RW + 15) / 16 * 16;
     if (RW < 128) RW = 128;
@@ -1414,7 +1415,7 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
     const int Rk = kRuns[m.fmt] == 1 ? 4 : 2;
     const int Gmax = 512 / ipr;
     if (Gmax >= 1) {
-      const int slices_want = (2 * kCUs + ranks - 1) / ranks;
+      const int slices_want = (2 * cus + ranks - 1) / ranks;
       const int rows_want = (M + slices_want - 1) / slices_want;
       int Ge = (rows_want + Rk - 1) / Rk;
       if (Ge > Gmax) Ge = Gmax;
@@ -1457,7 +1458,7 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
       }
     }
   }
-  const int slices = (2 * kCUs + ranks - 1) / ranks;
+  const int slices = (2 * cus + ranks - 1) / ranks;
   // (256 threads: each workgroup streams a short slice, and two share a CU)
   const Shape s = make_shape(M, nU, kRuns[m.fmt], kBuckets[bi], (M + slices - 1) / slices, 256);
   GemvArgs a{};

@@ -11,6 +11,7 @@ struct MatDesc {
   int fmt;                // FMT_*
   int64_t n_experts, M, K;
   uint64_t row_bytes;
+  int cus;                // compute units of the device (launch shapes are sized to fill them)
 };
 
 // Largest expert count the expert-indexed path accepts (its presence bitmap

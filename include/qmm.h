@@ -94,7 +94,14 @@ typedef int qmm_status;
 typedef struct qmm_matrix qmm_matrix;
 
 /*
- * qmm_create -- describe a quantized weight tensor.
+ * qmm_create -- describe a quantized weight tensor: the block buffer, its format
+ * and its shape, the operand every page's kernel reads (candle pull request,
+ * section "Why the tile sets the weight reuse": a weight tile read from the
+ * quantized blocks; llama.cpp pull request, section "Overview": rows of
+ * 32-weight chunks; tiny-llm pull request, section "Benchmark setup": 4-bit
+ * groups with a scale and a bias).  For the expert-indexed path the tensor is
+ * the experts' matrices stacked (llama.cpp pull request, section "Additional
+ * information": MUL_MAT_ID picks one expert's matrix per token and slot).
  *   out        receives the handle (host memory owned by the library; free it with
  *              qmm_destroy).
  *   type       block format.
@@ -110,7 +117,8 @@ typedef struct qmm_matrix qmm_matrix;
 qmm_status qmm_create(qmm_matrix **out, qmm_type type, const void *blocks,
                       int64_t n_experts, int64_t M, int64_t K);
 
-/* qmm_destroy -- free a handle's host metadata.  NULL is accepted. */
+/* qmm_destroy -- free a handle's host metadata (the blocks stay the caller's; see
+ * qmm_create).  NULL is accepted.  Returns QMM_OK. */
 qmm_status qmm_destroy(qmm_matrix *h);
 
 /*
@@ -208,9 +216,21 @@ qmm_status qmm_gemm_id_tiled(const qmm_matrix *h, const void *x, qmm_dtype xt, i
                              qmm_tile tile, qmm_stream_t stream);
 
 /*
- * qmm_dequantize -- decode one expert's matrix (expert 0 for a plain matrix).
- *   out  DEVICE [M, K] of type ot, 16-byte aligned.  QMM_F32: the exact dequantized
- *        weights.  QMM_F16: the fp16 values the matrix-matrix path stages in LDS.
+ * qmm_dequantize -- decode one expert's matrix (expert 0 for a plain matrix): the
+ * per-block decode step of every path, written out.  The candle pull request
+ * (section "Why the tile sets the weight reuse") decodes each weight tile once
+ * into threadgroup memory before the matrix product; QMM_F16 returns exactly those
+ * staged values, QMM_F32 the exact dequantized weights the matrix-vector paths
+ * multiply by (llama.cpp pull request, section "Additional information", checks
+ * both paths against a CPU backend working from the same weights).
+ *   expert  0 .. n_experts - 1 (QMM_E_SHAPE otherwise).
+ *   out     DEVICE [M, K] of type ot, 16-byte aligned, every element written.
+ *           QMM_F32: the exact dequantized weights (the fp32 round-to-nearest-even
+ *           of each formula above).  QMM_F16: round-to-nearest-even of those fp32
+ *           values, as the matrix-matrix path stages them (an fp16 overflow gives
+ *           an infinity).
+ * Errors: QMM_E_ARG (NULL handle or out), QMM_E_TYPE (ot), QMM_E_ALIGN, QMM_E_DEVICE
+ * (not the handle's device), QMM_E_HIP (launch).
  */
 qmm_status qmm_dequantize(const qmm_matrix *h, int64_t expert, void *out, qmm_dtype ot,
                           qmm_stream_t stream);

@@ -13,11 +13,13 @@ matrix-matrix kernel" (section "Same results, bit for bit") requires every
 output to be equal bit for bit at the 32- and 64-token tiles, on 7, 32, 33 and
 130 tokens and a batch of 2 x 65, with a guard that the result is not all zero."""
 
+import ctypes
 import numpy as np
 import pytest
 import torch
 
 import block_quantized_weight_matmul_amd as q
+from block_quantized_weight_matmul_amd import _lib as L
 from tests.gpu_helpers import FORMATS, assert_within, count_differences, make_matrix, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -112,7 +114,8 @@ def test_gemm_deterministic_and_zero_tokens():
     a, b = to_host(qm.gemm(xd, 64)), to_host(qm.gemm(xd, 64))
     assert count_differences(a, b) == 0
     y = torch.full((1, M), 3.0, device="cuda")
-    q.qmm_gemm(qm.handle, xd, 0, y, 0)
+    # N = 0 through the C ABI itself (the binding wants x [0, K], which holds no pointer)
+    assert L.lib.qmm_gemm(qm.handle, ctypes.c_void_p(xd.data_ptr()), 1, 0, ctypes.c_void_p(y.data_ptr()), 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
     assert np.all(to_host(y) == 3.0)
 
 

@@ -3,11 +3,13 @@ request "metal : fix idle threads in mul_mv_iq3_xxs for ne00 < 1024") against
 the oracle: tolerance 1e-5 * S, exact equality with the dense path when every
 slot picks one expert, NaN rows for ids outside [0, E)."""
 
+import ctypes
 import numpy as np
 import pytest
 import torch
 
 import block_quantized_weight_matmul_amd as q
+from block_quantized_weight_matmul_amd import _lib as L
 from tests.gpu_helpers import FORMATS, assert_within, count_differences, make_matrix, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -110,7 +112,7 @@ def test_gemm_id_zero_tokens_is_noop():
     ids = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
     x = torch.zeros((1, 1, K), device="cuda")
     y = torch.full((1, 1, M), 5.0, device="cuda")
-    q.qmm_gemm_id(qm.handle, x, 0, 1, 1, ids, y)
+    assert L.lib.qmm_gemm_id(qm.handle, ctypes.c_void_p(x.data_ptr()), 0, 0, 1, 1, ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
     assert np.all(to_host(y) == 5.0)
 
 

@@ -120,7 +120,7 @@ def test_gemm_id_tiled_zero_tokens_and_errors():
     ids = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
     x = torch.zeros((1, 1, K), device="cuda")
     y = torch.full((1, 1, M), 5.0, device="cuda")
-    q.qmm_gemm_id_tiled(qm.handle, x, 0, 1, 1, ids, y)
+    assert L.lib.qmm_gemm_id_tiled(qm.handle, ctypes.c_void_p(x.data_ptr()), 0, 0, 1, 1, ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(y.data_ptr()), 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
     assert np.all(to_host(y) == 5.0)
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     xp, yp, ip = (ctypes.c_void_p(t.data_ptr()) for t in (x, y, ids))

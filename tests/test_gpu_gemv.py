@@ -6,11 +6,13 @@ then add up over at most K/32 chunks and a log2(64)-step butterfly, so the
 worst-case bound is (32 + K/32/lanes + 6) * 2^-24 * S, below 1e-5 * S for every
 K here).  One-hot activations must reproduce the dequantized weights exactly."""
 
+import ctypes
 import numpy as np
 import pytest
 import torch
 
 import block_quantized_weight_matmul_amd as q
+from block_quantized_weight_matmul_amd import _lib as L
 from tests.gpu_helpers import FORMATS, assert_within, make_matrix, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -83,7 +85,7 @@ def test_gemv_zero_tokens_is_noop():
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [45])), fmt, M, K)
     x = torch.zeros((1, K), device="cuda")
     y = torch.full((1, M), 7.0, device="cuda")
-    q.qmm_gemv(qm.handle, x, 0, y)
+    assert L.lib.qmm_gemv(qm.handle, ctypes.c_void_p(x.data_ptr()), 0, 0, ctypes.c_void_p(y.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
     assert np.all(to_host(y) == 7.0)
 
 
