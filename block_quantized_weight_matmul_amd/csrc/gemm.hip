@@ -111,20 +111,33 @@ __device__ __forceinline__ half8 weights_pk(u32 c0, u32 c1, half2v off, half2v d
 // 8 weights from code bytes, fp32-coefficient path, codes as fp16 subnormals:
 // w = fp16(fma(code * 2^-24, a24, b)) with a24 = a * 2^24 (exact), so the fma
 // forms the same exact code * a + b, rounded once to fp32 then to fp16, as
-// fma(code, a, b) -- with no subtraction of an offset per pair.
+// fma(code, a, b) -- with no subtraction of an offset per pair.  The fp32 weight
+// is held opaque before its conversion: the compiler would otherwise fuse the
+// fma and the conversion into one v_fma_mix with an fp16 result, which rounds
+// the exact code * a + b once, to fp16, and differs from the fp16 rounding of
+// the fp32 weight where that weight is an fp16 tie (measured: a Q4_K weight of
+// exact value 2 + 2^-10 + 2^-24 staged as 2 + 2^-9 instead of 2).  The pairs are
+// converted by v_cvt_pk_f16_f32 (nearest even).
+typedef float float2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half8 weights_sub(u32 c0, u32 c1, float a24, float b) {
   const half2v p[4] = {code_pair_lo_sub(c0), code_pair_hi_sub(c0), code_pair_lo_sub(c1), code_pair_hi_sub(c1)};
   half8 h;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    h[2 * i] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(p[i][0]), a24, b));
-    h[2 * i + 1] = static_cast<_Float16>(__builtin_fmaf(static_cast<float>(p[i][1]), a24, b));
+    float f0 = __builtin_fmaf(static_cast<float>(p[i][0]), a24, b);
+    float f1 = __builtin_fmaf(static_cast<float>(p[i][1]), a24, b);
+    asm("" : "+v"(f0), "+v"(f1));
+    const half2v r = __builtin_convertvector(float2v{f0, f1}, half2v);
+    h[2 * i] = r[0];
+    h[2 * i + 1] = r[1];
   }
   return h;
 }
 
 // 8 weights, fp32-coefficient path: w = fp16(fma(code - off, a, b)); off is
-// subtracted exactly in fp16 (or 0 when b already absorbs it).
+// subtracted exactly in fp16 (or 0 when b already absorbs it).  Used where the
+// weight is exact in fp32 (Q6_K: (q - 32) * a), so the one rounding of a fused
+// fma-to-fp16 is the fp16 rounding of the fp32 weight.
 template <bool SUB>
 __device__ __forceinline__ half8 weights_mix(u32 c0, u32 c1, half2v off, float a, float b) {
   half2v p[4] = {code_pair_lo(c0), code_pair_hi(c0), code_pair_lo(c1), code_pair_hi(c1)};

@@ -11,7 +11,7 @@ FORMATS = ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64"]
 
 
 def to_dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return torch.from_numpy(np.array(a, order="C")).to(DEV)
 
 
 def to_host(t):

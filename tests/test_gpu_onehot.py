@@ -129,6 +129,17 @@ def test_gemm_one_hot(fmt, xdt):
             same_values(to_host(qm.gemm(to_dev(one_hot(ks, K, xdt)), tile)), want[ks], f"{fmt} gemm N=7 tile {tile}")
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_dequantize_pool(fmt):
+    # the decode-only kernel on the same blocks: fp32 bits and the fp16 staging values
+    K = K_of(fmt)
+    blob = matrix(fmt)
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    same_values(to_host(qm.dequantize(0, torch.float32)), w, f"{fmt} dequantize fp32")
+    same_values(to_host(qm.dequantize(0, torch.float16)), staged(w), f"{fmt} dequantize fp16")
+
+
 def stack(fmt):
     blobs = [matrix(fmt, 13 * e) for e in range(E)]
     K = K_of(fmt)
