@@ -2,6 +2,9 @@
 """Benchmark of the fused dequantize-and-multiply on one MI355X.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-extras] [--no-cpu-baseline]
+    python bench.py --calibrate                       # launch and streaming-read calibration
+    python bench.py --summarize-trace DIR             # rocprofv3 kernel-trace summary (markdown)
+    python bench.py --summarize-counters F W CF CW    # rocprofv3 FETCH/WRITE summary (markdown)
 
 Headline (one JSON line on stdout): quantized-weight GB/s of the matrix-vector
 path at one token on the seven projections of a Qwen3-Embedding-4B decoder
@@ -14,18 +17,24 @@ graphs captured from the library's launches (the graph only removes host
 launch overhead; the kernels are the ones an eager call runs).
 
 Also reported:
-  roofline      the dominant kernel (the GEMV instance with the most time per
-                step): algorithmic bytes per launch / its mean launch time, from
-                HIP events around a graph of back-to-back launches of each
-                projection, against 8 TB/s; "traffic" from the rocprofv3 counter
-                summary in profiles/ when it was taken on the current kernel
-                source, else null.
+  roofline      the step's kernel: all seven launches are the one-token GEMV
+                kernel (k_gemv1, a Q4_K and a Q6_K instance), run back to back,
+                so its average launch duration is the HIP-event-timed step over
+                seven launches, and its algorithmic bytes per launch the layer's
+                weights + x + y over seven; against 8 TB/s.  "traffic" from the
+                rocprofv3 counter summary in profiles/ when it was taken on the
+                current kernel source, else null.
   cpu_baseline  the CPU oracle (NumPy dequantization + fp64 matmul) on a bounded
-                sample of the same workload, in the same unit.
-  extras        the other workloads: the single Q4_0 256x512 matvec, 4-bit
-                affine-group decode at 1..16 tokens, the prefill GEMM at
-                7..2048 tokens with both token tiles, and the expert-indexed
-                matvec at 2..24 tokens with ids re-drawn per call.
+                sample of the same workload, in the same unit; per-config
+                oracle timings (median of 3) in extras.oracle_per_config.
+  extras        the other workloads, each timed over more than 1 GiB of
+                distinct weight copies per sample: the single Q4_0 256x512
+                matvec, 4-bit affine-group decode at 1..16 tokens (with its fp32
+                VALU ceiling fraction), the prefill GEMM at 7..2048 tokens with
+                both token tiles, the batch of 2 x 65 tokens on 128 x 768 in all
+                five formats, the expert-indexed matvec at 2..24 tokens with ids
+                re-drawn per call and its matrix-core form at 64..1024 tokens,
+                and the GPU quantizer.
 """
 
 import argparse
@@ -44,6 +53,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix cores
+# fp32 vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (fma) x 2.4 GHz = 78.6 TFLOP/s for
+# one fma per lane per cycle; packed fp32 (two per lane) doubles it to 157.3, but this library
+# is built without packed fp32 instructions, so 78.6 is the ceiling its fmas can reach
+VALU_F32_FMA_TFLOPS = 78.6
+VALU_F32_PACKED_TFLOPS = 157.3
 ROTATE_BYTES = 1 << 30         # > 256 MB Infinity Cache
 METRIC = "quantized-weight GB/s at n<=16 and TFLOP/s at n>=64, as % of roofline"
 
@@ -55,10 +69,18 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--event-launches", type=int, default=64, help="launches per projection in the per-kernel pass")
+    p.add_argument("--event-launches", type=int, default=64,
+                   help="launches per projection in the isolated per-projection pass (0: skip it)")
     p.add_argument("--calls", type=int, default=20, help="calls per timed sample in the extras")
     p.add_argument("--rounds", type=int, default=6, help="timed samples per extra case (median)")
     p.add_argument("--copy-probe", action="store_true", help="only run a 256 MiB device copy (counter calibration)")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only time an empty kernel and plain streaming reads of the decode-layer projection sizes")
+    p.add_argument("--summarize-trace", default=None, metavar="DIR",
+                   help="print a markdown summary of a rocprofv3 kernel trace of this benchmark (no GPU needed)")
+    p.add_argument("--summarize-counters", nargs=4, default=None, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="print a markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this benchmark and "
+                        "of --copy-probe (no GPU needed)")
     p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
                    help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
     p.add_argument("--moe-only", default=None, metavar="N[,N...]",
@@ -181,58 +203,61 @@ def decode_layer(torch, q, W, args):
     ms_per_step = wall_s * 1e3 / args.steps
     value = layer_weight_bytes * args.steps / wall_s / 1e9
 
-    # per-kernel pass: for each projection, a graph of R back-to-back launches (rotating
-    # copies) timed with HIP events on the stream it is replayed on; mean per launch
+    # isolated per-projection pass: for each projection, a graph of R back-to-back launches
+    # of that projection alone (rotating copies), timed with HIP events; a launch that
+    # follows a launch of the same kernel overlaps it more than in the layer step, so
+    # these are context, not the roofline's launch time
     R = args.event_launches
     mean_us = np.zeros(P)
-    for j in range(P):
+    for j in range(P if R > 0 else 0):
         g = capture(torch, lambda j=j: [q.qmm_gemv(handles[r % rot.copies][j].handle, xs[j], 1, ys[j])
                                        for r in range(R)])
         mean_us[j] = time_graph(torch, g, 5) * 1e3 / R
         del g
-    # kernels are instantiated per block format (the token bucket is fixed at one token)
-    per_kernel = {}
-    for j, m in enumerate(mats):
-        k = per_kernel.setdefault(m["fmt"], {"launches": 0, "us": 0.0, "alg_bytes": 0, "weight_bytes": 0,
-                                             "projections": []})
-        k["launches"] += 1
-        k["us"] += float(mean_us[j])
-        k["alg_bytes"] += int(m["blob"].size) + 4 * m["K"] + 4 * m["M"]
-        k["weight_bytes"] += int(m["blob"].size)
-        k["projections"].append(m["name"])
-    dom_fmt = max(per_kernel, key=lambda f: per_kernel[f]["us"])
-    dk = per_kernel[dom_fmt]
-    avg_us = dk["us"] / dk["launches"]
-    alg_per_launch = dk["alg_bytes"] / dk["launches"]
-    achieved = alg_per_launch / (avg_us * 1e-6) / 1e9
     projections = [{"name": m["name"], "fmt": m["fmt"], "M": m["M"], "K": m["K"], "weight_bytes": int(m["blob"].size),
-                    "mean_us": round(float(mean_us[j]), 3),
-                    "weight_gbs": round(m["blob"].size / (mean_us[j] * 1e-6) / 1e9, 1)}
+                    "isolated_us": round(float(mean_us[j]), 3),
+                    "isolated_weight_gbs": round(m["blob"].size / (mean_us[j] * 1e-6) / 1e9, 1)}
                    for j, m in enumerate(mats)]
+    # the roofline's kernel: every launch of the step is k_gemv1 (Q4_K or Q6_K instance)
+    # and they run back to back, so the event-timed step over P launches is its average
+    # launch duration (the rocprofv3 trace in profiles/ checks this against per-dispatch
+    # durations)
+    step_us = ev_ms / args.steps * 1e3
+    avg_us = step_us / P
+    alg_per_launch = layer_alg_bytes / P
     out = {
         "value": value, "ms_per_step": ms_per_step, "event_ms_per_step": ev_ms / args.steps,
         "layer_weight_bytes": layer_weight_bytes, "layer_alg_bytes": layer_alg_bytes,
         "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
         "projections": projections,
-        "dominant": {"fmt": dom_fmt, "launches_per_step": dk["launches"], "avg_us": avg_us,
-                     "alg_bytes_per_launch": alg_per_launch, "achieved_gbs": achieved,
-                     "projections": dk["projections"]},
-        "sum_kernel_us": float(mean_us.sum()),
+        "kernel": {"launches_per_step": P, "avg_us": avg_us, "alg_bytes_per_launch": alg_per_launch,
+                   "achieved_gbs": alg_per_launch / (avg_us * 1e-6) / 1e9},
+        "sum_isolated_us": float(mean_us.sum()),
     }
     del handles, full, singles
     return out, mats
 
 
-def traffic_from_profile(fmt, digest):
-    """HBM bytes per launch from the committed counter summary, if it matches this source."""
-    path = os.path.join(ROOT, "profiles", f"gemv_{fmt}_decode_layer_counters.md")
-    if not os.path.exists(path):
-        return None, "no counter summary"
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_decode_layer_counters.md")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "gemv_decode_layer_kernel_trace.md")
+
+
+def _summary_values(path):
     vals = {}
-    for line in open(path):
-        if ":" in line and line.strip().startswith("- "):
-            k, _, v = line.strip()[2:].partition(":")
-            vals[k.strip()] = v.strip()
+    if os.path.exists(path):
+        for line in open(path):
+            if ":" in line and line.strip().startswith("- "):
+                k, _, v = line.strip()[2:].partition(":")
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def traffic_from_profile(digest):
+    """HBM bytes per launch of the step's kernel from the committed counter summary, if it
+    was taken on this kernel source."""
+    vals = _summary_values(COUNTER_SUMMARY)
+    if not vals:
+        return None, "no counter summary"
     if vals.get("source_digest") != digest:
         return None, "counters taken on another kernel source"
     try:
@@ -271,20 +296,79 @@ def cpu_baseline(mats):
                        f"takes >99% of the time")}
 
 
+def _median3(fn):
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def oracle_per_config(W, mats):
+    """The oracle (dequantization + fp64 products, as the parity tests run it) on one bounded
+    sample of each workload, median of 3 runs: its throughput in the workload's own unit."""
+    import oracle
+    out = []
+    d = W.single_matvec()
+    t = _median3(lambda: oracle.matmul_ref(d["x"], oracle.dequantize(d["fmt"], d["blob"], d["M"], d["K"])))
+    out.append({"config": "Q4_0 256x512 matvec, 1 token", "sample": "whole", "s": t,
+                "weight_gbs": d["blob"].size / t / 1e9})
+    for j in (1, 6):  # attn_k (Q4_K) and ffn_down (Q6_K)
+        m = mats[j]
+        x = W.decode_x(j, 1)
+        t = _median3(lambda: oracle.matmul_ref(x, oracle.dequantize(m["fmt"], m["blob"], m["M"], m["K"])))
+        out.append({"config": "decode layer, 1 fp32 token", "sample": m["name"], "s": t,
+                    "weight_gbs": m["blob"].size / t / 1e9})
+    sm = W.small_decode_weights(0)
+    x = W.small_decode_x(0, 16)
+    t = _median3(lambda: oracle.matmul_ref(x, oracle.dequantize("a4g64", sm["blob"], sm["M"], sm["K"])))
+    out.append({"config": "A4G64 layer, 16 fp16 tokens", "sample": sm["name"], "s": t,
+                "weight_gbs": sm["blob"].size / t / 1e9, "gflops": 2 * 16 * sm["M"] * sm["K"] / t / 1e9})
+    m = mats[1]
+    x = W.prefill_x(1, 512)
+    t = _median3(lambda: oracle.matmul_ref(x, oracle.dequantize(m["fmt"], m["blob"], m["M"], m["K"])))
+    out.append({"config": "prefill GEMM, 512 fp16 tokens", "sample": m["name"], "s": t,
+                "gflops": 2 * 512 * m["M"] * m["K"] / t / 1e9})
+    pb = W.prefill_batch(2)
+    t = _median3(lambda: oracle.matmul_ref(pb["x"], oracle.dequantize(pb["fmt"], pb["blob"], pb["M"], pb["K"])))
+    out.append({"config": "batch 2 x 65 tokens, 128 x 768", "sample": pb["fmt"], "s": t,
+                "gflops": 2 * 130 * pb["M"] * pb["K"] / t / 1e9})
+    ids = W.moe_ids(2, 0)
+    used = sorted(set(ids.reshape(-1).tolist()))
+    x = W.moe_x(2)
+    blobs = {e: W.moe_expert(e) for e in used}
+
+    def moe():
+        ws = [None] * W.MOE_EXPERTS
+        for e in used:
+            ws[e] = oracle.dequantize("q4_0", blobs[e], W.MOE_M, W.MOE_K)
+        zero = np.zeros((W.MOE_M, W.MOE_K), np.float32)
+        oracle.matmul_id_ref(x, ids, [w if w is not None else zero for w in ws])
+    t = _median3(moe)
+    out.append({"config": "expert-indexed matvec, 2 tokens x 8 slots", "sample": f"{len(used)} distinct experts",
+                "s": t, "weight_gbs": len(used) * blobs[used[0]].size / t / 1e9})
+    return {"kind": "oracle", "cores": 1, "note": "NumPy dequantization (single-threaded) dominates; fp64 "
+            "products through BLAS", "results": out}
+
+
 # ------------------------------------------------------------------------------------------------
 # extras
 
 def extra_single_matvec(torch, q, W, args):
     d = W.single_matvec()
-    rot = Rotation(torch, [d["blob"]], min_total=64 << 20)
+    rot = Rotation(torch, [d["blob"]])
     hs = [q.QMatrix(rot.slice(c, 0), d["fmt"], d["M"], d["K"]) for c in range(rot.copies)]
     x = torch.from_numpy(d["x"]).to("cuda")
     y = torch.empty((1, d["M"]), device="cuda")
-    g = capture(torch, lambda: [q.qmm_gemv(hs[i % rot.copies].handle, x, 1, y) for i in range(args.calls)])
-    us = time_graph(torch, g, args.rounds) * 1e3 / args.calls
-    return {"workload": "Q4_0 256x512, 1 fp32 token", "us_per_call": us,
+    # one sample = one call on every copy (> 1 GiB of distinct weights)
+    g = capture(torch, lambda: [q.qmm_gemv(h.handle, x, 1, y) for h in hs])
+    us = time_graph(torch, g, args.rounds) * 1e3 / len(hs)
+    del g
+    return {"workload": "Q4_0 256x512, 1 fp32 token", "us_per_call": us, "copies": rot.copies,
             "weight_gbs": d["blob"].size / (us * 1e-6) / 1e9,
-            "frac_hbm": d["blob"].size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            "frac_hbm": d["blob"].size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "a 73,728-byte matrix: the call is bound by the launch, not by its bytes"}
 
 
 def extra_small_decode(torch, q, W, args):
@@ -297,7 +381,7 @@ def extra_small_decode(torch, q, W, args):
     for n in W.SMALL_DECODE_TOKENS:
         xs = [torch.from_numpy(W.small_decode_x(j, n)).to("cuda") for j in range(len(mats))]
         ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
-        layers = min(args.calls, rot.copies)
+        layers = rot.copies  # one sample = one layer pass on every copy (> 1 GiB)
 
         def fn():
             for c in range(layers):
@@ -305,17 +389,25 @@ def extra_small_decode(torch, q, W, args):
                     q.qmm_gemv(hs[c][j].handle, xs[j], n, ys[j])
         g = capture(torch, fn)
         us = time_graph(torch, g, args.rounds) * 1e3 / layers
+        del g
         flops = 2 * n * sum(m["M"] * m["K"] for m in mats)
+        tflops = flops / (us * 1e-6) / 1e12
         res.append({"n": n, "us_per_layer": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
                     "frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                    "tflops": flops / (us * 1e-6) / 1e12})
+                    "tflops": tflops,
+                    "frac_valu_fma": tflops / VALU_F32_FMA_TFLOPS,
+                    "frac_valu_packed": tflops / VALU_F32_PACKED_TFLOPS,
+                    "binding": "hbm" if n <= 4 else "alu"})
     return {"workload": "Qwen3-0.6B layer, A4G64 (group 64), fp16 tokens", "layer_weight_bytes": wbytes,
-            "copies": rot.copies, "results": res}
+            "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
+            "valu_peaks_tflops": {"fma": VALU_F32_FMA_TFLOPS, "packed": VALU_F32_PACKED_TFLOPS},
+            "results": res}
 
 
 def extra_prefill(torch, q, W, mats, args):
-    # weight copies rotate over >1 GiB, as for the decode layer: at few tokens the
-    # path streams its weights, which must not come from a warm cache
+    # weight copies rotate over >1 GiB, as for the decode layer, and every sample
+    # passes over all of them: at few tokens the path streams its weights, which
+    # must not come from a warm cache
     rot = Rotation(torch, [m["blob"] for m in mats])
     hss = [[q.QMatrix(rot.slice(c, j), m["fmt"], m["M"], m["K"]) for j, m in enumerate(mats)]
            for c in range(rot.copies)]
@@ -326,12 +418,12 @@ def extra_prefill(torch, q, W, mats, args):
     for n in tokens:
         xs = [torch.from_numpy(W.prefill_x(j, n)).to("cuda") for j in range(len(mats))]
         ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
-        # the workspace of the K-split few-token calls (QMatrix.gemm's path)
+        # the workspace of the K-split calls (QMatrix.gemm's path)
         wss = []
         for j in range(len(mats)):
             nb = q.qmm_gemm_workspace_bytes(hss[0][j].handle, n)
             wss.append(torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None)
-        calls = max(1, min(args.calls, rot.copies, int(2e10 // (flops_tok * n)) or 1))
+        calls = rot.copies
         per_tile = {}
         for tile in (32, 64):
             g = capture(torch, lambda tile=tile: [q.qmm_gemm_ws(hss[c][j].handle, xs[j], n, ys[j], tile, wss[j])
@@ -349,10 +441,48 @@ def extra_prefill(torch, q, W, mats, args):
                     "us_tile32": us[32], "us_tile64": us[64], "ratio_64_over_32": us[64] / us[32],
                     "tflops": flops_tok * n / (us[chosen] * 1e-6) / 1e12,
                     "frac_mfma": flops_tok * n / (us[chosen] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-                    "weight_gbs": wbytes / (us[chosen] * 1e-6) / 1e9})
-        del per_tile
-    return {"workload": "decode-layer shapes as prefill GEMM, fp16 tokens, auto tile, weights rotated",
-            "copies": rot.copies, "results": res}
+                    "weight_gbs": wbytes / (us[chosen] * 1e-6) / 1e9,
+                    "frac_hbm": wbytes / (us[chosen] * 1e-6) / 1e9 / HBM_PEAK_GBS})
+        del per_tile, xs, ys, wss
+    return {"workload": "decode-layer shapes as prefill GEMM, fp16 tokens, auto tile, "
+                        "weights rotated over >1 GiB per sample",
+            "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes, "results": res}
+
+
+def extra_prefill_batch(torch, q, W, args):
+    """A batch of two 65-token sequences (flattened to 130 tokens) on a 128 x 768 matrix in
+    every format, both tiles; weights rotated over > 1 GiB per sample."""
+    res = []
+    for fi, fmt in enumerate(W.FORMAT_ORDER):
+        d = W.prefill_batch(fi)
+        n = d["x"].shape[0]
+        rot = Rotation(torch, [d["blob"]])
+        hs = [q.QMatrix(rot.slice(c, 0), fmt, d["M"], d["K"]) for c in range(rot.copies)]
+        x = torch.from_numpy(d["x"]).to("cuda")
+        y = torch.empty((n, d["M"]), device="cuda")
+        nb = q.qmm_gemm_workspace_bytes(hs[0].handle, n)
+        ws = torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None
+        graphs = {t: capture(torch, lambda t=t: [q.qmm_gemm_ws(h.handle, x, n, y, t, ws) for h in hs])
+                  for t in (32, 64)}
+        ts = {32: [], 64: []}
+        for r in range(args.rounds):
+            for t in ((32, 64) if r % 2 == 0 else (64, 32)):
+                ts[t].append(time_graph(torch, graphs[t], 1) * 1e3 / len(hs))
+        us = {t: float(np.median(v)) for t, v in ts.items()}
+        chosen = q.qmm_tile_for_tokens(n)
+        flops = 2 * d["M"] * d["K"] * n
+        res.append({"fmt": fmt, "chosen_tile": chosen, "us_per_call": us[chosen], "us_tile32": us[32],
+                    "us_tile64": us[64], "k_split": nb > 0, "weight_bytes": int(d["blob"].size),
+                    "tflops": flops / (us[chosen] * 1e-6) / 1e12,
+                    "frac_mfma": flops / (us[chosen] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+                    "weight_gbs": d["blob"].size / (us[chosen] * 1e-6) / 1e9,
+                    "frac_hbm": d["blob"].size / (us[chosen] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "copies": rot.copies})
+        del graphs, hs, rot, x, y, ws
+        torch.cuda.empty_cache()
+    return {"workload": "batch of 2 x 65 fp16 tokens (flattened to 130) on 128 x 768, qmm_gemm_ws, "
+                        "weights rotated over >1 GiB per sample; 1.4 MFLOP-scale calls bound by their launch",
+            "results": res}
 
 
 def extra_moe(torch, q, W, args):
@@ -420,6 +550,123 @@ def extra_quantize(torch, q, W, mats, args):
 
 # ------------------------------------------------------------------------------------------------
 
+def calibrate(torch, W):
+    """Reference points for the one-token GEMV, both as replays of HIP graphs over rotating
+    copies (> 1 GiB): the launch of a one-element in-place add (an empty kernel), and a
+    plain streaming read of each decode-layer projection's byte count (torch's int32 sum
+    over the bytes) and of the whole layer in one launch."""
+    out = {}
+    t = torch.zeros(1, device="cuda")
+    g = capture(torch, lambda: [t.add_(1) for _ in range(1000)])
+    out["empty_kernel_us"] = time_graph(torch, g, 5) * 1e3 / 1000
+    del g
+    sizes = [(name, M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256) for name, M, K, fmt in W.DECODE_SHAPES]
+    sizes.append(("whole layer", sum(b for _, b in sizes)))
+    reads = []
+    for name, nbytes in sizes:
+        per = (nbytes + 255) // 256 * 256
+        copies = max(2, -(-ROTATE_BYTES // per))
+        buf = torch.ones(copies * per, dtype=torch.uint8, device="cuda")
+        views = [buf[c * per:c * per + nbytes // 4 * 4].view(torch.int32) for c in range(copies)]
+        g = capture(torch, lambda: [v.sum(dtype=torch.int32) for v in views])
+        us = time_graph(torch, g, 5) * 1e3 / copies
+        reads.append({"name": name, "bytes": nbytes, "us": us, "gbs": nbytes / (us * 1e-6) / 1e9})
+        del g, views, buf
+        torch.cuda.empty_cache()
+    out["streaming_read"] = reads
+    return out
+
+
+def _csv_rows(root, suffix):
+    import csv
+    rows = []
+    for path in sorted(glob.glob(os.path.join(root, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def summarize_trace(root):
+    """Markdown summary of a rocprofv3 --kernel-trace run of this benchmark."""
+    from qmm_synth import workloads as W
+    rows = _csv_rows(root, "kernel_trace.csv")
+    if not rows:
+        raise SystemExit(f"no *kernel_trace.csv under {root}")
+    stats = {}
+    for r in rows:
+        name = _col(r, "Kernel_Name", "Kernel-Name")
+        dur = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+        grid = int(_col(r, "Grid_Size_X", "Grid_Size"))
+        wg = int(_col(r, "Workgroup_Size_X", "Workgroup_Size"))
+        stats.setdefault((name, grid, wg), []).append(dur)
+    lines = ["| kernel | grid x | workgroup | dispatches | median us | mean us |", "|---|---|---|---|---|---|"]
+    gemv = []
+    for (name, grid, wg), ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(ds)} | {np.median(ds):.2f} | {np.mean(ds):.2f} |")
+        if "k_gemv1<" in name:
+            gemv.extend(ds)
+    alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M
+              for _, M, K, fmt in W.DECODE_SHAPES) / len(W.DECODE_SHAPES)
+    mean = float(np.mean(gemv)) if gemv else float("nan")
+    lines += ["", f"All one-token GEMV dispatches (k_gemv1, both instances): {len(gemv)}, mean {mean:.3f} us; "
+              f"{len(W.DECODE_SHAPES)} per step -> {len(W.DECODE_SHAPES) * mean:.2f} us of kernel time per step; "
+              f"algorithmic bytes per launch {alg:.0f} -> {alg / (mean * 1e-6) / 1e9:.1f} GB/s "
+              f"= {alg / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} of 8 TB/s.", "",
+              "Machine-readable:", "",
+              f"- source_digest: {source_digest()}",
+              f"- gemv1_dispatches: {len(gemv)}",
+              f"- gemv1_mean_us: {mean:.4f}",
+              f"- alg_bytes_per_launch: {alg:.0f}"]
+    print("\n".join(lines))
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE passes over this benchmark's
+    headline (kernels k_gemv1) and over --copy-probe (the calibration copy)."""
+    from qmm_synth import workloads as W
+
+    def per_dispatch(root, counter, match):
+        vals = {}
+        for r in _csv_rows(root, "counter_collection.csv"):
+            if _col(r, "Counter_Name") != counter or match not in _col(r, "Kernel_Name"):
+                continue
+            key = _col(r, "Dispatch_Id")
+            vals[key] = vals.get(key, 0.0) + float(_col(r, "Counter_Value"))
+        return list(vals.values())
+
+    f = per_dispatch(fetch_dir, "FETCH_SIZE", "k_gemv1<")
+    w = per_dispatch(write_dir, "WRITE_SIZE", "k_gemv1<")
+    cf = per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw = per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    moved_kib = (256 << 20) / 1024
+    ff, wf = moved_kib / float(np.mean(cf)), moved_kib / float(np.mean(cw))
+    traffic = (float(np.mean(f)) * ff + float(np.mean(w)) * wf) * 1024
+    alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M
+              for _, M, K, fmt in W.DECODE_SHAPES) / len(W.DECODE_SHAPES)
+    lines = ["| quantity | value |", "|---|---|",
+             f"| k_gemv1 dispatches (fetch pass / write pass) | {len(f)} / {len(w)} |",
+             f"| FETCH_SIZE per dispatch (KiB, raw) | {np.mean(f):.1f} |",
+             f"| WRITE_SIZE per dispatch (KiB, raw) | {np.mean(w):.2f} |",
+             f"| copy probe: FETCH_SIZE / WRITE_SIZE for {moved_kib:.0f} KiB moved | {np.mean(cf):.1f} / {np.mean(cw):.1f} KiB |",
+             f"| calibration factor fetch / write | {ff:.4f} / {wf:.4f} |",
+             f"| HBM traffic per launch (bytes, calibrated) | {traffic:.0f} |",
+             f"| algorithmic bytes per launch (weights + x + y, mean of the seven) | {alg:.0f} |",
+             f"| traffic / algorithmic | {traffic / alg:.3f} |",
+             "", "Machine-readable (read by bench.py; valid only for this kernel source):", "",
+             f"- source_digest: {source_digest()}",
+             f"- traffic_bytes_per_launch: {traffic:.0f}",
+             f"- fetch_factor: {ff:.4f}",
+             f"- write_factor: {wf:.4f}"]
+    print("\n".join(lines))
+
+
 def copy_probe(torch):
     n = 256 << 20
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -434,6 +681,12 @@ def copy_probe(torch):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -449,6 +702,9 @@ def main():
     if args.copy_probe:
         copy_probe(torch)
         return
+    if args.calibrate:
+        print(json.dumps({"calibration": calibrate(torch, W)}), flush=True)
+        return
     if args.moe_only:
         print(json.dumps({"expert_matvec": extra_moe(torch, q, W, args)}), flush=True)
         return
@@ -460,8 +716,8 @@ def main():
     head, mats = decode_layer(torch, q, W, args)
     log(f"[bench] decode layer: {head['value']:.1f} GB/s, {head['ms_per_step'] * 1e3:.2f} us/step")
     digest = source_digest()
-    dom = head["dominant"]
-    traffic, traffic_note = traffic_from_profile(dom["fmt"], digest)
+    kern = head["kernel"]
+    traffic, traffic_note = traffic_from_profile(digest)
     result = {
         "metric": METRIC,
         "value": round(head["value"], 2),
@@ -482,40 +738,47 @@ def main():
             "layer_weight_bytes": head["layer_weight_bytes"],
             "frac_hbm": head["value"] / HBM_PEAK_GBS,
             "event_ms_per_step": head["event_ms_per_step"],
-            "sum_of_kernel_us": head["sum_kernel_us"],
+            "sum_of_isolated_kernel_us": head["sum_isolated_us"],
             "copies": head["copies"],
+            "rotation_bytes": head["rotation_bytes"],
             "source_digest": digest,
             "projections": head["projections"],
         },
         "roofline": {
-            "kernel": f"qmm::k_gemv1<{dom['fmt']}, fp32 x> (one-token GEMV)",
+            "kernel": "qmm::k_gemv1 (one-token GEMV; Q4_K and Q6_K instances, seven launches per step)",
             "bound": "hbm",
-            "achieved": round(dom["achieved_gbs"], 1),
+            "achieved": round(kern["achieved_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": dom["achieved_gbs"] / HBM_PEAK_GBS,
+            "frac": kern["achieved_gbs"] / HBM_PEAK_GBS,
             "traffic": traffic,
             "traffic_note": traffic_note,
-            "avg_launch_us": dom["avg_us"],
-            "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
-            "launches_per_step": dom["launches_per_step"],
-            "projections": dom["projections"],
+            "avg_launch_us": kern["avg_us"],
+            "alg_bytes_per_launch": kern["alg_bytes_per_launch"],
+            "launches_per_step": kern["launches_per_step"],
+            "launch_time_source": "HIP events around the timed region (graph replays on the current stream) / "
+                                  "launches; per-dispatch trace durations in profiles/ add up to the step",
         },
     }
+    extras = {}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(mats)
         log(f"[bench] cpu baseline: {result['cpu_baseline']['value']:.4f} GB/s")
+        t0 = time.time()
+        extras["oracle_per_config"] = oracle_per_config(W, mats)
+        log(f"[bench] oracle per config done in {time.time() - t0:.1f}s")
     if not args.no_extras:
-        extras = {}
         for name, fn in (("single_matvec", lambda: extra_single_matvec(torch, q, W, args)),
                          ("small_decode_a4g64", lambda: extra_small_decode(torch, q, W, args)),
                          ("prefill_gemm", lambda: extra_prefill(torch, q, W, mats, args)),
+                         ("prefill_batch_2x65", lambda: extra_prefill_batch(torch, q, W, args)),
                          ("expert_matvec", lambda: extra_moe(torch, q, W, args)),
                          ("quantize", lambda: extra_quantize(torch, q, W, mats, args))):
             t0 = time.time()
             extras[name] = fn()
             log(f"[bench] extra {name} done in {time.time() - t0:.1f}s")
             torch.cuda.empty_cache()
+    if extras:
         result["extras"] = extras
     print(json.dumps(result), flush=True)
 
