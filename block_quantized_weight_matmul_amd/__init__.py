@@ -18,11 +18,12 @@ import ctypes
 
 import torch
 
-from ._lib import DTYPES, LIB_PATH, QMM_OK, STATUS, TILES, TYPES, QmmError, check, lib  # noqa: F401
+from ._lib import DTYPES, LIB_PATH, NOALLOC_SCRATCH_BYTES, QMM_OK, STATUS, TILES, TYPES, QmmError, check, lib  # noqa: F401
 
 __all__ = [
     "QMatrix", "QmmError", "LIB_PATH", "TYPES",
     "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
+    "qmm_gemm_noalloc",
     "qmm_gemm_id", "qmm_gemm_id_tiled", "qmm_dequantize", "qmm_quantize", "quantize",
     "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_block_weights", "qmm_block_bytes",
 ]
@@ -198,6 +199,14 @@ def qmm_gemm_ws(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, ws: torch.T
         xp, yp, wp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32), (ws, "ws", None, None))
         wb = ws.numel() * ws.element_size()
     check(lib.qmm_gemm_ws(h, xp, _xt(x), N, yp, t, wp, wb, _stream(stream)))
+
+
+def qmm_gemm_noalloc(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, stream=None) -> None:
+    m = _meta(h)
+    N = _count(N, "N", 0)
+    t = TILES[tile] if tile in TILES else int(tile)
+    xp, yp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32))
+    check(lib.qmm_gemm_noalloc(h, xp, _xt(x), N, yp, t, _stream(stream)))
 
 
 def _id_args(m, x, N, S, x_per_slot, ids, y):

@@ -17,6 +17,7 @@ STATUS = {
 TYPES = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "q6_k": 3, "a4g64": 4}
 DTYPES = {"f32": 0, "f16": 1}
 TILES = {"auto": 0, 32: 32, 64: 64}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # QMM_NOALLOC_SCRATCH_BYTES of include/qmm.h
 
 
 class QmmError(RuntimeError):
@@ -38,6 +39,7 @@ def _load():
         "qmm_gemm": (c_int, [vp, vp, c_int, i64, vp, c_int, vp]),
         "qmm_gemm_ws": (c_int, [vp, vp, c_int, i64, vp, c_int, vp, ctypes.c_size_t, vp]),
         "qmm_gemm_workspace_bytes": (ctypes.c_size_t, [vp, i64]),
+        "qmm_gemm_noalloc": (c_int, [vp, vp, c_int, i64, vp, c_int, vp]),
         "qmm_gemm_id": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, vp]),
         "qmm_gemm_id_tiled": (c_int, [vp, vp, c_int, i64, i64, c_int, vp, vp, c_int, vp]),
         "qmm_dequantize": (c_int, [vp, i64, vp, c_int, vp]),

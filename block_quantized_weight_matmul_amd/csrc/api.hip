@@ -138,6 +138,9 @@ qmm_status qmm_create(qmm_matrix** out, qmm_type type, const void* blocks, int64
   h->d.row_bytes = rb;
   h->d.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   h->device = dev;
+  // set-up of qmm_gemm_noalloc's scratch on this device (once per device); a failure
+  // is reported by that entry point, the others do not need it
+  (void)qmm::gemm_scratch_init(dev);
   *out = h;
   return ok();
 }
@@ -215,6 +218,38 @@ qmm_status qmm_gemm_ws(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t
   const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
   const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, need > 0 ? static_cast<float*>(ws) : nullptr,
                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return ok();
+}
+
+qmm_status qmm_gemm_noalloc(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N, float* y, qmm_tile tile,
+                            qmm_stream_t stream) {
+  if (!h) return fail(QMM_E_ARG, "handle is NULL");
+  if (h->d.n_experts != 1) return fail(QMM_E_ARG, "qmm_gemm_noalloc needs a handle with n_experts == 1");
+  if (tile != QMM_TILE_AUTO && tile != QMM_TILE_32 && tile != QMM_TILE_64)
+    return fail(QMM_E_ARG, "tile must be QMM_TILE_AUTO, QMM_TILE_32 or QMM_TILE_64 (got %d)", static_cast<int>(tile));
+  if (N < 0 || N > (1LL << 24))
+    return fail(QMM_E_SHAPE, "qmm_gemm_noalloc takes 0..2^24 tokens (got %lld)", static_cast<long long>(N));
+  if (h->d.K >= qmm::kMaxGemmK)
+    return fail(QMM_E_SHAPE, "qmm_gemm_noalloc takes K below %lld (handle has K=%lld)",
+                static_cast<long long>(qmm::kMaxGemmK), static_cast<long long>(h->d.K));
+  qmm_status s;
+  if ((s = check_x(x, xt)) != QMM_OK || (s = check_y(y)) != QMM_OK) return s;
+  if (N == 0) return ok();
+  const size_t need = qmm::gemm_workspace_bytes(h->d, N);
+  if (need > qmm::gemm_scratch_bytes())
+    return fail(QMM_E_SHAPE,
+                "qmm_gemm_noalloc: this call's K split needs %zu bytes of scratch, above the library's %zu "
+                "(use qmm_gemm_ws with a workspace, or qmm_gemm)", need, qmm::gemm_scratch_bytes());
+  if ((s = check_device(h)) != QMM_OK) return s;
+  float* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t ei = qmm::gemm_scratch_init(h->device);  // no-op after qmm_create's
+    if (ei != hipSuccess) return hip_fail(ei, "hipGetSymbolAddress(scratch)");
+    scratch = qmm::gemm_scratch(h->device);
+  }
+  const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
+  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, scratch, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }

@@ -30,10 +30,12 @@
 #include <algorithm>
 #include <atomic>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "decode.hpp"
 #include "internal.hpp"
+#include "qmm.h"
 
 namespace qmm {
 
@@ -1111,6 +1113,41 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
   a.id_ranks = static_cast<int>(ranks);
   hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(groups * ranks8)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Scratch of the allocation-free matrix-matrix entry point (qmm_gemm_noalloc): the K-split
+// partial products of qmm_gemm_ws live in this file-scope device array instead of a
+// caller's workspace.  Every GPU the library runs on holds its own copy until the process
+// ends.  Host code never names the array in a launch or a copy: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and kept.
+constexpr size_t kScratchBytes = QMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+size_t gemm_scratch_bytes() { return kScratchBytes; }
+
+hipError_t gemm_scratch_init(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev] = p;
+  return hipSuccess;
+}
+
+float* gemm_scratch(int dev) {
+  if (dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return static_cast<float*>(g_scratch_ptr[dev]);
 }
 
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,

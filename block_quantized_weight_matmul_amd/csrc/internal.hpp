@@ -42,6 +42,11 @@ size_t gemm_workspace_bytes(const MatDesc& m, int64_t N);
 // (unsplit)
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
                        hipStream_t s);
+// The allocation-free entry point's scratch: its size, the once-per-device lookup of its
+// device address (call with dev current), and that address (nullptr before the lookup).
+size_t gemm_scratch_bytes();
+hipError_t gemm_scratch_init(int dev);
+float* gemm_scratch(int dev);
 // tile: 32 or 64, or 0 for the tile rule on each expert's pair count
 hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N, int64_t S, int x_per_slot,
                           const int32_t* ids, float* y, int tile, hipStream_t s);

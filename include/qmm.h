@@ -179,6 +179,28 @@ qmm_status qmm_gemm_ws(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t
                        qmm_stream_t stream);
 
 /*
+ * qmm_gemm_noalloc -- qmm_gemm_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, arguments, tile rule, K split and results, bit for
+ * bit, as qmm_gemm_ws, with the split's partial products in a scratch array the
+ * library holds in device memory (QMM_NOALLOC_SCRATCH_BYTES per GPU, reserved when the
+ * library's code is loaded on that GPU and kept until the process ends).  The call
+ * allocates nothing, on the device or the host.
+ *   x, xt, N, y, tile  as qmm_gemm.
+ * Errors: as qmm_gemm, and QMM_E_SHAPE when the call's split needs more than
+ * QMM_NOALLOC_SCRATCH_BYTES, i.e. qmm_gemm_workspace_bytes(h, N) above it (nothing is
+ * launched; use qmm_gemm_ws or qmm_gemm).  QMM_E_HIP if the scratch's
+ * device address cannot be found.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and must be serialised by the
+ * caller, e.g. by issuing them on one stream.  The scratch keeps the last call's
+ * partial products; each split call overwrites every element it reads.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qmm_status qmm_gemm_noalloc(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
+                            float *y, qmm_tile tile, qmm_stream_t stream);
+
+/*
  * qmm_gemm_id -- expert-indexed matrix-vector path (MUL_MAT_ID in the llama.cpp
  * pull request above): y[t, s, r] = sum_k x_ts[k] * w_{ids[t, s]}[r, k].
  *   h           handle with n_experts = E >= 1 (experts stacked in `blocks`).

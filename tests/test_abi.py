@@ -102,3 +102,10 @@ def test_binding_refuses_bad_type_name():
 def test_workspace_query_without_handle():
     L = _lib()
     assert L.lib.qmm_gemm_workspace_bytes(None, 7) == 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define QMM_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "QMM_NOALLOC_SCRATCH_BYTES not found"
+    assert _lib().NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
