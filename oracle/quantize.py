@@ -149,6 +149,8 @@ def quant_a4g64(w):
 
 
 _QUANT = {"q4_0": quant_q4_0, "q8_0": quant_q8_0, "q4_k": quant_q4_k, "q6_k": quant_q6_k, "a4g64": quant_a4g64}
+# the formats with a reference quantizer (the library's GPU quantizer covers the same ones)
+QUANT_FORMATS = tuple(_QUANT)
 
 
 def quantize_blocks(fmt: str, w: np.ndarray) -> np.ndarray:

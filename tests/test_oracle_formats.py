@@ -21,6 +21,9 @@ from qmm_synth import quantize
 from tests.golden_io import GOLDEN, read_blocks
 
 CASES = read_blocks()
+# byte offsets of each format's fp16 scale fields
+SCALE_OFFSETS = {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2], "q4_1": [0, 2],
+                 "q5_0": [0], "q5_1": [0, 2], "q2_k": [0, 2], "q3_k": [0], "q5_k": [0, 2]}
 
 
 def test_golden_covers_every_format():
@@ -42,7 +45,12 @@ def test_golden_block(case):
 
 def test_block_geometry():
     assert oracle.FORMATS == {
-        "q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210), "a4g64": (64, 36)}
+        "q4_0": (32, 18), "q8_0": (32, 34), "q4_k": (256, 144), "q6_k": (256, 210), "a4g64": (64, 36),
+        "q4_1": (32, 20), "q5_0": (32, 22), "q5_1": (32, 24), "q2_k": (256, 84), "q3_k": (256, 110),
+        "q5_k": (256, 176)}
+    # bits per weight: 4.5, 8.5, 4.5, 6.5625, 4.5, 5, 5.5, 6, 2.625, 3.4375, 5.5
+    assert oracle.row_bytes("q2_k", 2560) == 840 and oracle.row_bytes("q3_k", 2560) == 1100
+    assert oracle.row_bytes("q5_k", 2560) == 1760 and oracle.row_bytes("q5_0", 512) == 352
     assert oracle.row_bytes("q4_0", 512) == 288
     assert oracle.row_bytes("q4_k", 2560) == 1440
     assert oracle.row_bytes("q6_k", 9728) == 7980
@@ -88,6 +96,31 @@ def _bound(fmt, blocks_u8, w_true, w_hat):
     if fmt == "q6_k":
         sc = np.abs(blk[:, 2:18].view(np.int8).astype(np.float64))
         return np.repeat(f16(0)[:, None] * sc / 2 * rel, 16, axis=1)
+    if fmt in ("q4_1", "q5_1"):
+        return np.repeat(f16(0)[:, None] / 2 * rel, 32, axis=1) + 2.0 ** -24 * np.abs(w_hat.reshape(nb, 32))
+    if fmt == "q5_0":
+        d = np.abs(f16(0))[:, None]
+        qs = blk[:, 6:22]
+        qh = sum(blk[:, 2 + b].astype(np.int64) << (8 * b) for b in range(4))
+        q = np.concatenate([qs & 15, qs >> 4], axis=1) | (((qh[:, None] >> np.arange(32)) & 1) << 4)
+        return np.where(q == 31, d * (1 + 2.0 ** -7), d / 2 * rel)
+    if fmt == "q2_k":
+        sc = (blk[:, 4:20] & 15).astype(np.float64)
+        step = f16(0)[:, None] * sc
+        return np.repeat(step / 2 * rel, 16, axis=1) + 2.0 ** -24 * np.abs(w_hat.reshape(nb, 256))
+    if fmt == "q3_k":
+        bits = [int.from_bytes(bytes(row), "little") for row in blk[:, 2:14]]   # 96-bit strings
+        s = np.array([[((b >> (6 * j)) & 63) - 32 for j in range(16)] for b in bits], np.float64)
+        step = np.repeat(np.abs(f16(0)[:, None] * s), 16, axis=1)
+        code = np.divide(w_hat.reshape(nb, 256), np.where(step == 0, 1, np.repeat(f16(0)[:, None] * s, 16, axis=1)))
+        # the far end of the codes (+3) may hold a clamped value: one full step there
+        return np.where(np.abs(code - 3) < 1e-9, step * rel, step / 2 * rel)
+    if fmt == "q5_k":
+        raw = blk[:, 4:16].astype(np.int64)
+        bits = sum(raw[:, i] << (8 * i) for i in range(12))
+        sc = np.stack([(bits >> (6 * j)) & 63 for j in range(8)], axis=1).astype(np.float64)
+        step = f16(0)[:, None] * sc
+        return np.repeat(step / 2 * rel, 32, axis=1) + 2.0 ** -24 * np.abs(w_hat.reshape(nb, 256))
     raise AssertionError(fmt)
 
 
@@ -143,7 +176,7 @@ def test_random_bytes_structure(fmt):
     g = np.random.default_rng([11, bb])
     blk = g.integers(0, 256, size=(64, bb), dtype=np.uint8)
     # keep fp16 scale fields finite and normal-sized
-    for off in {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2]}[fmt]:
+    for off in SCALE_OFFSETS[fmt]:
         blk[:, off + 1] &= 0x3B
     w = oracle.dequantize_blocks(fmt, blk).astype(np.float64)
     assert np.all(np.isfinite(w))
@@ -158,6 +191,19 @@ def test_random_bytes_structure(fmt):
     elif fmt == "q6_k":
         r = w[nz] / d[nz]
         assert np.all(r == np.round(r)) and np.abs(r).max() <= 4096
+    elif fmt == "q5_0":
+        r = w[nz] / d[nz]
+        assert np.all(r == np.round(r)) and r.min() >= -16 and r.max() <= 15
+        assert r.min() == -16 and r.max() == 15       # the top bit reaches both ends on random bytes
+    elif fmt == "q3_k":
+        r = w[nz] / d[nz]
+        assert np.all(r == np.round(r)) and np.abs(r).max() <= 128
+    elif fmt in ("q4_1", "q5_1"):
+        # (w - m) / d is a code 0..15 or 0..31 wherever the add was exact
+        m = (blk[:, 2].astype(np.uint16) | (blk[:, 3].astype(np.uint16) << 8)).view(np.float16).astype(np.float64)
+        r = (w - m[:, None])[nz] / d[nz]
+        near = np.abs(r - np.round(r)) < 1e-3
+        assert near.mean() > 0.9 and np.round(r[near]).max() <= (15 if fmt == "q4_1" else 31)
 
 
 # --- the fp16 staging value of the matrix-matrix path -----------------------------------------
@@ -199,16 +245,22 @@ def test_staged_fp16_keeps_signed_zero():
 
 def test_staged_fp16_of_double_rounding_blocks():
     # the golden blocks built so that rounding the exact weight once to fp16 would give
-    # 2+2^-9: staging rounds the fp32 weight, so weight 0 stages as 2.0
-    for case in CASES:
-        if case["name"].endswith("_fp16_staging_double_rounding"):
-            w = oracle.dequantize_blocks(case["fmt"], np.frombuffer(case["data"], np.uint8))[0]
-            assert float(w[0]) == 2.0 + 2.0 ** -10
-            exact = case["expect"][0]
-            assert float(oracle.staged_fp16(w)[0]) == 2.0
-            # and the tie is a real one: the exact value lies strictly above the fp16 midpoint
-            assert exact == Fraction(2) + Fraction(1, 1024)
-            assert float(np.float16(float(Fraction(2) + Fraction(1, 1024) + Fraction(1, 2 ** 24)))) == 2.0 + 2.0 ** -9
+    # another value than staging does: staging rounds the fp32 weight (an fp16 tie) to even
+    cases = [c for c in CASES if c["name"].endswith("_fp16_staging_double_rounding")]
+    assert {c["fmt"] for c in cases} == {"q4_k", "a4g64", "q4_1", "q5_1", "q2_k", "q5_k"}
+    for case in cases:
+        w = oracle.dequantize_blocks(case["fmt"], np.frombuffer(case["data"], np.uint8))[0]
+        if case["fmt"] == "q2_k":
+            # exact 3 + 3*2^-10 - 2^-24 -> fp32 3 + 3*2^-10, between 3+2^-9 and 3+2^-8
+            tie, exact, even, one_rounding = 3 + 3 * 2.0 ** -10, Fraction(3) + Fraction(3, 1024) - Fraction(1, 2 ** 24), \
+                3 + 2.0 ** -8, 3 + 2.0 ** -9
+        else:
+            # exact 2 + 2^-10 (+ or -) 2^-24 -> fp32 2 + 2^-10, between 2 and 2+2^-9
+            tie, exact, even, one_rounding = 2 + 2.0 ** -10, None, 2.0, 2 + 2.0 ** -9
+        assert float(w[0]) == tie
+        assert float(oracle.staged_fp16(w)[0]) == even
+        if exact is not None:
+            assert float(np.float16(float(exact))) == one_rounding
 
 
 def test_golden_file_matches_its_packer():

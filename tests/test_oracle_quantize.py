@@ -16,6 +16,7 @@ import pytest
 
 import oracle
 from oracle import quantize as oq
+from oracle.quantize import QUANT_FORMATS
 from tests.test_oracle_formats import _bound
 
 encoders = importlib.import_module("qmm_synth.quantize")
@@ -37,7 +38,7 @@ def test_f16_helpers():
     assert oq.rha(2.5) == 3.0 and oq.rha(-2.5) == -3.0 and oq.rha(2.49) == 2.0 and oq.rha(0.0) == 0.0
 
 
-@pytest.mark.parametrize("fmt", list(oracle.FORMATS))
+@pytest.mark.parametrize("fmt", list(QUANT_FORMATS))
 def test_zero_blocks(fmt):
     blob = oracle.quantize_blocks(fmt, np.zeros((1, oracle.block_weights(fmt)), np.float32))
     expect = {
@@ -78,10 +79,10 @@ def test_q8_0_ramp():
     assert np.all(q == np.sign(w[0]) * np.floor(np.abs(w[0] / d) + 0.5))
 
 
-@pytest.mark.parametrize("fmt", list(oracle.FORMATS))
+@pytest.mark.parametrize("fmt", list(QUANT_FORMATS))
 @pytest.mark.parametrize("dist", ["normal", "uniform_pos", "all_negative", "spiky", "constant"])
 def test_round_trip_bound(fmt, dist):
-    g = np.random.default_rng([8, list(oracle.FORMATS).index(fmt), len(dist)])
+    g = np.random.default_rng([8, list(QUANT_FORMATS).index(fmt), len(dist)])
     M, K = 3, 512
     if dist == "normal":
         w = g.normal(0, 0.02, (M, K))
@@ -102,7 +103,7 @@ def test_round_trip_bound(fmt, dist):
     assert np.all(err <= _bound(fmt, blob, w, w_hat) + 1e-30)
 
 
-@pytest.mark.parametrize("fmt", list(oracle.FORMATS))
+@pytest.mark.parametrize("fmt", list(QUANT_FORMATS))
 def test_agrees_with_test_data_encoders(fmt):
     w = np.random.default_rng(9).normal(0, 0.5, (4, 512)).astype(np.float32)
     w[1, :64] = 0.0
