@@ -14,7 +14,8 @@ STATUS = {
     0: "QMM_OK", -1: "QMM_E_ARG", -2: "QMM_E_TYPE", -3: "QMM_E_SHAPE",
     -4: "QMM_E_ALIGN", -5: "QMM_E_DEVICE", -6: "QMM_E_HIP",
 }
-TYPES = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "q6_k": 3, "a4g64": 4}
+TYPES = {"q4_0": 0, "q8_0": 1, "q4_k": 2, "q6_k": 3, "a4g64": 4,
+         "q4_1": 5, "q5_0": 6, "q5_1": 7, "q2_k": 8, "q3_k": 9, "q5_k": 10}
 DTYPES = {"f32": 0, "f16": 1}
 TILES = {"auto": 0, 32: 32, 64: 64}
 NOALLOC_SCRATCH_BYTES = 64 << 20  # QMM_NOALLOC_SCRATCH_BYTES of include/qmm.h

@@ -34,10 +34,12 @@ qmm_status ok() {
   return QMM_OK;
 }
 
-constexpr int kBW[5] = {32, 32, 256, 256, 64};
-constexpr int kBB[5] = {18, 34, 144, 210, 36};
+constexpr int kBW[qmm::kNumFormats] = {32, 32, 256, 256, 64, 32, 32, 32, 256, 256, 256};
+constexpr int kBB[qmm::kNumFormats] = {18, 34, 144, 210, 36, 20, 22, 24, 84, 110, 176};
 
-bool valid_type(int t) { return t >= 0 && t < 5; }
+bool valid_type(int t) { return t >= 0 && t < qmm::kNumFormats; }
+// the types qmm_quantize encodes (the others have no quantizer here)
+bool quantizable_type(int t) { return t >= 0 && t <= QMM_A4G64; }
 bool valid_dtype(int t) { return t == QMM_F32 || t == QMM_F16; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -314,6 +316,9 @@ qmm_status qmm_gemm_id_tiled(const qmm_matrix* h, const void* x, qmm_dtype xt, i
 
 qmm_status qmm_quantize(qmm_type type, const float* w, int64_t M, int64_t K, void* blocks, qmm_stream_t stream) {
   if (!valid_type(type)) return fail(QMM_E_TYPE, "unknown block type %d", static_cast<int>(type));
+  if (!quantizable_type(type))
+    return fail(QMM_E_TYPE, "qmm_quantize encodes Q4_0, Q8_0, Q4_K, Q6_K and A4G64 only (got type %d)",
+                static_cast<int>(type));
   if (M < 0 || M > INT_MAX / 2) return fail(QMM_E_SHAPE, "M=%lld out of range", static_cast<long long>(M));
   const size_t rb = qmm_row_bytes(type, K);
   if (rb == 0 || K > INT_MAX / 2)

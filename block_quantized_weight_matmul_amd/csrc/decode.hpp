@@ -27,6 +27,14 @@
 //   Q4_K   w = d*sc*q - dmin*m -> fma(q, d*sc, -(dmin*m))
 //   Q6_K   w = d*sc*(q-32)     -> fma(q, d*sc, -32*d*sc)
 //   A4G64  w = scale*q + bias  -> fma(q, scale, bias)
+// and the other types that section lists, whose formulas are read from their
+// names (a scale times a zero-centred code for an "_0" type, a scale and a
+// minimum for an "_1" type, per-sub-block scales and minimums in a K-quant):
+//   Q4_1, Q5_1  w = d*q + m    -> fma(q, d, m)
+//   Q5_0   w = d*(q-16)        -> fma(q, d, -16d)
+//   Q2_K   w = d*sc*q - dmin*m -> fma(q, d*sc, -(dmin*m))   (16-weight sub-blocks)
+//   Q3_K   w = d*(s-32)*(q-4)  -> fma(q, d*(s-32), -4*d*(s-32))
+//   Q5_K   w = d*sc*q - dmin*m -> fma(q, d*sc, -(dmin*m))   (a fifth code bit)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,7 +47,11 @@ using u16 = uint16_t;
 using u32 = uint32_t;
 using u64 = uint64_t;
 
-enum : int { FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_A4G64 = 4 };
+enum : int {
+  FMT_Q4_0 = 0, FMT_Q8_0 = 1, FMT_Q4_K = 2, FMT_Q6_K = 3, FMT_A4G64 = 4,
+  FMT_Q4_1 = 5, FMT_Q5_0 = 6, FMT_Q5_1 = 7, FMT_Q2_K = 8, FMT_Q3_K = 9, FMT_Q5_K = 10,
+  kNumFormats = 11
+};
 
 template <int F> struct FmtInfo;
 template <> struct FmtInfo<FMT_Q4_0> { static constexpr int BW = 32, BB = 18; };
@@ -47,6 +59,12 @@ template <> struct FmtInfo<FMT_Q8_0> { static constexpr int BW = 32, BB = 34; };
 template <> struct FmtInfo<FMT_Q4_K> { static constexpr int BW = 256, BB = 144; };
 template <> struct FmtInfo<FMT_Q6_K> { static constexpr int BW = 256, BB = 210; };
 template <> struct FmtInfo<FMT_A4G64> { static constexpr int BW = 64, BB = 36; };
+template <> struct FmtInfo<FMT_Q4_1> { static constexpr int BW = 32, BB = 20; };
+template <> struct FmtInfo<FMT_Q5_0> { static constexpr int BW = 32, BB = 22; };
+template <> struct FmtInfo<FMT_Q5_1> { static constexpr int BW = 32, BB = 24; };
+template <> struct FmtInfo<FMT_Q2_K> { static constexpr int BW = 256, BB = 84; };
+template <> struct FmtInfo<FMT_Q3_K> { static constexpr int BW = 256, BB = 110; };
+template <> struct FmtInfo<FMT_Q5_K> { static constexpr int BW = 256, BB = 176; };
 
 // fp16 bit pattern (low 16 bits) -> exact fp32 (subnormals included).
 __device__ __forceinline__ float h2f(u32 bits) {
@@ -251,6 +269,176 @@ template <> struct Decoder<FMT_A4G64> {
   }
 };
 
+// Four bits n (0..15) spread to bit 0 of the four bytes of a word: bit k of n to byte k.
+__device__ __forceinline__ u32 spread4(u32 n) { return (n * 0x00204081u) & 0x01010101u; }
+
+// Field f of a little-endian string of 6-bit fields held in words w1 (bits 0..31), w2, w3
+// (the 96-bit string of the K-quants), for f < 16, without a runtime-indexed word.
+__device__ __forceinline__ u32 six_bit_field(u32 w1, u32 w2, u32 w3, u32 f) {
+  const u32 b = 6u * f;  // 0..90
+  const u32 t0 = __builtin_amdgcn_alignbit(w2, w1, b & 31u);
+  const u32 t1 = __builtin_amdgcn_alignbit(w3, w2, b & 31u);
+  const u32 t2 = w3 >> (b & 31u);
+  return (b < 32 ? t0 : (b < 64 ? t1 : t2)) & 63u;
+}
+
+// Q4_1: block u: fp16 d and m, codes as Q4_0.  20-byte blocks: every block is 4-byte aligned.
+template <> struct Decoder<FMT_Q4_1> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { u32 hdr; u32 q[4]; };
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32* p = reinterpret_cast<const u32*>(base + row_off + 20u * u);
+    r.hdr = p[0];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.q[k] = p[1 + k];
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o.c[j] = r.q[j] & 0x0F0F0F0Fu;
+      o.c[4 + j] = (r.q[j] >> 4) & 0x0F0F0F0Fu;
+    }
+    o.a0 = o.a1 = h2f(r.hdr);
+    o.b0 = o.b1 = h2f(r.hdr >> 16);
+  }
+};
+
+// The 32 five-bit codes of a Q5_0/Q5_1 block: low nibbles from the 16 code bytes as
+// Q4_0, bit i of the 32-bit qh word on top of code i.
+__device__ __forceinline__ void five_bit_codes(u32 qh, const u32 (&q)[4], Unit& o) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o.c[j] = (q[j] & 0x0F0F0F0Fu) | (spread4((qh >> (4 * j)) & 15u) << 4);
+    o.c[4 + j] = ((q[j] >> 4) & 0x0F0F0F0Fu) | (spread4((qh >> (16 + 4 * j)) & 15u) << 4);
+  }
+}
+
+// Q5_0: block u: fp16 d, qh, codes; 22-byte blocks are 2-byte aligned (realigned words).
+template <> struct Decoder<FMT_Q5_0> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { RawBytes<20> b; u32 d; };  // bytes [2, 22): qh, then the 16 code bytes
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 bo = row_off + 22u * u;
+    r.b.load(base + bo + 2);
+    r.d = load_u16(base + bo);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 q[4] = {r.b.word(1), r.b.word(2), r.b.word(3), r.b.word(4)};
+    five_bit_codes(r.b.word(0), q, o);
+    const float d = h2f(r.d);
+    o.a0 = o.a1 = d;
+    o.b0 = o.b1 = -16.0f * d;  // exact
+  }
+};
+
+// Q5_1: block u: fp16 d and m, qh, codes; 24-byte blocks are 8-byte aligned.
+template <> struct Decoder<FMT_Q5_1> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { u32 hdr, qh; u32 q[4]; };
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32* p = reinterpret_cast<const u32*>(base + row_off + 24u * u);
+    r.hdr = p[0];
+    r.qh = p[1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.q[k] = p[2 + k];
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    five_bit_codes(r.qh, r.q, o);
+    o.a0 = o.a1 = h2f(r.hdr);
+    o.b0 = o.b1 = h2f(r.hdr >> 16);
+  }
+};
+
+// Q2_K: super-block u/8, a = u%8 covers weights 32a .. 32a+31 (16-weight sub-blocks 2a,
+// 2a+1): codes are bits 2(a/2) .. +1 of qs[32(a%2) + i]; sc and m of sub-block j are the
+// nibbles of sm[j].  84-byte super-blocks are 4-byte aligned.
+template <> struct Decoder<FMT_Q2_K> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { u32 hdr, sm; u32 q[8]; int a; };
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 so = row_off + 84u * (u >> 3);
+    r.a = u & 7;
+    r.hdr = *reinterpret_cast<const u32*>(base + so);
+    r.sm = load_u16(base + so + 4 + 2 * r.a);
+    const u32* q = reinterpret_cast<const u32*>(base + so + 20 + 32 * (r.a & 1));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r.q[k] = q[k];
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 sh = 2u * static_cast<u32>(r.a >> 1);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o.c[k] = (r.q[k] >> sh) & 0x03030303u;
+    const float d = h2f(r.hdr), dmin = h2f(r.hdr >> 16);
+    o.a0 = d * static_cast<float>(r.sm & 15u);          // exact
+    o.b0 = -(dmin * static_cast<float>((r.sm >> 4) & 15u));
+    o.a1 = d * static_cast<float>((r.sm >> 8) & 15u);
+    o.b1 = -(dmin * static_cast<float>((r.sm >> 12) & 15u));
+  }
+};
+
+// Q3_K: super-block u/8, a = u%8 covers weights 32a .. 32a+31 (sub-blocks 2a, 2a+1): low
+// bits are bits 2(a/2) .. +1 of ql[32(a%2) + i], the top bit is bit a of qh[i]; the scale
+// fields s_2a, s_2a+1 are the 12 bits at bit 12a of the 96-bit string.  110-byte
+// super-blocks are 2-byte aligned (realigned words).
+template <> struct Decoder<FMT_Q3_K> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { RawBytes<32> ql, qh; RawBytes<4> s; u32 d; int a; };
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 so = row_off + 110u * (u >> 3);
+    r.a = u & 7;
+    r.ql.load(base + so + 14 + 32 * (r.a & 1));
+    r.qh.load(base + so + 78);
+    r.s.load(base + so + 2 + ((12 * r.a) >> 3));  // within the block: ends before byte 16
+    r.d = load_u16(base + so);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 sh = 2u * static_cast<u32>(r.a >> 1);
+    const u32 hb = static_cast<u32>(r.a);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      o.c[k] = ((r.ql.word(k) >> sh) & 0x03030303u) | (((r.qh.word(k) >> hb) & 0x01010101u) << 2);
+    const u32 f = r.s.word(0) >> ((12u * hb) & 7u);
+    const float d = h2f(r.d);
+    o.a0 = d * static_cast<float>(static_cast<int>(f & 63u) - 32);         // exact
+    o.a1 = d * static_cast<float>(static_cast<int>((f >> 6) & 63u) - 32);
+    o.b0 = -4.0f * o.a0;  // exact (power of two)
+    o.b1 = -4.0f * o.a1;
+  }
+};
+
+// Q5_K: super-block u/8, sub-block j = u%8: low nibbles as Q4_K, the top bit is bit j of
+// qh[i].  176-byte super-blocks are 16-byte aligned.
+template <> struct Decoder<FMT_Q5_K> {
+  static constexpr float kCodeBias = 0.0f;
+  struct Raw { u32 h[4]; u32 qh[8]; u32 q[8]; int j; };
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int u, Raw& r) {
+    const u32 so = row_off + 176u * (u >> 3);
+    r.j = u & 7;
+    const u32* h = reinterpret_cast<const u32*>(base + so);
+    const u32* qh = reinterpret_cast<const u32*>(base + so + 16);
+    const u32* q = reinterpret_cast<const u32*>(base + so + 48 + 32 * (r.j >> 1));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.h[k] = h[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      r.qh[k] = qh[k];
+      r.q[k] = q[k];
+    }
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit& o) {
+    const u32 sh = 4u * static_cast<u32>(r.j & 1);
+    const u32 hb = static_cast<u32>(r.j);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      o.c[k] = ((r.q[k] >> sh) & 0x0F0F0F0Fu) | (((r.qh[k] >> hb) & 0x01010101u) << 4);
+    const float d = h2f(r.h[0]), dmin = h2f(r.h[0] >> 16);
+    const u32 sc = six_bit_field(r.h[1], r.h[2], r.h[3], hb);
+    const u32 m = six_bit_field(r.h[1], r.h[2], r.h[3], 8u + hb);
+    o.a0 = o.a1 = d * static_cast<float>(sc);        // exact
+    o.b0 = o.b1 = -(dmin * static_cast<float>(m));   // exact
+  }
+};
+
 // The 32 codes of an unpacked unit as floats, in K order (weight i sits in byte
 // i%4 of word i/4), with the format's code bias removed (exact: small integers).
 template <int F>
@@ -289,7 +477,8 @@ namespace qmm {
 // ---------------------------------------------------------------------------------------------
 // Matrix-vector work items: RUNS runs of 32 weights that share their bytes, so the
 // scale fields and code bytes are fetched and unpacked once for all of them.
-//   Q4_0, Q8_0  one block (1 run, unit i).
+//   Q4_0, Q8_0  one block (1 run, unit i); the types read from their names
+//               likewise take one unit per item.
 //   Q4_K        sub-blocks 2p, 2p+1 of a super-block (units 2i, 2i+1): the low and
 //               high nibbles of the same 32 code bytes, one 16-byte header.
 //   Q6_K        runs a and a+4 of a super-block (units 8s+a, 8s+a+4, a = i%4): the
@@ -320,6 +509,23 @@ template <> struct Item<FMT_Q8_0> {
   }
   __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[1]) { Decoder<FMT_Q8_0>::unpack(r, o[0]); }
 };
+
+// One-unit items of the other types: the unit's decoder as it is.
+template <int F> struct ItemOne {
+  static constexpr int RUNS = 1;
+  using Raw = typename Decoder<F>::Raw;
+  __device__ __forceinline__ static int unit(int i, int) { return i; }
+  __device__ __forceinline__ static void load(const u8* base, u32 row_off, int i, Raw& r) {
+    Decoder<F>::load(base, row_off, i, r);
+  }
+  __device__ __forceinline__ static void unpack(const Raw& r, Unit (&o)[1]) { Decoder<F>::unpack(r, o[0]); }
+};
+template <> struct Item<FMT_Q4_1> : ItemOne<FMT_Q4_1> {};
+template <> struct Item<FMT_Q5_0> : ItemOne<FMT_Q5_0> {};
+template <> struct Item<FMT_Q5_1> : ItemOne<FMT_Q5_1> {};
+template <> struct Item<FMT_Q2_K> : ItemOne<FMT_Q2_K> {};
+template <> struct Item<FMT_Q3_K> : ItemOne<FMT_Q3_K> {};
+template <> struct Item<FMT_Q5_K> : ItemOne<FMT_Q5_K> {};
 
 template <> struct Item<FMT_Q4_K> {
   static constexpr int RUNS = 2;

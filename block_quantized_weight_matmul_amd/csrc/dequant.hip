@@ -46,6 +46,12 @@ hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f
     case FMT_Q4_K: k = k_dequant<FMT_Q4_K>; break;
     case FMT_Q6_K: k = k_dequant<FMT_Q6_K>; break;
     case FMT_A4G64: k = k_dequant<FMT_A4G64>; break;
+    case FMT_Q4_1: k = k_dequant<FMT_Q4_1>; break;
+    case FMT_Q5_0: k = k_dequant<FMT_Q5_0>; break;
+    case FMT_Q5_1: k = k_dequant<FMT_Q5_1>; break;
+    case FMT_Q2_K: k = k_dequant<FMT_Q2_K>; break;
+    case FMT_Q3_K: k = k_dequant<FMT_Q3_K>; break;
+    case FMT_Q5_K: k = k_dequant<FMT_Q5_K>; break;
     default: return hipErrorInvalidValue;
   }
   hipLaunchKernelGGL(k, grid, dim3(256), 0, st, W, m.row_bytes, static_cast<int>(m.M), nU, out, out_f16);

@@ -322,6 +322,182 @@ template <> struct AStage<FMT_A4G64> {
   }
 };
 
+// Q4_1 (unit = block, 20 bytes, 4-byte aligned): weights 16h .. 16h+15 are nibble h of
+// code bytes 0 .. 15; w = d * q + m (one rounding: the fp32-then-fp16 path).
+template <> struct AStage<FMT_Q4_1> {
+  u32 hdr;
+  u32 q[4];
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) hdr = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
+    const u32 bo = row_off + 20u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
+    hdr = ld32(W, bo);
+    ld128_a4(W, bo + 4, q);
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const bool hi = (g & 1) != 0;
+    const float a24 = h2f(hdr) * (hi ? 1048576.0f : 16777216.0f);  // d * 2^24 (/16 high), exact
+    const float b = h2f(hdr >> 16);
+    const u32 mask = hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_sub(q[2 * j] & mask, q[2 * j + 1] & mask, a24, b);
+  }
+};
+
+// The four-byte spread of the top bits of codes 4k .. 4k+3 (bits t .. t+3 of qh), at bit
+// `at` of each byte.
+__device__ __forceinline__ u32 top_bits4(u32 qh, u32 t, u32 at) { return spread4((qh >> t) & 15u) << at; }
+
+// Q5_0 (22-byte blocks, 2-byte aligned): weights 16h + i are nibble h of code byte i with
+// bit 16h + i of qh on top; w = d * (q - 16), exact in fp32, formed in packed fp16.
+template <> struct AStage<FMT_Q5_0> {
+  Bytes16 q;
+  u32 qh0, qh1, qsh;
+  u32 d;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
+    const u32 bo = row_off + 22u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
+    q.load(W, bo + 6);
+    qh0 = ld32(W, (bo + 2) & ~3u);   // the dwords holding qh's first and last byte
+    qh1 = ld32(W, (bo + 5) & ~3u);
+    qsh = ((bo + 2) & 3u) * 8u;
+    d = ld16(W, bo);
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const u32 h = static_cast<u32>(g & 1);
+    const u32 qh = __builtin_amdgcn_alignbit(qh1, qh0, qsh);
+    const half2v dd = bits_h2(d * 0x10001u);
+    const half2v off = half2v{1040, 1040};
+    u32 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = ((q.word(k) >> (4u * h)) & 0x0F0F0F0Fu) | top_bits4(qh, 16u * h + 4u * k, 4u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_pk(c[2 * j], c[2 * j + 1], off, dd);
+  }
+};
+
+// Q5_1 (24-byte blocks, 8-byte aligned): codes as Q5_0; w = d * q + m.
+template <> struct AStage<FMT_Q5_1> {
+  u32 hdr, qh;
+  u32 q[4];
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) hdr = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int nU, int g) {
+    const u32 bo = row_off + 24u * static_cast<u32>(min(u0 + (g >> 1), nU - 1));
+    hdr = ld32(W, bo);
+    qh = ld32(W, bo + 4);
+    ld128_a4(W, bo + 8, q);
+  }
+  __device__ __forceinline__ void operands(int g, half8 (&A)[2]) const {
+    const u32 h = static_cast<u32>(g & 1);
+    const float a24 = h2f(hdr) * 16777216.0f;  // d * 2^24, exact
+    const float b = h2f(hdr >> 16);
+    u32 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = ((q[k] >> (4u * h)) & 0x0F0F0F0Fu) | top_bits4(qh, 16u * h + 4u * k, 4u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_sub(c[2 * j], c[2 * j + 1], a24, b);
+  }
+};
+
+// Q2_K (84-byte super-blocks, 4-byte aligned): the stage is units a0, a0+1 (a0 even) of a
+// super-block; lane group g takes unit a = a0 + g/2, 16-weight sub-block j = 2a + g%2:
+// bits 2(a/2) .. +1 of qs[32(a%2) + 16(g%2) + i]; sc_j, m_j the nibbles of sm[j].
+template <> struct AStage<FMT_Q2_K> {
+  u32 hdr, sm, smsh;
+  u32 q[4];
+  int a;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) hdr = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 so = row_off + 84u * static_cast<u32>(u0 >> 3);
+    a = (u0 & 7) + (g >> 1);
+    const u32 jb = so + 4u + 2u * static_cast<u32>(a) + static_cast<u32>(g & 1);  // byte sm[j]
+    hdr = ld32(W, so);
+    sm = ld32(W, jb & ~3u);
+    smsh = (jb & 3u) * 8u;
+    ld128_a4(W, so + 20u + 32u * static_cast<u32>(a & 1) + 16u * static_cast<u32>(g & 1), q);
+  }
+  __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
+    const u32 sh = 2u * static_cast<u32>(a >> 1);
+    const u32 f = sm >> smsh;
+    const float a24 = h2f(hdr) * static_cast<float>(f & 15u) * 16777216.0f;  // exact
+    const float b = -(h2f(hdr >> 16) * static_cast<float>((f >> 4) & 15u));   // exact
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      A[j] = weights_sub((q[2 * j] >> sh) & 0x03030303u, (q[2 * j + 1] >> sh) & 0x03030303u, a24, b);
+  }
+};
+
+// Q3_K (110-byte super-blocks, 2-byte aligned): lane group g takes unit a = a0 + g/2,
+// sub-block j = 2a + g%2: low bits 2(a/2) .. +1 of ql[32(a%2) + 16(g%2) + i], top bit a
+// of qh[16(g%2) + i], scale field j of the 6-bit string.  (q - 4) * d * (s - 32) is exact
+// in fp32, so the fused fma-to-fp16 rounds it once, as the fp32-then-fp16 path would.
+template <> struct AStage<FMT_Q3_K> {
+  Bytes16 ql, qh;
+  u32 d, s0, s1, ssh;
+  int a;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) d = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 so = row_off + 110u * static_cast<u32>(u0 >> 3);
+    a = (u0 & 7) + (g >> 1);
+    const u32 h = static_cast<u32>(g & 1);
+    const u32 j = 2u * static_cast<u32>(a) + h;
+    ql.load(W, so + 14u + 32u * static_cast<u32>(a & 1) + 16u * h);
+    qh.load(W, so + 78u + 16u * h);
+    d = ld16(W, so);
+    // the two bytes holding field j (bits 6j .. 6j+5 of the string at so + 2)
+    const u32 fb = so + 2u + ((6u * j) >> 3);
+    s0 = ld32(W, fb & ~3u);
+    s1 = ld32(W, (fb + 1u) & ~3u);
+    ssh = (fb & 3u) * 8u + ((6u * j) & 7u);
+  }
+  __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
+    const u32 sh = 2u * static_cast<u32>(a >> 1);
+    const u32 hb = static_cast<u32>(a);
+    const u32 f = (__builtin_amdgcn_alignbit(s1, s0, ssh & 24u) >> (ssh & 7u)) & 63u;
+    const float ac = h2f(d) * static_cast<float>(static_cast<int>(f) - 32);  // exact
+    u32 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      c[k] = ((ql.word(k) >> sh) & 0x03030303u) | (((qh.word(k) >> hb) & 0x01010101u) << 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) A[j] = weights_mix<true>(c[2 * j], c[2 * j + 1], half2v{1028, 1028}, ac, 0.0f);
+  }
+};
+
+// Q5_K (176-byte super-blocks, 16-byte aligned): lane group g takes sub-block a = a0 + g/2,
+// weights 16(g%2) .. +15: nibble a%2 of qs[32(a/2) + 16(g%2) + i] with bit a of
+// qh[16(g%2) + i] on top; sc_a, m_a as Q4_K.
+template <> struct AStage<FMT_Q5_K> {
+  u32 h[4];
+  u32 q[4];
+  u32 qh[4];
+  int a;
+  __device__ __forceinline__ void zero_second(int g) { if (g >= 2) h[0] = 0; }
+  __device__ __forceinline__ void load(const u8* W, u32 row_off, int u0, int, int g) {
+    const u32 so = row_off + 176u * static_cast<u32>(u0 >> 3);
+    a = (u0 & 7) + (g >> 1);
+    const u32 hh = 16u * static_cast<u32>(g & 1);
+    const uint4 hv = ld128(W, so);
+    const uint4 qhv = ld128(W, so + 16u + hh);
+    const uint4 qv = ld128(W, so + 48u + 32u * static_cast<u32>(a >> 1) + hh);
+    h[0] = hv.x; h[1] = hv.y; h[2] = hv.z; h[3] = hv.w;
+    qh[0] = qhv.x; qh[1] = qhv.y; qh[2] = qhv.z; qh[3] = qhv.w;
+    q[0] = qv.x; q[1] = qv.y; q[2] = qv.z; q[3] = qv.w;
+  }
+  __device__ __forceinline__ void operands(int, half8 (&A)[2]) const {
+    const u32 j = static_cast<u32>(a);
+    const u32 sc = six_bit_field(h[1], h[2], h[3], j);
+    const u32 m = six_bit_field(h[1], h[2], h[3], 8u + j);
+    const float a24 = h2f(h[0]) * static_cast<float>(sc) * 16777216.0f;  // exact
+    const float b = -(h2f(h[0] >> 16) * static_cast<float>(m));           // exact
+    const u32 sh = 4u * (j & 1u);
+    u32 c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c[k] = ((q[k] >> sh) & 0x0F0F0F0Fu) | (((qh[k] >> j) & 0x01010101u) << 4);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) A[jj] = weights_sub(c[2 * jj], c[2 * jj + 1], a24, b);
+  }
+};
+
 // ---------------------------------------------------------------------------------------------
 // Activations of one stage: K [k0, k0 + 64) of tokens [tok0, tok0 + TT), as TT*8
 // chunks of 8 values spread over the 256 threads; held in registers from load
@@ -457,7 +633,9 @@ __device__ __forceinline__ void stage_barrier() {
 constexpr int kNoVmemCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0080 | 0x0100 | 0x0200 | 0x0400;
 
 // Approximate VALU instructions of one row block's A-operand decode per stage.
-template <int F> constexpr int kDecodeValu = F == FMT_Q6_K ? 90 : (F == FMT_Q4_K ? 64 : 48);
+template <int F> constexpr int kDecodeValu =
+    F == FMT_Q6_K || F == FMT_Q3_K || F == FMT_Q5_K ? 90
+    : (F == FMT_Q4_K || F == FMT_Q5_0 || F == FMT_Q5_1 || F == FMT_Q2_K ? 64 : 48);
 
 // Instruction order asked of the scheduler for a steady full stage: the first
 // two token blocks' B operands read from LDS up front, then each MFMA followed
@@ -911,7 +1089,7 @@ typedef void (*GemmKernel)(GemmArgs);
 // 64 x 256 and 128 x 256 with fp16 activations, one workgroup per CU.
 constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
   if (TT == 256) return F == FMT_Q6_K && xf16 && (RB == 1 || RB == 2);
-  if (RB == 2) return TT == 128 && F != FMT_Q6_K && xf16;
+  if (RB == 2) return TT == 128 && F != FMT_Q6_K && F != FMT_Q3_K && xf16;  // (Q3_K x 128 rows spills)
   return TT == 32 || TT == 64 || TT == 128;
 }
 
@@ -937,7 +1115,11 @@ GemmKernel pick(int RB, int TT, bool xf16) {
 // flight per workgroup; Q6_K's decode would not fit the registers), 64 rows at
 // the 128-token one
 template <int F, int TT>
-constexpr int id_rows_blocks() { return TT == 64 && F != FMT_Q6_K ? 2 : 1; }
+constexpr int id_rows_blocks() { return TT == 64 && F != FMT_Q6_K && F != FMT_Q3_K && F != FMT_Q5_0 ? 2 : 1; }
+
+// the formats whose expert-indexed kernel takes the 64-token super-tile only (their
+// decode state spills the registers at 128 tokens)
+constexpr bool id_narrow_tile(int F) { return F == FMT_Q6_K || F == FMT_Q3_K; }
 
 template <int F, int TT>
 GemmKernel pick_id(bool xf16) {
@@ -951,7 +1133,7 @@ GemmKernel pick_id(bool xf16) {
 // and 160 KB of LDS over its LDS size; 2 when the attributes are unavailable,
 // at most 3.  Memoised per (format, super-tile, activation type).
 int id_resident_per_cu(int fmt, int TT, bool xf16, GemmKernel k) {
-  static std::atomic<int> memo[5][2][2];
+  static std::atomic<int> memo[kNumFormats][2][2];
   std::atomic<int>& slot = memo[fmt][TT == 128 ? 1 : 0][xf16 ? 1 : 0];
   int n = slot.load(std::memory_order_relaxed);
   if (n > 0) return n;
@@ -1086,7 +1268,7 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
   // once, their pairs gathered once): 128 experts at 1024 tokens, 64 pairs each
   // on average, run in 210 us at 128 against 322 at 64
   const bool xf16 = x_f16 != 0;
-  const int TT = P >= 48 * m.n_experts && m.fmt != FMT_Q6_K ? 128 : 64;  // (Q6_K x 128 spills)
+  const int TT = P >= 48 * m.n_experts && !id_narrow_tile(m.fmt) ? 128 : 64;  // (Q6_K, Q3_K x 128 spill)
   GemmKernel k = nullptr;
   switch (m.fmt) {
     case FMT_Q4_0: k = TT == 128 ? pick_id<FMT_Q4_0, 128>(xf16) : pick_id<FMT_Q4_0, 64>(xf16); break;
@@ -1094,10 +1276,16 @@ hipError_t launch_gemm_id(const MatDesc& m, const void* x, int x_f16, int64_t N,
     case FMT_Q4_K: k = TT == 128 ? pick_id<FMT_Q4_K, 128>(xf16) : pick_id<FMT_Q4_K, 64>(xf16); break;
     case FMT_Q6_K: k = pick_id<FMT_Q6_K, 64>(xf16); break;
     case FMT_A4G64: k = TT == 128 ? pick_id<FMT_A4G64, 128>(xf16) : pick_id<FMT_A4G64, 64>(xf16); break;
+    case FMT_Q4_1: k = TT == 128 ? pick_id<FMT_Q4_1, 128>(xf16) : pick_id<FMT_Q4_1, 64>(xf16); break;
+    case FMT_Q5_0: k = TT == 128 ? pick_id<FMT_Q5_0, 128>(xf16) : pick_id<FMT_Q5_0, 64>(xf16); break;
+    case FMT_Q5_1: k = TT == 128 ? pick_id<FMT_Q5_1, 128>(xf16) : pick_id<FMT_Q5_1, 64>(xf16); break;
+    case FMT_Q2_K: k = TT == 128 ? pick_id<FMT_Q2_K, 128>(xf16) : pick_id<FMT_Q2_K, 64>(xf16); break;
+    case FMT_Q3_K: k = pick_id<FMT_Q3_K, 64>(xf16); break;
+    case FMT_Q5_K: k = TT == 128 ? pick_id<FMT_Q5_K, 128>(xf16) : pick_id<FMT_Q5_K, 64>(xf16); break;
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;
-  const int RB = TT == 64 && m.fmt != FMT_Q6_K ? 2 : 1;  // as id_rows_blocks
+  const int RB = TT == 64 && m.fmt != FMT_Q6_K && m.fmt != FMT_Q3_K && m.fmt != FMT_Q5_0 ? 2 : 1;  // as id_rows_blocks
   // as many workgroups over the ranks as the CUs hold at once (from the
   // kernel's registers and LDS: two for each of these kernels), each taking
   // every groups-th row tile of its expert (the routing is done once per
@@ -1207,6 +1395,12 @@ hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, fl
     case FMT_Q4_K: k = pick<FMT_Q4_K>(RB, TT, xf16); break;
     case FMT_Q6_K: k = pick<FMT_Q6_K>(RB, TT, xf16); break;
     case FMT_A4G64: k = pick<FMT_A4G64>(RB, TT, xf16); break;
+    case FMT_Q4_1: k = pick<FMT_Q4_1>(RB, TT, xf16); break;
+    case FMT_Q5_0: k = pick<FMT_Q5_0>(RB, TT, xf16); break;
+    case FMT_Q5_1: k = pick<FMT_Q5_1>(RB, TT, xf16); break;
+    case FMT_Q2_K: k = pick<FMT_Q2_K>(RB, TT, xf16); break;
+    case FMT_Q3_K: k = pick<FMT_Q3_K>(RB, TT, xf16); break;
+    case FMT_Q5_K: k = pick<FMT_Q5_K>(RB, TT, xf16); break;
     default: return hipErrorInvalidValue;
   }
   if (!k) return hipErrorInvalidValue;

@@ -376,10 +376,11 @@ constexpr int kTokPerUnit = 4;
 
 // Items per thread per batch.  A thread holds two batches: while it decodes one,
 // the loads of the next are in flight.
-// Q6_K items carry 34 raw bytes and two scale pairs, so it holds fewer.
+// Q6_K items carry 34 raw bytes and two scale pairs (Q3_K and Q5_K units 70-80 bytes),
+// so they hold fewer.
 template <int F>
 constexpr int ipt_max(int NB) {
-  if (F == FMT_Q6_K) return NB <= 2 ? 2 : 1;
+  if (F == FMT_Q6_K || F == FMT_Q3_K || F == FMT_Q5_K) return NB <= 2 ? 2 : 1;
   return NB <= 2 ? 3 : 2;
 }
 
@@ -1158,39 +1159,35 @@ constexpr void fill_multi(GemvKernel (&t)[2], GemvKernel (&ti)[2]) {
 }
 
 struct Tables {
-  GemvKernel dense[5][kNumBuckets];
-  GemvKernel id[5][kIdBuckets];
-  GemvKernel one[5][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
-  int one_regs[5][2][3];    // their VGPRs per lane (512 when unknown)
-  GemvKernel multi[5][2];  // [format][fp16 activations], one row per thread
-  GemvKernel multi_id[5][2];
+  GemvKernel dense[kNumFormats][kNumBuckets];
+  GemvKernel id[kNumFormats][kIdBuckets];
+  GemvKernel one[kNumFormats][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
+  int one_regs[kNumFormats][2][3];    // their VGPRs per lane (512 when unknown)
+  GemvKernel multi[kNumFormats][2];   // [format][fp16 activations], one row per thread
+  GemvKernel multi_id[kNumFormats][2];
   GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
+  template <int F>
+  void fill_format() {
+    fill_multi<F>(multi[F], multi_id[F]);
+    fill_one<F>(one[F]);
+    fill_dense<F>(dense[F], std::make_integer_sequence<int, kNumBuckets>{});
+    fill_id<F>(id[F], std::make_integer_sequence<int, kIdBuckets>{});
+  }
   Tables() {
     narrow_id[0] = k_gemv_id_narrow<false>;
     narrow_id[1] = k_gemv_id_narrow<true>;
-    fill_multi<FMT_Q4_0>(multi[FMT_Q4_0], multi_id[FMT_Q4_0]);
-    fill_multi<FMT_Q8_0>(multi[FMT_Q8_0], multi_id[FMT_Q8_0]);
-    fill_multi<FMT_Q4_K>(multi[FMT_Q4_K], multi_id[FMT_Q4_K]);
-    fill_multi<FMT_Q6_K>(multi[FMT_Q6_K], multi_id[FMT_Q6_K]);
-    fill_multi<FMT_A4G64>(multi[FMT_A4G64], multi_id[FMT_A4G64]);
-    fill_one<FMT_Q4_0>(one[FMT_Q4_0]);
-    fill_one<FMT_Q8_0>(one[FMT_Q8_0]);
-    fill_one<FMT_Q4_K>(one[FMT_Q4_K]);
-    fill_one<FMT_Q6_K>(one[FMT_Q6_K]);
-    fill_one<FMT_A4G64>(one[FMT_A4G64]);
-    auto seq = std::make_integer_sequence<int, kNumBuckets>{};
-    fill_dense<FMT_Q4_0>(dense[FMT_Q4_0], seq);
-    fill_dense<FMT_Q8_0>(dense[FMT_Q8_0], seq);
-    fill_dense<FMT_Q4_K>(dense[FMT_Q4_K], seq);
-    fill_dense<FMT_Q6_K>(dense[FMT_Q6_K], seq);
-    fill_dense<FMT_A4G64>(dense[FMT_A4G64], seq);
-    auto idseq = std::make_integer_sequence<int, kIdBuckets>{};
-    fill_id<FMT_Q4_0>(id[FMT_Q4_0], idseq);
-    fill_id<FMT_Q8_0>(id[FMT_Q8_0], idseq);
-    fill_id<FMT_Q4_K>(id[FMT_Q4_K], idseq);
-    fill_id<FMT_Q6_K>(id[FMT_Q6_K], idseq);
-    fill_id<FMT_A4G64>(id[FMT_A4G64], idseq);
-    for (int f = 0; f < 5; ++f)
+    fill_format<FMT_Q4_0>();
+    fill_format<FMT_Q8_0>();
+    fill_format<FMT_Q4_K>();
+    fill_format<FMT_Q6_K>();
+    fill_format<FMT_A4G64>();
+    fill_format<FMT_Q4_1>();
+    fill_format<FMT_Q5_0>();
+    fill_format<FMT_Q5_1>();
+    fill_format<FMT_Q2_K>();
+    fill_format<FMT_Q3_K>();
+    fill_format<FMT_Q5_K>();
+    for (int f = 0; f < kNumFormats; ++f)
       for (int h = 0; h < 2; ++h)
         for (int r = 0; r < 3; ++r) {
           hipFuncAttributes at{};
@@ -1240,7 +1237,7 @@ Shape make_shape(int M, int nU, int runs, int NB, int RW, int max_threads = 512)
 }  // namespace
 
 // Runs (32-weight units) per work item of each format.
-constexpr int kRuns[5] = {1, 1, 2, 2, 2};
+constexpr int kRuns[kNumFormats] = {1, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1};
 
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t st) {
   const int cus = m.cus;

@@ -63,6 +63,26 @@ typedef struct ihipStream_t *qmm_stream_t;
  *  QMM_A4G64  64 weights / 36 B: [0,2) scale | [2,4) bias | [4,36) qs[32]; weight i =
  *             low nibble of qs[i], weight i+32 = high nibble.  w = scale * q + bias.
  *
+ * The other types the candle pull request lists (section "What changes"); the
+ * pages give no formula for them, so they are read from their names ("_0": a
+ * scale times a zero-centred code, "_1": a scale and a minimum, K-quants:
+ * 256-weight super-blocks with per-sub-block scales and minimums):
+ *  QMM_Q4_1   32 weights / 20 B: [0,2) d | [2,4) m | [4,20) qs[16] as Q4_0.  w = d * q + m.
+ *  QMM_Q5_0   32 weights / 22 B: [0,2) d | [2,6) qh, 32-bit little-endian, bit i the top
+ *             (fifth) bit of weight i | [6,22) qs[16], low nibbles as Q4_0.  w = d * (q - 16).
+ *  QMM_Q5_1   32 weights / 24 B: [0,2) d | [2,4) m | [4,8) qh | [8,24) qs[16] as Q5_0.
+ *             w = d * q + m.
+ *  QMM_Q2_K   256 weights / 84 B: [0,2) d | [2,4) dmin | [4,20) sm[16]: sc_j low nibble,
+ *             m_j high nibble of sm[j] | [20,84) qs[64]: weight i is bits 2(i/64)..+1 of
+ *             qs[i % 64].  w = d * sc_j * q - dmin * m_j with j = weight / 16.
+ *  QMM_Q3_K   256 weights / 110 B: [0,2) d | [2,14) 96-bit string of sixteen 6-bit s_j |
+ *             [14,78) ql[64]: low two bits of weight i are bits 2(i/64)..+1 of ql[i % 64] |
+ *             [78,110) qh[32]: top bit of weight i is bit i/32 of qh[i % 32].
+ *             w = d * (s_j - 32) * (q - 4) with j = weight / 16.
+ *  QMM_Q5_K   256 weights / 176 B: [0,2) d | [2,4) dmin | [4,16) sc/m string as Q4_K |
+ *             [16,48) qh[32]: top bit of weight i is bit i/32 of qh[i % 32] | [48,176)
+ *             qs[128], low nibbles as Q4_K.  w = d * sc_j * q - dmin * m_j, j = weight / 32.
+ *
  * Every product in these formulas is exact in fp32, so the dequantized weight is
  * the fp32 round-to-nearest-even of the formula's exact value.
  */
@@ -71,7 +91,13 @@ typedef enum {
   QMM_Q8_0 = 1,
   QMM_Q4_K = 2,
   QMM_Q6_K = 3,
-  QMM_A4G64 = 4
+  QMM_A4G64 = 4,
+  QMM_Q4_1 = 5,
+  QMM_Q5_0 = 6,
+  QMM_Q5_1 = 7,
+  QMM_Q2_K = 8,
+  QMM_Q3_K = 9,
+  QMM_Q5_K = 10
 } qmm_type;
 
 /* Element type of activations (x) and of qmm_dequantize's output. */
@@ -110,7 +136,8 @@ typedef struct qmm_matrix qmm_matrix;
  *              the handle and stay unmodified.
  *   n_experts  1 for a plain matrix; E for the stacked experts of qmm_gemm_id.
  *   M, K       rows and reduction length; K a positive multiple of the block's
- *              weight count (32, 32, 256, 256, 64); M >= 1; one matrix
+ *              weight count (32 for the 32-weight types, 64 for A4G64, 256 for the
+ *              K-quants); M >= 1; one matrix
  *              (M * row_bytes(K)) below 4 GiB.
  * Checks that the current device is gfx950 (QMM_E_DEVICE otherwise) and records it.
  */
@@ -259,7 +286,7 @@ qmm_status qmm_dequantize(const qmm_matrix *h, int64_t expert, void *out, qmm_dt
 
 /*
  * qmm_quantize -- encode fp32 weights into blocks of `type` on the GPU (the step
- * before the path).  The pages quantize random weights to each type before
+ * before the path), for Q4_0, Q8_0, Q4_K, Q6_K and A4G64 (QMM_E_TYPE for the others).  The pages quantize random weights to each type before
  * timing (candle pull request above, section "Numbers") but print no quantizer;
  * these are this library's closed forms, evaluated in fp64 on the exact fp32
  * inputs in the order written.  rne/up/down round to the nearest fp16 (ties to

@@ -7,7 +7,12 @@ import oracle
 from qmm_synth import quantize, workloads
 
 DEV = "cuda"
-FORMATS = ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64"]
+FORMATS = ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64", "q4_1", "q5_0", "q5_1", "q2_k", "q3_k", "q5_k"]
+# byte offsets of each format's fp16 scale fields (kept finite in random-byte blocks)
+SCALE_OFFSETS = {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2], "q4_1": [0, 2],
+                 "q5_0": [0], "q5_1": [0, 2], "q2_k": [0, 2], "q3_k": [0], "q5_k": [0, 2]}
+# the formats the GPU quantizer (and the oracle's reference quantizer) encode
+QUANT_FORMATS = ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64"]
 
 
 def to_dev(a):
@@ -47,5 +52,5 @@ def count_differences(a, b):
     return int(np.count_nonzero(a.view(np.uint32) != b.view(np.uint32)))
 
 
-__all__ = ["DEV", "FORMATS", "to_dev", "to_host", "make_matrix", "assert_within", "count_differences",
+__all__ = ["DEV", "FORMATS", "QUANT_FORMATS", "SCALE_OFFSETS", "to_dev", "to_host", "make_matrix", "assert_within", "count_differences",
            "oracle", "quantize", "workloads"]

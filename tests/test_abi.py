@@ -58,7 +58,7 @@ def test_row_bytes_and_blocks():
         assert L.lib.qmm_row_bytes(t, bw + 16) == 0
         assert L.lib.qmm_row_bytes(t, 0) == 0
         assert L.lib.qmm_row_bytes(t, -bw) == 0
-    assert L.lib.qmm_row_bytes(7, 256) == 0
+    assert L.lib.qmm_row_bytes(11, 256) == 0 and L.lib.qmm_row_bytes(-1, 256) == 0
     assert L.lib.qmm_block_weights(-1) == 0
 
 
@@ -76,7 +76,7 @@ def test_argument_errors_before_device():
     buf = ctypes.create_string_buffer(4096 + 32)
     base = (ctypes.addressof(buf) + 15) & ~15
     assert lib.qmm_create(None, 0, ctypes.c_void_p(base), 1, 4, 32) == -1
-    assert lib.qmm_create(ctypes.byref(h), 9, ctypes.c_void_p(base), 1, 4, 32) == -2
+    assert lib.qmm_create(ctypes.byref(h), 11, ctypes.c_void_p(base), 1, 4, 32) == -2
     assert lib.qmm_create(ctypes.byref(h), 0, None, 1, 4, 32) == -1
     assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base + 2), 1, 4, 32) == -4
     assert lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(base), 1, 4, 48) == -3
@@ -95,7 +95,7 @@ def test_argument_errors_before_device():
 def test_binding_refuses_bad_type_name():
     import block_quantized_weight_matmul_amd as q
     with pytest.raises(ValueError):
-        q.qmm_row_bytes("q5_1", 256)
+        q.qmm_row_bytes("q7_0", 256)
     assert q.qmm_row_bytes("q6_k", 256) == 210
 
 

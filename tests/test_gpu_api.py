@@ -30,7 +30,7 @@ def test_create_errors_on_device_pointers():
     h = ctypes.c_void_p()
     p = blob.data_ptr()
     assert L.lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(p + 2), 1, M, K) == -4
-    assert L.lib.qmm_create(ctypes.byref(h), 5, ctypes.c_void_p(p), 1, M, K) == -2
+    assert L.lib.qmm_create(ctypes.byref(h), 11, ctypes.c_void_p(p), 1, M, K) == -2
     assert L.lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(p), 1, M, 40) == -3
     assert L.lib.qmm_create(ctypes.byref(h), 0, ctypes.c_void_p(p), 1, M, K) == 0
     assert L.lib.qmm_destroy(h) == 0

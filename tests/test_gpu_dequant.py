@@ -11,7 +11,7 @@ import torch
 
 import block_quantized_weight_matmul_amd as q
 from tests.golden_io import read_blocks
-from tests.gpu_helpers import FORMATS, make_matrix, oracle, to_dev, to_host
+from tests.gpu_helpers import FORMATS, SCALE_OFFSETS, make_matrix, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_random_bytes(fmt):
     g = np.random.default_rng([32, bb])
     M, nblk = 37, 5
     blk = g.integers(0, 256, size=(M * nblk, bb), dtype=np.uint8)
-    for off in {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2]}[fmt]:
+    for off in SCALE_OFFSETS[fmt]:
         blk[:, off + 1] &= 0xBF      # exponent field <= 15: finite, either sign
     _check(fmt, blk.reshape(-1), M, nblk * bw)
 

@@ -24,15 +24,15 @@ import torch
 
 import block_quantized_weight_matmul_amd as q
 from tests.golden_io import read_blocks
-from tests.gpu_helpers import FORMATS, oracle, to_dev, to_host
+from tests.gpu_helpers import FORMATS, SCALE_OFFSETS, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
 # blocks per row: K = 512 for every format (Q4_0 rows of 16 blocks take the narrow
 # expert-indexed kernel), 72 rows (a ragged second 64-row tile), 3 experts
-BLOCKS_PER_ROW = {"q4_0": 16, "q8_0": 16, "q4_k": 2, "q6_k": 2, "a4g64": 8}
+BLOCKS_PER_ROW = {"q4_0": 16, "q8_0": 16, "q4_k": 2, "q6_k": 2, "a4g64": 8, "q4_1": 16, "q5_0": 16, "q5_1": 16,
+                  "q2_k": 2, "q3_k": 2, "q5_k": 2}
 M, E = 72, 3
-SCALE_OFFSETS = {"q4_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "a4g64": [0, 2]}
 
 
 def block_pool(fmt):
@@ -90,7 +90,8 @@ def test_pool_holds_the_edge_cases():
         d = block_pool(fmt)[:, 0:2].copy().view(np.float16)[:, 0]
         assert ((d != 0) & (np.abs(d.astype(np.float32)) < 2.0 ** -14)).any(), fmt
     names = [c["name"] for c in read_blocks()]
-    assert "q4_k_fp16_staging_double_rounding" in names and "a4g64_fp16_staging_double_rounding" in names
+    for fmt in ("q4_k", "a4g64", "q4_1", "q5_1", "q2_k", "q5_k"):
+        assert f"{fmt}_fp16_staging_double_rounding" in names
 
 
 @pytest.mark.parametrize("xdt", [np.float32, np.float16])

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import block_quantized_weight_matmul_amd as q
-from tests.gpu_helpers import FORMATS, oracle, to_dev, to_host
+from tests.gpu_helpers import FORMATS, QUANT_FORMATS, oracle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def _weights(fmt, dist, M, K, seed):
     return w.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", QUANT_FORMATS)
 @pytest.mark.parametrize("dist", ["normal", "wide", "spiky", "edges"])
 def test_quantize_matches_oracle(fmt, dist):
     bw = oracle.block_weights(fmt)
@@ -47,7 +47,7 @@ def test_quantize_matches_oracle(fmt, dist):
     assert bad.size == 0, f"{fmt} {dist}: {bad.size} bytes differ, first at byte {bad[:1]} (block {bad[:1] // oracle.block_bytes(fmt)})"
 
 
-@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("fmt", QUANT_FORMATS)
 def test_quantized_blocks_feed_the_path(fmt):
     """Blocks made on the GPU go straight into a handle; the matrix-vector result
     matches the oracle on the oracle's own encoding of the same weights."""
@@ -78,3 +78,13 @@ def test_quantize_errors_and_empty():
     assert L.lib.qmm_quantize(0, None, 2, 64, bp, s) == -1
     assert L.lib.qmm_quantize(0, wp, 2, 64, ctypes.c_void_p(b.data_ptr() + 2), s) == -4
     assert L.lib.qmm_quantize(0, wp, 0, 64, bp, s) == 0                  # M = 0: nothing to do
+
+
+@pytest.mark.parametrize("fmt", [f for f in FORMATS if f not in QUANT_FORMATS])
+def test_quantize_refuses_types_without_a_quantizer(fmt):
+    from block_quantized_weight_matmul_amd import _lib as L
+    w = torch.zeros((2, 256), device="cuda")
+    blocks = torch.zeros(2 * oracle.row_bytes(fmt, 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_quantize(fmt, w, 2, 256, blocks)
+    assert e.value.status == -2
