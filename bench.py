@@ -83,6 +83,7 @@ def parse():
                         "of --copy-probe (no GPU needed)")
     p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
                    help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
+    p.add_argument("--formats-only", action="store_true", help="only run the per-format sweep")
     p.add_argument("--moe-only", default=None, metavar="N[,N...]",
                    help="only time the expert-indexed paths at these token counts: the matvec up to 32 "
                         "tokens, the matrix-core path above (for profiling)")
@@ -485,6 +486,44 @@ def extra_prefill_batch(torch, q, W, args):
             "results": res}
 
 
+def extra_formats(torch, q, W, args):
+    """Every block format on one 4096 x 4096 matrix: the one-token matrix-vector call
+    (quantized-weight GB/s) and the 512-token matrix-core call (TFLOP/s), weights rotated
+    over > 1 GiB of copies per sample."""
+    res = []
+    for fmt in W.ALL_FORMATS:
+        d = W.format_sweep_weights(fmt)
+        rot = Rotation(torch, [d["blob"]])
+        hs = [q.QMatrix(rot.slice(c, 0), fmt, d["M"], d["K"]) for c in range(rot.copies)]
+        row = {"fmt": fmt, "weight_bytes": int(d["blob"].size), "bits_per_weight": d["blob"].size * 8 / (d["M"] * d["K"]),
+               "copies": rot.copies}
+        x1 = torch.from_numpy(W.format_sweep_x(1)).to("cuda")
+        y1 = torch.empty((1, d["M"]), device="cuda")
+        g = capture(torch, lambda: [q.qmm_gemv(h.handle, x1, 1, y1) for h in hs])
+        us = time_graph(torch, g, args.rounds) * 1e3 / len(hs)
+        del g
+        row["gemv_n1_us"] = us
+        row["gemv_n1_weight_gbs"] = d["blob"].size / (us * 1e-6) / 1e9
+        row["gemv_n1_frac_hbm"] = row["gemv_n1_weight_gbs"] / HBM_PEAK_GBS
+        n = 512
+        xn = torch.from_numpy(W.format_sweep_x(n)).to("cuda")
+        yn = torch.empty((n, d["M"]), device="cuda")
+        nb = q.qmm_gemm_workspace_bytes(hs[0].handle, n)
+        ws = torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None
+        g = capture(torch, lambda: [q.qmm_gemm_ws(h.handle, xn, n, yn, 0, ws) for h in hs])
+        us = time_graph(torch, g, max(2, args.rounds // 2)) * 1e3 / len(hs)
+        del g
+        row["gemm_n512_us"] = us
+        row["gemm_n512_tflops"] = 2.0 * d["M"] * d["K"] * n / (us * 1e-6) / 1e12
+        row["gemm_n512_frac_mfma"] = row["gemm_n512_tflops"] / MFMA_F16_PEAK_TFLOPS
+        res.append(row)
+        del hs, rot, x1, y1, xn, yn, ws
+        torch.cuda.empty_cache()
+    return {"workload": "every block format, 4096 x 4096, N(0,0.02^2) weights; 1 fp32 token (qmm_gemv) and "
+                        "512 fp16 tokens (qmm_gemm_ws, auto tile); weights rotated over >1 GiB per sample",
+            "results": res}
+
+
 def extra_moe(torch, q, W, args):
     t0 = time.time()
     stack = W.moe_stack()
@@ -720,6 +759,9 @@ def main():
     if args.moe_only:
         print(json.dumps({"expert_matvec": extra_moe(torch, q, W, args)}), flush=True)
         return
+    if args.formats_only:
+        print(json.dumps({"formats": extra_formats(torch, q, W, args)}), flush=True)
+        return
     if args.prefill_only:
         mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
         print(json.dumps({"prefill_gemm": extra_prefill(torch, q, W, mats, args)}), flush=True)
@@ -784,6 +826,7 @@ def main():
                          ("small_decode_a4g64", lambda: extra_small_decode(torch, q, W, args)),
                          ("prefill_gemm", lambda: extra_prefill(torch, q, W, mats, args)),
                          ("prefill_batch_2x65", lambda: extra_prefill_batch(torch, q, W, args)),
+                         ("formats", lambda: extra_formats(torch, q, W, args)),
                          ("expert_matvec", lambda: extra_moe(torch, q, W, args)),
                          ("quantize", lambda: extra_quantize(torch, q, W, mats, args))):
             t0 = time.time()

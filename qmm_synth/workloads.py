@@ -43,6 +43,10 @@ SMALL_DECODE_TOKENS = [1, 2, 4, 8, 16]
 
 PREFILL_TOKENS = [7, 33, 64, 96, 130, 512, 2048]
 FORMAT_ORDER = ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64"]
+# every block format, for the per-format sweep (one 4096 x 4096 matrix each)
+ALL_FORMATS = FORMAT_ORDER + ["q4_1", "q5_0", "q5_1", "q2_k", "q3_k", "q5_k"]
+SWEEP_M = SWEEP_K = 4096
+SWEEP_TOKENS = [1, 512]
 
 # Expert-indexed narrow-K matvec: E experts of M x K in Q4_0, S ids per token.
 MOE_EXPERTS, MOE_M, MOE_K, MOE_SLOTS = 128, 4096, 512, 8
@@ -149,3 +153,15 @@ def generic(fmt, M, K, n, seed, xdtype=np.float32):
     g = rng(seed)
     w = draw_weights(g, M, K)
     return {"fmt": fmt, "M": M, "K": K, "blob": quantize(fmt, w), "x": draw_x(g, (n, K), xdtype)}
+
+
+# --- per-format sweep: one 4096 x 4096 matrix per block format ------------------------------
+def format_sweep_weights(fmt):
+    """Weights N(0, 0.02^2) of a 4096 x 4096 matrix encoded as `fmt`, seed [5, format index]."""
+    w = draw_weights(rng([5, ALL_FORMATS.index(fmt)]), SWEEP_M, SWEEP_K)
+    return {"fmt": fmt, "M": SWEEP_M, "K": SWEEP_K, "blob": quantize(fmt, w)}
+
+
+def format_sweep_x(n):
+    """n tokens of activations for the sweep: fp32 for the matrix-vector call, fp16 otherwise."""
+    return draw_x(rng([5, 99, n]), (n, SWEEP_K), np.float32 if n == 1 else np.float16)
