@@ -598,14 +598,16 @@ __device__ __forceinline__ void clear_k_tail(_Float16* sx, int tid, int k_end) {
 
 // The stage's products: B operands of token block t from LDS (lane: token
 // 16t + l % 16, k-chunks 2g and 2g+1 at offsets o0 and o1 of the block's first
-// row), each used by the wave's RB row blocks.  FULL: all NTB blocks; else only
-// blocks t < ntb (the last super-tile, filled to whole T-token tiles).
-template <bool FULL, int RB, int NTB>
+// row), each used by the wave's RB row blocks, for the NA token blocks the
+// super-tile computes (all NTB, or fewer in a last super-tile filled to whole
+// T-token tiles).
+template <int RB, int NTB, int NA>
 __device__ __forceinline__ void stage_products(const _Float16* sx, int o0, int o1, const half8 (&A)[RB][2],
-                                               floatx4 (&acc)[RB][NTB], int ntb) {
+                                               floatx4 (&acc)[RB][NTB]) {
+  static_assert(NA <= NTB, "active blocks");
 #pragma unroll
-  for (int t = 0; t < NTB; ++t) {
-    if (FULL || t < ntb) {
+  for (int t = 0; t < NA; ++t) {
+    {
       const half8 B0 = *reinterpret_cast<const half8*>(sx + 16 * t * kKS + o0);
       const half8 B1 = *reinterpret_cast<const half8*>(sx + 16 * t * kKS + o1);
 #pragma unroll
@@ -656,7 +658,7 @@ __device__ __forceinline__ void interleave_stage() {
   }
 }
 
-// One workgroup's K loop for token blocks [0, NTB) (FULL) or [0, ntb).  The
+// One workgroup's K loop for token blocks [0, NA).  The
 // products of stage s run while the wave decodes the A operands of stage s+1,
 // so the matrix cores and the VALU work side by side within one wave.  Weight
 // bytes are fetched three stages ahead of their products (two ahead of their
@@ -665,10 +667,10 @@ __device__ __forceinline__ void interleave_stage() {
 // and writes those of stage s+1 (fetched during stage s-1) into the other LDS
 // buffer.  Stages are taken two at a time so the register sets swap roles
 // without copies.
-template <int F, int RB, int TT, bool XF16, bool FULL>
+template <int F, int RB, int TT, bool XF16, int NA>
 __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT * kKS], floatx4 (&acc)[RB][TT / 16],
                                        const u32 (&row_off)[RB], const XLanes<TT, XF16 ? 2 : 4>& xl, const u8* xb,
-                                       int ntb, int o0, int o1, int tid, int g, int sb, int nstages) {
+                                       int o0, int o1, int tid, int g, int sb, int nstages) {
   // stages sb .. sb + nstages - 1 of K; s below counts from 0 within them
   AStage<F> w0[RB], w1[RB];
   XStage<TT, XF16> x0, x1;
@@ -713,9 +715,9 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
     if (fetch2) fetch_x(s + 2, xs, !STEADY);
     __builtin_amdgcn_sched_barrier(kNoVmemCross);
     if (fetch3) fetch_w(s + 3, wn);
-    stage_products<FULL>(sX[s & 1], o0, o1, Ac, acc, ntb);
+    stage_products<RB, TT / 16, NA>(sX[s & 1], o0, o1, Ac, acc);
     if (next) put(s + 1, xo, !STEADY);
-    if constexpr (STEADY && FULL) interleave_stage<F, RB, TT / 16>();
+    if constexpr (STEADY) interleave_stage<F, RB, NA>();
     if (next) stage_barrier();
     // keep the next step's decode below this point: hoisted above the barrier it
     // waits for the weight loads this step just issued (the load counter retires
@@ -745,6 +747,24 @@ __device__ __forceinline__ void k_loop(const GemmArgs& a, _Float16 (&sX)[2][TT *
     if (++s >= nstages) break;
     step(edge_t{}, s, w0, A1, A0, x1, x0);
     ++s;
+  }
+}
+
+// The K loop for ntb active token blocks (an even count, 2 .. NTB), each count its own
+// instance, so a partly filled last super-tile runs the same scheduled steady state
+// over fewer blocks and never costs more than a full one.
+template <int F, int RB, int TT, bool XF16, int NA = TT / 16>
+__device__ __forceinline__ void k_loop_ntb(int ntb, const GemmArgs& a, _Float16 (&sX)[2][TT * kKS],
+                                           floatx4 (&acc)[RB][TT / 16], const u32 (&row_off)[RB],
+                                           const XLanes<TT, XF16 ? 2 : 4>& xl, const u8* xb, int o0, int o1, int tid,
+                                           int g, int sb, int nstages) {
+  if constexpr (NA <= 2) {
+    k_loop<F, RB, TT, XF16, 2>(a, sX, acc, row_off, xl, xb, o0, o1, tid, g, sb, nstages);
+  } else {
+    if (ntb >= NA)
+      k_loop<F, RB, TT, XF16, NA>(a, sX, acc, row_off, xl, xb, o0, o1, tid, g, sb, nstages);
+    else
+      k_loop_ntb<F, RB, TT, XF16, NA - 2>(ntb, a, sX, acc, row_off, xl, xb, o0, o1, tid, g, sb, nstages);
   }
 }
 
@@ -793,10 +813,7 @@ __global__ __launch_bounds__(256, TT >= 256 ? 1 : 2) void k_gemm(GemmArgs a) {
   XLanes<TT, ES> xl;
   xl.init(a.K, a.N, tok0, tid);
   const u8* xb = reinterpret_cast<const u8*>(a.x) + static_cast<u64>(tok0) * static_cast<u64>(a.K) * ES;
-  if (ntb == NTB)
-    k_loop<F, RB, TT, XF16, true>(a, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, sb, ns);
-  else
-    k_loop<F, RB, TT, XF16, false>(a, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, sb, ns);
+  k_loop_ntb<F, RB, TT, XF16>(ntb, a, sX, acc, row_off, xl, xb, o0, o1, tid, g, sb, ns);
 
   // D[4*(l/16) + v][l % 16] of block (b, t): row rw0 + 16b + 4g + v, token tok0 + 16t + l % 16
 #pragma unroll
@@ -1026,10 +1043,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < NTB; ++t) acc[b][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     const u8* xb = reinterpret_cast<const u8*>(a.x);
-    if (ntb == NTB)
-      k_loop<F, RB, TT, XF16, true>(ae, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, 0, all);
-    else
-      k_loop<F, RB, TT, XF16, false>(ae, sX, acc, row_off, xl, xb, ntb, o0, o1, tid, g, 0, all);
+    k_loop_ntb<F, RB, TT, XF16>(ntb, ae, sX, acc, row_off, xl, xb, o0, o1, tid, g, 0, all);
 #pragma unroll
     for (int t = 0; t < NTB; ++t) {
       const int i = 16 * t + (lane & 15);
@@ -1089,7 +1103,8 @@ typedef void (*GemmKernel)(GemmArgs);
 // 64 x 256 and 128 x 256 with fp16 activations, one workgroup per CU.
 constexpr bool shape_ok(int F, bool xf16, int RB, int TT) {
   if (TT == 256) return F == FMT_Q6_K && xf16 && (RB == 1 || RB == 2);
-  if (RB == 2) return TT == 128 && F != FMT_Q6_K && F != FMT_Q3_K && xf16;  // (Q3_K x 128 rows spills)
+  // (Q3_K, Q5_0 and Q5_K x 128 rows spill: their decode state is wider)
+  if (RB == 2) return TT == 128 && F != FMT_Q6_K && F != FMT_Q3_K && F != FMT_Q5_0 && F != FMT_Q5_K && xf16;
   return TT == 32 || TT == 64 || TT == 128;
 }
 
