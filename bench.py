@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--prefill-only", default=None, metavar="N[,N...]",
                    help="only time the decode layer's prefill GEMM at these token counts (for profiling)")
     p.add_argument("--formats-only", action="store_true", help="only run the per-format sweep")
+    p.add_argument("--small-decode-only", default=None, metavar="N[,N...]",
+                   help="only time the 4-bit-group layer at these token counts (for profiling)")
     p.add_argument("--moe-only", default=None, metavar="N[,N...]",
                    help="only time the expert-indexed paths at these token counts: the matvec up to 32 "
                         "tokens, the matrix-core path above (for profiling)")
@@ -379,7 +381,8 @@ def extra_small_decode(torch, q, W, args):
           for c in range(rot.copies)]
     wbytes = sum(int(m["blob"].size) for m in mats)
     res = []
-    for n in W.SMALL_DECODE_TOKENS:
+    tokens = [int(t) for t in args.small_decode_only.split(",")] if args.small_decode_only else W.SMALL_DECODE_TOKENS
+    for n in tokens:
         xs = [torch.from_numpy(W.small_decode_x(j, n)).to("cuda") for j in range(len(mats))]
         ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
         layers = rot.copies  # one sample = one layer pass on every copy (> 1 GiB)
@@ -761,6 +764,9 @@ def main():
         return
     if args.formats_only:
         print(json.dumps({"formats": extra_formats(torch, q, W, args)}), flush=True)
+        return
+    if args.small_decode_only:
+        print(json.dumps({"small_decode_a4g64": extra_small_decode(torch, q, W, args)}), flush=True)
         return
     if args.prefill_only:
         mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
