@@ -78,6 +78,8 @@ def parse():
                    help="only time an empty kernel and plain streaming reads of the decode-layer projection sizes")
     p.add_argument("--summarize-trace", default=None, metavar="DIR",
                    help="print a markdown summary of a rocprofv3 kernel trace of this benchmark (no GPU needed)")
+    p.add_argument("--summarize-sq", nargs="+", default=None, metavar="DIR",
+                   help="print per-kernel SQ counter fractions from rocprofv3 --pmc runs (no GPU needed)")
     p.add_argument("--summarize-counters", nargs=4, default=None, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="print a markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this benchmark and "
                         "of --copy-probe (no GPU needed)")
@@ -272,31 +274,31 @@ def traffic_from_profile(digest):
 # ------------------------------------------------------------------------------------------------
 # CPU oracle baseline
 
-def cpu_baseline(mats):
+def cpu_baseline(mats, min_seconds=10.0):
+    """The oracle on the headline workload itself: whole passes over the decode layer's
+    seven projections at one token, repeated until about min_seconds of CPU work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         blas_threads = None
-    names = ("ffn_gate", "ffn_down")
-    sample = [m for m in mats if m["name"] in names]
     from qmm_synth import workloads as W
+    xs = [W.decode_x(j, 1) for j in range(len(mats))]
     t0 = time.perf_counter()
-    nbytes = 0
-    for m in sample:
-        w = oracle.dequantize(m["fmt"], m["blob"], m["M"], m["K"])
-        x = W.decode_x([d[0] for d in W.DECODE_SHAPES].index(m["name"]), 1)
-        oracle.matmul_ref(x, w)
-        nbytes += int(m["blob"].size)
+    nbytes, passes = 0, 0
+    while passes == 0 or time.perf_counter() - t0 < min_seconds:
+        for m, x in zip(mats, xs):
+            oracle.matmul_ref(x, oracle.dequantize(m["fmt"], m["blob"], m["M"], m["K"]))
+            nbytes += int(m["blob"].size)
+        passes += 1
     dt = time.perf_counter() - t0
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": (f"{'+'.join(names)} of the same layer ({nbytes} quantized bytes, "
-                       f"{nbytes / sum(m['blob'].size for m in mats):.0%} of it) at one token: NumPy "
-                       f"dequantization (single-threaded) + fp64 matmul (BLAS threads available: "
-                       f"{blas_threads}), {dt:.1f} s; cores counts the dequantization thread, which "
-                       f"takes >99% of the time")}
+            "sample": (f"{passes} pass(es) over all seven projections of the decode layer at one token "
+                       f"({nbytes} quantized bytes): NumPy dequantization (single-threaded) + fp64 matmul "
+                       f"(BLAS threads available: {blas_threads}), {dt:.1f} s; cores counts the "
+                       f"dequantization thread, which takes >99% of the time")}
 
 
 def _median3(fn):
@@ -666,6 +668,9 @@ def summarize_trace(root):
         lines.append(f"| `{name}` | {grid} | {wg} | {len(ds)} | {np.median(ds):.2f} | {np.mean(ds):.2f} |")
         if "k_gemv1<" in name:
             gemv.extend(ds)
+    if not gemv:  # another workload: the table only
+        print("\n".join(lines))
+        return
     alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M
               for _, M, K, fmt in W.DECODE_SHAPES) / len(W.DECODE_SHAPES)
     mean = float(np.mean(gemv)) if gemv else float("nan")
@@ -679,6 +684,31 @@ def summarize_trace(root):
               f"- gemv1_mean_us: {mean:.4f}",
               f"- alg_bytes_per_launch: {alg:.0f}"]
     print("\n".join(lines))
+
+
+def summarize_sq(dirs, top=8):
+    """Per kernel (name and grid) of rocprofv3 --pmc runs over the same workload: the SQ
+    counters summed over its dispatches, as fractions of wave-cycles and per wave."""
+    agg, disp = {}, {}
+    for d in dirs:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = f"{_col(r, 'Kernel_Name')[:60]} grid {_col(r, 'Grid_Size', 'Grid_Size_X')}"
+            a = agg.setdefault(k, {})
+            a[_col(r, "Counter_Name")] = a.get(_col(r, "Counter_Name"), 0.0) + float(_col(r, "Counter_Value"))
+            disp.setdefault((k, d), set()).add(_col(r, "Dispatch_Id"))
+    out = []
+    for k, v in sorted(agg.items(), key=lambda kv: -kv[1].get("SQ_WAVE_CYCLES", 0))[:top]:
+        nd = max(len(disp.get((k, d), ())) for d in dirs)
+        wc = v.get("SQ_WAVE_CYCLES", 0) or 1.0
+        waves = v.get("SQ_WAVES", 0) or 1.0
+        out.append(f"{k}: {nd} dispatches, {waves / nd:.0f} waves each")
+        out.append("   of wave-cycles: VALU %.2f, LDS %.2f, VMEM %.2f, waiting %.2f, dependency stalls %.2f" % (
+            v.get("SQ_ACTIVE_INST_VALU", 0) / wc, v.get("SQ_ACTIVE_INST_LDS", 0) / wc,
+            v.get("SQ_ACTIVE_INST_VMEM", 0) / wc, v.get("SQ_WAIT_ANY", 0) / wc, v.get("SQ_WAIT_INST_ANY", 0) / wc))
+        out.append("   per wave: VALU %.0f, MFMA %.0f, LDS %.0f, VMEM reads %.0f instructions" % (
+            v.get("SQ_INSTS_VALU", 0) / waves, v.get("SQ_INSTS_MFMA", 0) / waves, v.get("SQ_INSTS_LDS", 0) / waves,
+            v.get("SQ_INSTS_VMEM_RD", 0) / waves))
+    print("\n".join(out))
 
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
@@ -740,6 +770,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
