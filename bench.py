@@ -60,6 +60,10 @@ VALU_F32_FMA_TFLOPS = 78.6
 VALU_F32_PACKED_TFLOPS = 157.3
 ROTATE_BYTES = 1 << 30         # > 256 MB Infinity Cache
 METRIC = "quantized-weight GB/s at n<=16 and TFLOP/s at n>=64, as % of roofline"
+# the decode step's calls (indices into the layer's projections): attn_q, attn_k and
+# attn_v read one input, ffn_gate and ffn_up another; attn_output and ffn_down each
+# wait for the previous result
+DECODE_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]
 
 
 def parse():
@@ -69,6 +73,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ungrouped", action="store_true",
+                   help="headline step as seven separate qmm_gemv calls (default: the independent "
+                        "projections share qmm_gemv_group calls)")
     p.add_argument("--event-launches", type=int, default=64,
                    help="launches per projection in the isolated per-projection pass (0: skip it)")
     p.add_argument("--calls", type=int, default=20, help="calls per timed sample in the extras")
@@ -182,9 +189,18 @@ def decode_layer(torch, q, W, args):
     layer_weight_bytes = sum(int(m["blob"].size) for m in mats)
     layer_alg_bytes = sum(int(m["blob"].size) + 4 * m["K"] + 4 * m["M"] for m in mats)
 
+    # the step's calls: the layer's independent projections share a call (query, key
+    # and value read the same normed input in a layer, as do gate and up); the
+    # library gives matrices of one format and K one launch
+    calls = [[j] for j in range(P)] if args.ungrouped else DECODE_GROUPS
+    launches = sum(len({(mats[j]["fmt"], mats[j]["K"]) for j in c}) for c in calls)
+
     def step(c):
-        for j in range(P):
-            q.qmm_gemv(handles[c][j].handle, xs[j], 1, ys[j])
+        for grp in calls:
+            if len(grp) == 1:
+                q.qmm_gemv(handles[c][grp[0]].handle, xs[grp[0]], 1, ys[grp[0]])
+            else:
+                q.qmm_gemv_group([handles[c][j].handle for j in grp], [xs[j] for j in grp], 1, [ys[j] for j in grp])
 
     full = capture(torch, lambda: [step(c) for c in range(rot.copies)])
     singles = [capture(torch, lambda c=c: step(c)) for c in range(rot.copies)]
@@ -224,18 +240,21 @@ def decode_layer(torch, q, W, args):
                     "isolated_weight_gbs": round(m["blob"].size / (mean_us[j] * 1e-6) / 1e9, 1)}
                    for j, m in enumerate(mats)]
     # the roofline's kernel: every launch of the step is k_gemv1 (Q4_K or Q6_K instance)
-    # and they run back to back, so the event-timed step over P launches is its average
-    # launch duration (the rocprofv3 trace in profiles/ checks this against per-dispatch
-    # durations)
+    # and they run back to back, so the event-timed step over its launches is their
+    # average duration (the rocprofv3 trace in profiles/ checks this against
+    # per-dispatch durations)
     step_us = ev_ms / args.steps * 1e3
-    avg_us = step_us / P
-    alg_per_launch = layer_alg_bytes / P
+    avg_us = step_us / launches
+    alg_per_launch = layer_alg_bytes / launches
     out = {
         "value": value, "ms_per_step": ms_per_step, "event_ms_per_step": ev_ms / args.steps,
         "layer_weight_bytes": layer_weight_bytes, "layer_alg_bytes": layer_alg_bytes,
         "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
         "projections": projections,
-        "kernel": {"launches_per_step": P, "avg_us": avg_us, "alg_bytes_per_launch": alg_per_launch,
+        "calls": [[mats[j]["name"] for j in c] for c in calls],
+        "launch_sets": [[mats[j]["name"] for j in c if (mats[j]["fmt"], mats[j]["K"]) == k]
+                        for c in calls for k in dict.fromkeys((mats[j]["fmt"], mats[j]["K"]) for j in c)],
+        "kernel": {"launches_per_step": launches, "avg_us": avg_us, "alg_bytes_per_launch": alg_per_launch,
                    "achieved_gbs": alg_per_launch / (avg_us * 1e-6) / 1e9},
         "sum_isolated_us": float(mean_us.sum()),
     }
@@ -391,8 +410,12 @@ def extra_small_decode(torch, q, W, args):
 
         def fn():
             for c in range(layers):
-                for j in range(len(mats)):
-                    q.qmm_gemv(hs[c][j].handle, xs[j], n, ys[j])
+                for grp in DECODE_GROUPS:  # the layer's calls, as in the headline
+                    if len(grp) == 1:
+                        q.qmm_gemv(hs[c][grp[0]].handle, xs[grp[0]], n, ys[grp[0]])
+                    else:
+                        q.qmm_gemv_group([hs[c][j].handle for j in grp], [xs[j] for j in grp], n,
+                                         [ys[j] for j in grp])
         g = capture(torch, fn)
         us = time_graph(torch, g, args.rounds) * 1e3 / layers
         del g
@@ -404,7 +427,8 @@ def extra_small_decode(torch, q, W, args):
                     "frac_valu_fma": tflops / VALU_F32_FMA_TFLOPS,
                     "frac_valu_packed": tflops / VALU_F32_PACKED_TFLOPS,
                     "binding": "hbm" if n <= 4 else "alu"})
-    return {"workload": "Qwen3-0.6B layer, A4G64 (group 64), fp16 tokens", "layer_weight_bytes": wbytes,
+    return {"workload": "Qwen3-0.6B layer, A4G64 (group 64), fp16 tokens; q+k+v and gate+up share qmm_gemv_group "
+                        "calls (one launch each at one token)", "layer_weight_bytes": wbytes,
             "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
             "valu_peaks_tflops": {"fma": VALU_F32_FMA_TFLOPS, "packed": VALU_F32_PACKED_TFLOPS},
             "results": res}
@@ -836,9 +860,11 @@ def main():
             "rotation_bytes": head["rotation_bytes"],
             "source_digest": digest,
             "projections": head["projections"],
+            "calls": head["calls"],
         },
         "roofline": {
-            "kernel": "qmm::k_gemv1 (one-token GEMV; Q4_K and Q6_K instances, seven launches per step)",
+            "kernel": "qmm::k_gemv1 (one-token GEMV; Q4_K and Q6_K instances; the step's launches: "
+                      + ", ".join("+".join(c) for c in head["launch_sets"]) + ")",
             "bound": "hbm",
             "achieved": round(kern["achieved_gbs"], 1),
             "peak": HBM_PEAK_GBS,

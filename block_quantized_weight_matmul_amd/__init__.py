@@ -22,7 +22,7 @@ from ._lib import DTYPES, LIB_PATH, NOALLOC_SCRATCH_BYTES, QMM_OK, STATUS, TILES
 
 __all__ = [
     "QMatrix", "QmmError", "LIB_PATH", "TYPES",
-    "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
+    "qmm_create", "qmm_destroy", "qmm_gemv", "qmm_gemv_group", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_bytes",
     "qmm_gemm_noalloc",
     "qmm_gemm_id", "qmm_gemm_id_tiled", "qmm_dequantize", "qmm_quantize", "quantize",
     "qmm_tile_for_tokens", "qmm_row_bytes", "qmm_block_weights", "qmm_block_bytes",
@@ -174,6 +174,31 @@ def qmm_gemv(h, x: torch.Tensor, N: int, y: torch.Tensor, stream=None) -> None:
     N = _count(N, "N", 0)
     xp, yp = _need(m.device, (x, "x", (N, m.K), _ACT), (y, "y", (N, m.M), _F32))
     check(lib.qmm_gemv(h, xp, _xt(x), N, yp, _stream(stream)))
+
+
+def qmm_gemv_group(hs, xs, N: int, ys, stream=None) -> None:
+    """qmm_gemv on each (hs[i], xs[i], ys[i]); one-token matrices of one format and K
+    share launches.  Every x has the same dtype; every tensor is on the handles' device."""
+    hs, xs, ys = list(hs), list(xs), list(ys)
+    if not (len(hs) == len(xs) == len(ys)):
+        raise ValueError("hs, xs and ys must have the same length")
+    N = _count(N, "N", 0)
+    if not hs:
+        return
+    if len({x.dtype for x in xs}) > 1:
+        raise ValueError("every x must have the same dtype")
+    n = len(hs)
+    metas = [_meta(h) for h in hs]
+    if len({m.device for m in metas}) > 1:
+        raise ValueError("every handle must be on the same device")
+    specs = []
+    for i, (m, x, y) in enumerate(zip(metas, xs, ys)):
+        specs += [(x, f"xs[{i}]", (N, m.K), _ACT), (y, f"ys[{i}]", (N, m.M), _F32)]
+    ptrs = _need(metas[0].device, *specs)
+    ha = (ctypes.c_void_p * n)(*[h if isinstance(h, int) else h.value for h in hs])
+    xa = (ctypes.c_void_p * n)(*[p.value for p in ptrs[0::2]])
+    ya = (ctypes.c_void_p * n)(*[p.value for p in ptrs[1::2]])
+    check(lib.qmm_gemv_group(ha, xa, _xt(xs[0]), N, ya, n, _stream(stream)))
 
 
 def qmm_gemm(h, x: torch.Tensor, N: int, y: torch.Tensor, tile=0, stream=None) -> None:

@@ -37,6 +37,7 @@ def _load():
         "qmm_create": (c_int, [ctypes.POINTER(vp), c_int, vp, i64, i64, i64]),
         "qmm_destroy": (c_int, [vp]),
         "qmm_gemv": (c_int, [vp, vp, c_int, i64, vp, vp]),
+        "qmm_gemv_group": (c_int, [ctypes.POINTER(vp), ctypes.POINTER(vp), c_int, i64, ctypes.POINTER(vp), c_int, vp]),
         "qmm_gemm": (c_int, [vp, vp, c_int, i64, vp, c_int, vp]),
         "qmm_gemm_ws": (c_int, [vp, vp, c_int, i64, vp, c_int, vp, ctypes.c_size_t, vp]),
         "qmm_gemm_workspace_bytes": (ctypes.c_size_t, [vp, i64]),

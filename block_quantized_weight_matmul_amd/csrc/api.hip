@@ -169,6 +169,57 @@ qmm_status qmm_gemv(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N,
   return ok();
 }
 
+qmm_status qmm_gemv_group(const qmm_matrix* const* hs, const void* const* xs, qmm_dtype xt, int64_t N,
+                          float* const* ys, int count, qmm_stream_t stream) {
+  if (count < 0 || count > QMM_GEMV_GROUP_MAX)
+    return fail(QMM_E_ARG, "qmm_gemv_group takes 0..%d matrices (got %d)", QMM_GEMV_GROUP_MAX, count);
+  if (count == 0) return ok();
+  if (!hs || !xs || !ys) return fail(QMM_E_ARG, "handle, activation and output arrays must not be NULL");
+  if (N < 0 || N > qmm::kMaxGemvTokens)
+    return fail(QMM_E_SHAPE, "qmm_gemv_group takes 0..%lld tokens (got %lld)",
+                static_cast<long long>(qmm::kMaxGemvTokens), static_cast<long long>(N));
+  qmm_status s;
+  for (int i = 0; i < count; ++i) {
+    if (!hs[i]) return fail(QMM_E_ARG, "handle %d is NULL", i);
+    if (hs[i]->d.n_experts != 1) return fail(QMM_E_ARG, "qmm_gemv_group needs handles with n_experts == 1 (handle %d)", i);
+    if ((s = check_x(xs[i], xt)) != QMM_OK || (s = check_y(ys[i])) != QMM_OK) return s;
+  }
+  if (N == 0) return ok();
+  for (int i = 0; i < count; ++i)
+    if ((s = check_device(hs[i])) != QMM_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int xf = xt == QMM_F16;
+  // the matrices of each (format, K) in sets of up to kGemvGroupMax, in order of first
+  // appearance, one launch per set where the kernels allow it; every other call alone
+  bool done[QMM_GEMV_GROUP_MAX] = {};
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const qmm::MatDesc* ms[qmm::kGemvGroupMax];
+    const void* gx[qmm::kGemvGroupMax];
+    float* gy[qmm::kGemvGroupMax];
+    int idx[qmm::kGemvGroupMax];
+    int n = 0;
+    for (int j = i; j < count && n < qmm::kGemvGroupMax; ++j)
+      if (!done[j] && hs[j]->d.fmt == hs[i]->d.fmt && hs[j]->d.K == hs[i]->d.K) {
+        ms[n] = &hs[j]->d;
+        gx[n] = xs[j];
+        gy[n] = ys[j];
+        idx[n++] = j;
+      }
+    hipError_t e = hipErrorNotSupported;
+    if (n > 1) e = qmm::launch_gemv_group(ms, gx, gy, n, static_cast<int>(N), xf, st);
+    if (e == hipSuccess) {
+      for (int k = 0; k < n; ++k) done[idx[k]] = true;
+      continue;
+    }
+    if (e != hipErrorNotSupported) return hip_fail(e, "gemv group launch");
+    e = qmm::launch_gemv(hs[i]->d, xs[i], xf, static_cast<int>(N), ys[i], st);
+    if (e != hipSuccess) return hip_fail(e, "gemv launch");
+    done[i] = true;
+  }
+  return ok();
+}
+
 qmm_status qmm_gemm(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N, float* y, qmm_tile tile,
                     qmm_stream_t stream) {
   if (!h) return fail(QMM_E_ARG, "handle is NULL");

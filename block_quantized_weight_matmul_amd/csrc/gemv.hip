@@ -36,6 +36,7 @@
 // row's partials in a fixed order (lane l adds units l, l+64, ...; then a
 // butterfly over the wave), so results are deterministic and independent of
 // the launch shape, and the dense and expert-indexed paths agree bit for bit.
+#include <climits>
 #include <type_traits>
 #include <utility>
 
@@ -59,6 +60,17 @@ struct GemvArgs {
   int S, x_per_slot, E;
   int tok_groups;       // multi-token kernel: token groups of threads
   int tok_pass;         // multi-token kernel: tokens staged per pass
+};
+
+// Matrices of one one-token launch: the same format and K, each with its own blocks,
+// activations and outputs; matrix i takes workgroups first[i] .. first[i + 1] - 1.
+struct GemvGroup {
+  const u8* W[kGemvGroupMax];
+  const void* x[kGemvGroupMax];
+  float* y[kGemvGroupMax];
+  int M[kGemvGroupMax];
+  int first[kGemvGroupMax + 1];
+  int n;
 };
 
 template <int CTRL>
@@ -608,14 +620,42 @@ inline size_t one_lds_floats(int nU, int RW) {
   return static_cast<size_t>(kXU) * (nU + 1) + static_cast<size_t>(RW) * nU + 1;
 }
 
-// rows_per_wg = RW, chunk_units = G (row groups)
+// This workgroup's matrix: a's own fields for a single call (they load with the
+// rest of the arguments), else the grp entry whose workgroups hold blockIdx.x; wg0
+// receives that matrix's first workgroup.
+__device__ __forceinline__ void group_matrix(const GemvArgs& a, const GemvGroup& grp, const u8*& W, const void*& x,
+                                             float*& y, int& M, int& wg0) {
+  W = a.W;
+  x = a.x;
+  y = a.y;
+  M = a.M;
+  wg0 = 0;
+  if (grp.n > 1) {
+    int mi = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvGroupMax; ++i) mi += i < grp.n && static_cast<int>(blockIdx.x) >= grp.first[i] ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < kGemvGroupMax; ++i)
+      if (mi == i) {
+        W = grp.W[i]; x = grp.x[i]; y = grp.y[i]; M = grp.M[i]; wg0 = grp.first[i];
+      }
+  }
+}
+
+// rows_per_wg = RW, chunk_units = G (row groups); the matrices of grp share the
+// launch (one matrix for a single call), each workgroup on rows of one of them
 template <int F, bool XH, int R>
-__global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
+__global__ __launch_bounds__(512) void k_gemv1(GemvArgs a, GemvGroup grp) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
+  const u8* W;
+  const void* xg;
+  float* yg;
+  int Mg, wg0;
+  group_matrix(a, grp, W, xg, yg, Mg, wg0);
   const int RW = a.rows_per_wg;
-  const int r0 = blockIdx.x * RW;
-  const int rows = min(RW, a.M - r0);
+  const int r0 = (static_cast<int>(blockIdx.x) - wg0) * RW;
+  const int rows = min(RW, Mg - r0);
   const int nU = a.nU;
   const int ipr = nU / RUNS;
   const int G = a.chunk_units;
@@ -624,7 +664,6 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   const int g = tid / ipr;
   const bool active = g < G;
   const int gi = active ? tid - g * ipr : 0;
-  const u8* W = a.W;
   const u32 rb = static_cast<u32>(a.row_bytes);
   float* s_x = s_dyn;
   float* s_part = s_dyn + kXU * (nU + 1);
@@ -637,7 +676,7 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   uint4 xr[kX1Rounds][4];
 #pragma unroll
   for (int j = 0; j < kX1Rounds; ++j)
-    if (j < nr && tid + j * nthr < chunks) x1_fetch<XH>(a.x, tid + j * nthr, xr[j]);
+    if (j < nr && tid + j * nthr < chunks) x1_fetch<XH>(xg, tid + j * nthr, xr[j]);
   typename It::Raw wr[R];
 #pragma unroll
   for (int k = 0; k < R && k < kAhead; ++k) It::load(W, (u32)(r0 + min(g + G * k, rows - 1)) * rb, gi, wr[k]);
@@ -670,7 +709,7 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a) {
   one_items<F, R>(W, rb, r0, xv, sx, g, G, gi, active, rows, nU, s_part, RW * nU, wr);
   __syncthreads();
   const TokMap tm{nullptr, 1, 1};
-  reduce_rows(s_part, rows, 1, nU, RW, a.M, r0, tm, a.y);
+  reduce_rows(s_part, rows, 1, nU, RW, Mg, r0, tm, yg);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -851,12 +890,15 @@ __device__ __forceinline__ void multi_rows(const GemvArgs& a, const u8* W, int r
 }
 
 template <int F, bool XH, int R>
-__global__ __launch_bounds__(512) void k_gemvn(GemvArgs a) {
-  const int RW = a.rows_per_wg;
-  const int r0 = blockIdx.x * RW;
+__global__ __launch_bounds__(512) void k_gemvn(GemvArgs a, GemvGroup grp) {
+  GemvArgs b = a;  // this workgroup's matrix (see group_matrix)
+  int wg0;
+  group_matrix(a, grp, b.W, b.x, b.y, b.M, wg0);
+  const int RW = b.rows_per_wg;
+  const int r0 = (static_cast<int>(blockIdx.x) - wg0) * RW;
   const TokMap tm{nullptr, 1, 1};
-  multi_rows<F, XH, R, kXNRounds>(a, a.W, r0, min(RW, a.M - r0), RW, a.chunk_units, a.tok_groups, a.tok_pass, tm,
-                                  a.N, s_dyn);
+  multi_rows<F, XH, R, kXNRounds>(b, b.W, r0, min(RW, b.M - r0), RW, b.chunk_units, b.tok_groups, b.tok_pass, tm,
+                                  b.N, s_dyn);
 }
 
 // LDS floats of the multi-token kernel: TP token images and a spare unit, then
@@ -1128,6 +1170,7 @@ int bucket_index(int n) {
 }
 
 typedef void (*GemvKernel)(GemvArgs);
+typedef void (*GemvGroupKernel)(GemvArgs, GemvGroup);  // one-token and few-token kernels
 
 template <int F, int... BI>
 constexpr void fill_dense(GemvKernel* t, std::integer_sequence<int, BI...>) {
@@ -1141,15 +1184,16 @@ constexpr void fill_id(GemvKernel* t, std::integer_sequence<int, BI...>) {
 }
 
 template <int F>
-constexpr void fill_one(GemvKernel (&t)[2][3]) {
+constexpr void fill_one(GemvGroupKernel (&t)[2][3]) {
   t[0][0] = k_gemv1<F, false, 1>; t[0][1] = k_gemv1<F, false, 2>; t[0][2] = k_gemv1<F, false, 4>;
   t[1][0] = k_gemv1<F, true, 1>;  t[1][1] = k_gemv1<F, true, 2>;  t[1][2] = k_gemv1<F, true, 4>;
 }
 
 template <int F>
-constexpr void fill_multi(GemvKernel (&t)[2], GemvKernel (&ti)[2]) {
+constexpr void fill_multi(GemvGroupKernel (&t)[2], GemvKernel (&ti)[2]) {
   if constexpr (F == FMT_Q8_0) {  // its codes carry a bias: the general path takes it
-    t[0] = t[1] = ti[0] = ti[1] = nullptr;
+    t[0] = t[1] = nullptr;
+    ti[0] = ti[1] = nullptr;
   } else {
     t[0] = k_gemvn<F, false, 1>;
     t[1] = k_gemvn<F, true, 1>;
@@ -1161,9 +1205,9 @@ constexpr void fill_multi(GemvKernel (&t)[2], GemvKernel (&ti)[2]) {
 struct Tables {
   GemvKernel dense[kNumFormats][kNumBuckets];
   GemvKernel id[kNumFormats][kIdBuckets];
-  GemvKernel one[kNumFormats][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
+  GemvGroupKernel one[kNumFormats][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   int one_regs[kNumFormats][2][3];    // their VGPRs per lane (512 when unknown)
-  GemvKernel multi[kNumFormats][2];   // [format][fp16 activations], one row per thread
+  GemvGroupKernel multi[kNumFormats][2];   // [format][fp16 activations], one row per thread
   GemvKernel multi_id[kNumFormats][2];
   GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
   template <int F>
@@ -1239,108 +1283,205 @@ Shape make_shape(int M, int nU, int runs, int NB, int RW, int max_threads = 512)
 // Runs (32-weight units) per work item of each format.
 constexpr int kRuns[kNumFormats] = {1, 1, 2, 2, 2, 1, 1, 1, 1, 1, 1};
 
+namespace {
+
+// Launch shape of the one-token kernel for M rows (of one matrix, or of the matrices
+// of a grouped launch) of format fmt and K = 32 nU: G row groups (G * ipr <= 512
+// threads) x R rows per thread, RW = G * R rows per workgroup, so every thread has
+// R rows to compute.  Two workgroups per CU when R in {1, 2} makes G * ipr fill at
+// least 3/4 of their waves and the kernel's registers let both sit on the CU at once
+// (the second workgroup's loads and products overlap the first one's reduction);
+// otherwise about one workgroup per CU, R in {1, 2, 4} the smallest that covers
+// M / 256 rows.  False when the activation image and partials do not fit the LDS
+// budget (the general path takes such shapes).
+struct OneShape {
+  int ri, Ge, RW, threads;
+  size_t lds;
+};
+
+bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o) {
+  const int ipr = nU / kRuns[fmt];
+  if (ipr > 512 || ipr < 1) return false;
+  const int Gmax = 512 / ipr;
+  const int want = static_cast<int>((M + cus - 1) / cus);
+  const int xh = x_f16 ? 1 : 0;
+  auto two_fit = [&](int r, int ri) {
+    const int G2 = (want + 2 * r - 1) / (2 * r);
+    const int thr = (G2 * ipr + 63) / 64 * 64;
+    const int regs = (tables().one_regs[fmt][xh][ri] + 7) / 8 * 8;
+    const int waves_per_simd = (thr / 64 + 3) / 4;  // one workgroup's waves on each SIMD
+    return G2 <= Gmax && 4 * G2 * ipr >= 3 * thr && 2 * waves_per_simd * regs <= 512;
+  };
+  int R, Ge;
+  if (two_fit(1, 0) || two_fit(2, 1)) {
+    R = two_fit(1, 0) ? 1 : 2;
+    o.ri = R - 1;
+    Ge = (want + 2 * R - 1) / (2 * R);
+  } else {
+    R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
+    o.ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
+    Ge = (want + R - 1) / R;
+  }
+  if (Ge > Gmax) Ge = Gmax;
+  o.Ge = Ge;
+  o.RW = Ge * R;
+  o.threads = (Ge * ipr + 63) / 64 * 64;
+  o.lds = one_lds_floats(nU, o.RW) * sizeof(float);
+  return o.lds <= static_cast<size_t>(kLdsBudget);
+}
+
+hipError_t launch_one(int fmt, int nU, int64_t row_bytes, const OneShape& o, const GemvGroup& grp, int x_f16,
+                      hipStream_t st) {
+  GemvArgs a{};
+  a.W = grp.W[0];  // a single matrix is read from these fields
+  a.x = grp.x[0];
+  a.y = grp.y[0];
+  a.M = grp.M[0];
+  a.row_bytes = row_bytes;
+  a.nU = nU;
+  a.K = 32 * nU;
+  a.rows_per_wg = o.RW;
+  a.chunk_units = o.Ge;
+  a.x_f16 = x_f16;
+  a.N = 1;
+  hipLaunchKernelGGL(tables().one[fmt][x_f16 ? 1 : 0][o.ri], dim3(grp.first[grp.n]), dim3(o.threads), o.lds, st, a,
+                     grp);
+  return hipGetLastError();
+}
+
+// A few tokens (2 .. 32): the one-token layout with one row per thread (two would
+// spill registers with fp32 activations), about one workgroup per CU (two above 8
+// tokens, where the products outweigh staging the activations once more: the
+// 4-bit-group layer at 16 tokens 53.6 -> 50.5 us, while 2 and 4 tokens lose 4-5%),
+// TGN token groups filling up to 512 threads, TP tokens per pass as the LDS budget
+// and kXNRounds staging rounds allow.  M: the rows of the launch (of one matrix or
+// of a group).  False for Q8_0 (its codes carry a bias: the general path takes it)
+// and for shapes that do not fit.
+struct MultiShape {
+  int Ge, RW, TGN, TP, threads;
+  size_t lds;
+};
+
+bool multi_shape(int fmt, int nU, int64_t M, int N, int x_f16, int cus, MultiShape& o) {
+  if (fmt == FMT_Q8_0) return false;
+  const int ipr2 = nU / kRuns[fmt];
+  if (ipr2 < 1 || ipr2 > 512) return false;
+  const int Gmax = 512 / ipr2;
+  const int per_cu = N > 8 ? 2 : 1;
+  const int want = static_cast<int>((M + cus * per_cu - 1) / (cus * per_cu));
+  int Ge = want;
+  if (Ge > Gmax) Ge = Gmax;
+  const int RW = Ge;
+  const bool xh = x_f16 != 0;
+  int TP = N;
+  while (TP > 0 && multi_lds_floats(xh, nU, RW, TP) * sizeof(float) > static_cast<size_t>(kLdsBudget)) --TP;
+  int TGN = TP < 512 / (Ge * ipr2) ? TP : 512 / (Ge * ipr2);
+  if (TGN < 1) TGN = 1;
+  const int threads = (Ge * TGN * ipr2 + 63) / 64 * 64;
+  const int tp_rounds = kXNRounds * threads / (2 * nU);
+  if (TP > tp_rounds) TP = tp_rounds;
+  if (TP >= 1) TP = (N + (N + TP - 1) / TP - 1) / ((N + TP - 1) / TP);  // passes of equal size
+  if (TGN > TP) TGN = TP;
+  if (TP < 1) return false;
+  o.Ge = Ge;
+  o.RW = RW;
+  o.TGN = TGN;
+  o.TP = TP;
+  o.threads = threads;
+  o.lds = multi_lds_floats(xh, nU, RW, TP) * sizeof(float);
+  return true;
+}
+
+hipError_t launch_multi(int fmt, int nU, int64_t row_bytes, int N, const MultiShape& o, const GemvGroup& grp,
+                        int x_f16, hipStream_t st) {
+  GemvArgs a{};
+  a.W = grp.W[0];  // a single matrix is read from these fields
+  a.x = grp.x[0];
+  a.y = grp.y[0];
+  a.M = grp.M[0];
+  a.row_bytes = row_bytes;
+  a.nU = nU;
+  a.K = 32 * nU;
+  a.rows_per_wg = o.RW;
+  a.chunk_units = o.Ge;
+  a.x_f16 = x_f16;
+  a.N = N;
+  a.tok_groups = o.TGN;
+  a.tok_pass = o.TP;
+  hipLaunchKernelGGL(tables().multi[fmt][x_f16 ? 1 : 0], dim3(grp.first[grp.n]), dim3(o.threads), o.lds, st, a,
+                     grp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, float* const* ys, int n, int N,
+                             int x_f16, hipStream_t st) {
+  if (n < 1 || n > kGemvGroupMax || N < 1) return hipErrorNotSupported;
+  const MatDesc& m0 = *ms[0];
+  int64_t rows = 0;
+  for (int i = 0; i < n; ++i) {
+    if (ms[i]->fmt != m0.fmt || ms[i]->K != m0.K || ms[i]->blocks == nullptr) return hipErrorNotSupported;
+    rows += ms[i]->M;
+  }
+  const int nU = static_cast<int>(m0.K / 32);
+  OneShape o;
+  MultiShape mo;
+  int RW;
+  if (N == 1) {
+    if (!one_shape(m0.fmt, nU, rows, x_f16, m0.cus, o)) return hipErrorNotSupported;
+    RW = o.RW;
+  } else {
+    if (!multi_shape(m0.fmt, nU, rows, N, x_f16, m0.cus, mo)) return hipErrorNotSupported;
+    RW = mo.RW;
+  }
+  GemvGroup grp{};
+  grp.n = n;
+  int64_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    grp.W[i] = ms[i]->blocks;
+    grp.x[i] = xs[i];
+    grp.y[i] = ys[i];
+    grp.M[i] = static_cast<int>(ms[i]->M);
+    grp.first[i] = static_cast<int>(wg);
+    wg += (ms[i]->M + RW - 1) / RW;
+  }
+  if (wg > INT_MAX) return hipErrorNotSupported;
+  grp.first[n] = static_cast<int>(wg);
+  const int64_t rb = static_cast<int64_t>(m0.row_bytes);
+  return N == 1 ? launch_one(m0.fmt, nU, rb, o, grp, x_f16, st) : launch_multi(m0.fmt, nU, rb, N, mo, grp, x_f16, st);
+}
+
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t st) {
   const int cus = m.cus;
   const int bi = bucket_index(N);
   if (bi < 0) return hipErrorInvalidValue;
   const int nU = static_cast<int>(m.K / 32);
   const int M = static_cast<int>(m.M);
-  const int ipr = nU / kRuns[m.fmt];
-  if (N == 1 && ipr <= 512) {
-    // One token: G row groups (G * ipr <= 512 threads) x R rows per thread,
-    // RW = G * R rows per workgroup, so every thread has R rows to compute.
-    // Two workgroups per CU when R in {1, 2} makes G * ipr fill at least 3/4 of
-    // their waves and the kernel's registers let both sit on the CU at once (the
-    // second workgroup's loads and products overlap the first one's reduction);
-    // otherwise about one workgroup per CU, R in {1, 2, 4} the smallest that
-    // covers M / 256 rows.  Shapes whose activation image and partials do not
-    // fit the LDS budget take the general path below.
-    const int Gmax = 512 / ipr;
-    const int want = (M + cus - 1) / cus;
-    const int xh = x_f16 ? 1 : 0;
-    auto two_fit = [&](int r, int ri) {
-      const int G2 = (want + 2 * r - 1) / (2 * r);
-      const int thr = (G2 * ipr + 63) / 64 * 64;
-      const int regs = (tables().one_regs[m.fmt][xh][ri] + 7) / 8 * 8;
-      const int waves_per_simd = (thr / 64 + 3) / 4;  // one workgroup's waves on each SIMD
-      return G2 <= Gmax && 4 * G2 * ipr >= 3 * thr && 2 * waves_per_simd * regs <= 512;
-    };
-    int R, ri, Ge;
-    if (two_fit(1, 0) || two_fit(2, 1)) {
-      R = two_fit(1, 0) ? 1 : 2;
-      ri = R - 1;
-      Ge = (want + 2 * R - 1) / (2 * R);
-    } else {
-      R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
-      ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
-      Ge = (want + R - 1) / R;
-    }
-    if (Ge > Gmax) Ge = Gmax;
-    const int RW = Ge * R;
-    const size_t lds = one_lds_floats(nU, RW) * sizeof(float);
-    if (lds <= static_cast<size_t>(kLdsBudget)) {
-      GemvArgs a{};
-      a.W = m.blocks;
-      a.row_bytes = m.row_bytes;
-      a.M = M;
-      a.nU = nU;
-      a.K = static_cast<int>(m.K);
-      a.rows_per_wg = RW;
-      a.chunk_units = Ge;
-      a.x = x;
-      a.x_f16 = x_f16;
-      a.y = y;
-      a.N = 1;
-      const int threads = (Ge * ipr + 63) / 64 * 64;
-      hipLaunchKernelGGL(tables().one[m.fmt][xh][ri], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
-      return hipGetLastError();
-    }
+  OneShape o;
+  if (N == 1 && one_shape(m.fmt, nU, M, x_f16, cus, o)) {
+    GemvGroup grp{};
+    grp.n = 1;
+    grp.W[0] = m.blocks;
+    grp.x[0] = x;
+    grp.y[0] = y;
+    grp.M[0] = M;
+    grp.first[0] = 0;
+    grp.first[1] = (M + o.RW - 1) / o.RW;
+    return launch_one(m.fmt, nU, static_cast<int64_t>(m.row_bytes), o, grp, x_f16, st);
   }
-  if (N >= 2 && m.fmt != FMT_Q8_0) {
-    // A few tokens: the one-token layout with one row per thread (two would
-    // spill registers with fp32 activations), about one workgroup per CU (two
-    // above 8 tokens, where the products outweigh staging the activations once
-    // more: the 4-bit-group layer at 16 tokens 53.6 -> 50.5 us, while 2 and 4
-    // tokens lose 4-5%), TGN token groups filling up to 512 threads, TP tokens
-    // per pass as the LDS budget and kXNRounds staging rounds allow.
-    const int ipr2 = nU / kRuns[m.fmt];
-    const int Gmax = 512 / ipr2;
-    if (Gmax >= 1) {
-      const int per_cu = N > 8 ? 2 : 1;
-      const int want = (M + cus * per_cu - 1) / (cus * per_cu);
-      const int R = 1;
-      int Ge = (want + R - 1) / R;
-      if (Ge > Gmax) Ge = Gmax;
-      const int RW = Ge * R;
-      const bool xh = x_f16 != 0;
-      int TP = N;
-      while (TP > 0 && multi_lds_floats(xh, nU, RW, TP) * sizeof(float) > static_cast<size_t>(kLdsBudget)) --TP;
-      int TGN = TP < 512 / (Ge * ipr2) ? TP : 512 / (Ge * ipr2);
-      if (TGN < 1) TGN = 1;
-      const int threads = (Ge * TGN * ipr2 + 63) / 64 * 64;
-      const int tp_rounds = kXNRounds * threads / (2 * nU);
-      if (TP > tp_rounds) TP = tp_rounds;
-      if (TP >= 1) TP = (N + (N + TP - 1) / TP - 1) / ((N + TP - 1) / TP);  // passes of equal size
-      if (TGN > TP) TGN = TP;
-      if (TP >= 1) {
-        GemvArgs a{};
-        a.W = m.blocks;
-        a.row_bytes = m.row_bytes;
-        a.M = M;
-        a.nU = nU;
-        a.K = static_cast<int>(m.K);
-        a.rows_per_wg = RW;
-        a.chunk_units = Ge;
-        a.x = x;
-        a.x_f16 = x_f16;
-        a.y = y;
-        a.N = N;
-        a.tok_groups = TGN;
-        a.tok_pass = TP;
-        const size_t lds = multi_lds_floats(xh, nU, RW, TP) * sizeof(float);
-        hipLaunchKernelGGL(tables().multi[m.fmt][xh ? 1 : 0], dim3((M + RW - 1) / RW), dim3(threads), lds, st, a);
-        return hipGetLastError();
-      }
+  if (N >= 2) {
+    MultiShape ms;
+    if (multi_shape(m.fmt, nU, M, N, x_f16, cus, ms)) {
+      GemvGroup grp{};
+      grp.n = 1;
+      grp.W[0] = m.blocks;
+      grp.x[0] = x;
+      grp.y[0] = y;
+      grp.M[0] = M;
+      grp.first[0] = 0;
+      grp.first[1] = (M + ms.RW - 1) / ms.RW;
+      return launch_multi(m.fmt, nU, static_cast<int64_t>(m.row_bytes), N, ms, grp, x_f16, st);
     }
   }
   // about one workgroup per CU

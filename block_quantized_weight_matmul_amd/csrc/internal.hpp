@@ -29,6 +29,14 @@ constexpr int64_t kMaxGemmIdPairs = int64_t(1) << 18;
 hipError_t launch_dequant(const MatDesc& m, int64_t expert, void* out, int out_f16, hipStream_t s);
 hipError_t launch_quantize(int fmt, const float* w, int64_t M, int64_t K, void* out, hipStream_t s);
 hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float* y, hipStream_t s);
+// Matrix-vector products of N tokens (1 .. 32) on up to kGemvGroupMax matrices of one
+// format and K in one launch (y_i = x_i W_i^T, the bits of separate launch_gemv
+// calls).  Returns hipErrorNotSupported, launching nothing, when the matrices cannot
+// share the one-token or few-token kernel's launch shape; the caller then makes
+// separate calls.
+constexpr int kGemvGroupMax = 4;
+hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, float* const* ys, int n, int N,
+                             int x_f16, hipStream_t s);
 hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int S, int x_per_slot,
                           const int32_t* ids, float* y, hipStream_t s);
 // K splits of the matrix-matrix path for N tokens (splits = 1: unsplit)

@@ -163,6 +163,28 @@ qmm_status qmm_gemv(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
                     float *y, qmm_stream_t stream);
 
 /*
+ * qmm_gemv_group -- qmm_gemv on `count` independent matrices in one call: the
+ * matrix-vector product of the llama.cpp and tiny-llm pull requests above, for the
+ * projections of one decode step that read no output of each other (a layer's
+ * query, key and value projections; its gate and up projections).
+ *   hs, xs, ys  HOST arrays of `count` entries: handle i (n_experts == 1), its
+ *               activations ([N, K_i], element type xt, 16-byte aligned DEVICE
+ *               pointer) and its output ([N, M_i] fp32, 4-byte aligned DEVICE
+ *               pointer), as for qmm_gemv.  No output may overlap another output
+ *               or any activation.  The arrays are read during the call only.
+ *   N           0..32 tokens, the same for every matrix; 0 launches nothing.
+ *   count       0..QMM_GEMV_GROUP_MAX.
+ * Every output holds the bits qmm_gemv would give it.  At one token, matrices of
+ * the same format and K share launches (up to four matrices per launch, one kernel
+ * launch per such set); other matrices, and every matrix at N > 1, take a launch
+ * of their own.  All arguments are checked before anything is launched; errors as
+ * for qmm_gemv (QMM_E_ARG for a NULL array or a count out of range).
+ */
+#define QMM_GEMV_GROUP_MAX 64
+qmm_status qmm_gemv_group(const qmm_matrix *const *hs, const void *const *xs, qmm_dtype xt,
+                          int64_t N, float *const *ys, int count, qmm_stream_t stream);
+
+/*
  * qmm_gemm -- matrix-matrix path for any N (candle pull request above).  Each
  * workgroup dequantizes a tile of weight rows once per K step into LDS as fp16
  * (round to nearest even of the fp32 weight) and multiplies it on the matrix

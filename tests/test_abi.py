@@ -89,6 +89,12 @@ def test_argument_errors_before_device():
     assert lib.qmm_gemm_id(None, ctypes.c_void_p(base), 0, 1, 1, 1, ctypes.c_void_p(base),
                            ctypes.c_void_p(base), None) == -1
     assert lib.qmm_dequantize(None, 0, ctypes.c_void_p(base), 0, None) == -1
+    assert lib.qmm_gemv_group(None, None, 0, 1, None, 1, None) == -1     # NULL arrays
+    assert lib.qmm_gemv_group(None, None, 0, 1, None, -1, None) == -1    # count out of range
+    assert lib.qmm_gemv_group(None, None, 0, 1, None, 65, None) == -1
+    assert lib.qmm_gemv_group(None, None, 0, 1, None, 0, None) == 0      # nothing to do
+    nul = (ctypes.c_void_p * 1)()
+    assert lib.qmm_gemv_group(nul, nul, 0, 1, nul, 1, None) == -1        # NULL handle
     assert lib.qmm_destroy(None) == 0
 
 
@@ -102,6 +108,12 @@ def test_binding_refuses_bad_type_name():
 def test_workspace_query_without_handle():
     L = _lib()
     assert L.lib.qmm_gemm_workspace_bytes(None, 7) == 0
+
+
+def test_gemv_group_limit_in_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define QMM_GEMV_GROUP_MAX (\d+)", text)
+    assert m and int(m.group(1)) == 64
 
 
 def test_noalloc_scratch_size_matches_header():

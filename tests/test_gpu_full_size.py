@@ -183,3 +183,42 @@ def test_expert_tiled(n):
     toks = np.unique(np.concatenate([[0, n - 1], g.choice(n, size=min(6, n), replace=False)]))
     _moe_rows_check(yh[toks], x[toks], ids[toks], sample_rows(W.MOE_M, [85, n], k=16), TOL_GEMM,
                     f"moe tiled n={n}")
+
+
+@pytest.mark.parametrize("group", [(0, 1), (4, 5), (0, 1, 2)], ids=["attn_q+attn_k", "ffn_gate+ffn_up", "attn_q+k+v"])
+def test_decode_gemv_grouped(group):
+    """The headline's grouped launches: qmm_gemv_group of one fp32 token on the layer's
+    independent projections gives each the bits of its own qmm_gemv call."""
+    ms = [decode_matrix(j) for j in group]
+    xs = [W.decode_x(j) for j in group]
+    qms = [q.QMatrix(to_dev(m["blob"]), m["fmt"], m["M"], m["K"]) for m in ms]
+    xd = [to_dev(x) for x in xs]
+    ys = [torch.empty((1, m["M"]), device="cuda") for m in ms]
+    q.qmm_gemv_group([qm.handle for qm in qms], xd, 1, ys)
+    for m, x, qm, y, xx in zip(ms, xd, qms, ys, xs):
+        single = torch.empty((1, m["M"]), device="cuda")
+        q.qmm_gemv(qm.handle, x, 1, single)
+        got = to_host(y)
+        assert np.array_equal(got.view(np.uint32), to_host(single).view(np.uint32)), m["name"]
+        check_rows(got, xx, m, sample_rows(m["M"], [81, m["M"]]), TOL_GEMV, f"grouped {m['name']}")
+
+
+@pytest.mark.parametrize("n", W.SMALL_DECODE_TOKENS)
+def test_small_decode_layer_grouped(n):
+    """The 4-bit-group layer's calls as the benchmark makes them: q+k+v and gate+up
+    through qmm_gemv_group (one launch each), every output the bits of its own
+    qmm_gemv call."""
+    for grp in ([0, 1, 2], [4, 5]):
+        ms = [small_matrix(i) for i in grp]
+        xs = [W.small_decode_x(i, n) for i in grp]
+        qms = [q.QMatrix(to_dev(m["blob"]), m["fmt"], m["M"], m["K"]) for m in ms]
+        xd = [to_dev(x) for x in xs]
+        ys = [torch.empty((n, m["M"]), device="cuda") for m in ms]
+        q.qmm_gemv_group([qm.handle for qm in qms], xd, n, ys)
+        for m, qm, x, y, xx in zip(ms, qms, xd, ys, xs):
+            single = torch.empty((n, m["M"]), device="cuda")
+            q.qmm_gemv(qm.handle, x, n, single)
+            got = to_host(y)
+            assert np.array_equal(got.view(np.uint32), to_host(single).view(np.uint32)), (m["name"], n)
+            check_rows(got, xx.astype(np.float32), m, sample_rows(m["M"], [82, n]), TOL_GEMV,
+                       f"a4g64 grouped {m['name']} n={n}")

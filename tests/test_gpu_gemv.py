@@ -119,3 +119,57 @@ def test_gemv_tokens_match_single_token_calls(fmt):
         for t in range(N):
             one = to_host(qm.gemv(x[t:t + 1].contiguous()))
             assert np.array_equal(full[t:t + 1].view(np.uint32), one.view(np.uint32)), (fmt, xdtype, t)
+
+
+# matrices of a grouped call: two (format, K) classes with several members (one of five:
+# more than one launch holds), rows that are not a multiple of any workgroup's rows,
+# and matrices that take a launch of their own
+GROUP = [("q4_k", 300, 2560), ("q4_k", 1000, 2560), ("q6_k", 500, 2560), ("q4_k", 64, 512), ("q4_k", 7, 2560),
+         ("q4_0", 200, 512), ("q4_k", 2049, 2560), ("q4_k", 33, 2560), ("q4_0", 96, 512)]
+
+
+@pytest.mark.parametrize("xdt", [np.float32, np.float16])
+@pytest.mark.parametrize("N", [1, 3, 16])
+def test_gemv_group_matches_single_calls(N, xdt):
+    """qmm_gemv_group gives every output the bits of its own qmm_gemv call (a grouped
+    one-token or few-token launch runs each matrix's rows exactly as the single launch
+    does), within the oracle's bound."""
+    qms, xs, ws, xh = [], [], [], []
+    for i, (fmt, M, K) in enumerate(GROUP):
+        blob = make_matrix(fmt, M, K, [44, i])
+        ws.append(oracle.dequantize(fmt, blob, M, K))
+        qms.append(q.QMatrix(to_dev(blob), fmt, M, K))
+        x = np.random.default_rng([45, i, N]).standard_normal((N, K)).astype(np.float32).astype(xdt)
+        xh.append(x)
+        xs.append(to_dev(x))
+    ys = [torch.full((N, qm.M), float("nan"), device="cuda") for qm in qms]
+    q.qmm_gemv_group([qm.handle for qm in qms], xs, N, ys)
+    for i, (qm, x, y) in enumerate(zip(qms, xs, ys)):
+        single = to_host(qm.gemv(x))
+        got = to_host(y)
+        assert np.array_equal(got.view(np.uint32), single.view(np.uint32)), (GROUP[i], N)
+        assert_within(got, oracle.matmul_ref(xh[i], ws[i]), oracle.tolerance_scale(xh[i], ws[i]), TOL,
+                      f"gemv_group {GROUP[i]} N={N}")
+
+
+def test_gemv_group_edge_cases():
+    blob = make_matrix("q4_k", 64, 256, [46])
+    qm = q.QMatrix(to_dev(blob), "q4_k", 64, 256)
+    x = to_dev(np.ones((1, 256), np.float32))
+    q.qmm_gemv_group([], [], 1, [])                       # nothing to do
+    # one matrix: the single call's bits
+    y1 = torch.empty((1, 64), device="cuda")
+    q.qmm_gemv_group([qm.handle], [x], 1, [y1])
+    assert np.array_equal(to_host(y1), to_host(qm.gemv(x)))
+    # argument errors come before any launch
+    lib = L.lib
+    ha = (ctypes.c_void_p * 1)(qm.handle.value)
+    xa = (ctypes.c_void_p * 1)(x.data_ptr())
+    ya = (ctypes.c_void_p * 1)(y1.data_ptr())
+    y0 = torch.full((1, 64), 7.0, device="cuda")
+    assert lib.qmm_gemv_group(ha, xa, L.DTYPES["f32"], 0, (ctypes.c_void_p * 1)(y0.data_ptr()), 1, None) == 0
+    assert bool((y0 == 7.0).all())                             # zero tokens: nothing written
+    assert lib.qmm_gemv_group(ha, xa, L.DTYPES["f32"], 33, ya, 1, None) == -3
+    xa_bad = (ctypes.c_void_p * 1)(x.data_ptr() + 4)
+    assert lib.qmm_gemv_group(ha, xa_bad, L.DTYPES["f32"], 1, ya, 1, None) == -4
+    assert lib.qmm_gemv_group(ha, xa, L.DTYPES["f32"], 1, ya, 65, None) == -1
