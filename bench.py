@@ -176,6 +176,28 @@ def time_graph(torch, g, rounds):
 # ------------------------------------------------------------------------------------------------
 # headline: decode layer, one token
 
+def launch_sets(mats, call, N):
+    """The launches qmm_gemv_group makes for the matrices `call` (indices into mats) at N
+    tokens: in order, up to four not yet launched matrices of the first one's K (one
+    format, or Q4_K with Q6_K at one token), else those of its format and K, else it
+    alone."""
+    left, out = list(call), []
+    while left:
+        i = left[0]
+        for same_fmt in (False, True):
+            st = [j for j in left if mats[j]["K"] == mats[i]["K"]
+                  and (not same_fmt or mats[j]["fmt"] == mats[i]["fmt"])][:4]
+            fmts = {mats[j]["fmt"] for j in st}
+            if len(st) > 1 and (len(fmts) == 1 and (N == 1 or mats[i]["fmt"] != "q8_0")
+                                or (fmts <= {"q4_k", "q6_k"} and N == 1)):
+                break
+        else:
+            st = [i]
+        out.append(st)
+        left = [j for j in left if j not in st]
+    return out
+
+
 def decode_layer(torch, q, W, args):
     t0 = time.time()
     mats = [W.decode_weights(i) for i in range(len(W.DECODE_SHAPES))]
@@ -193,7 +215,8 @@ def decode_layer(torch, q, W, args):
     # and value read the same normed input in a layer, as do gate and up); the
     # library gives matrices of one format and K one launch
     calls = [[j] for j in range(P)] if args.ungrouped else DECODE_GROUPS
-    launches = sum(len({(mats[j]["fmt"], mats[j]["K"]) for j in c}) for c in calls)
+    sets = [s for c in calls for s in launch_sets(mats, c, 1)]
+    launches = len(sets)
 
     def step(c):
         for grp in calls:
@@ -252,8 +275,7 @@ def decode_layer(torch, q, W, args):
         "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
         "projections": projections,
         "calls": [[mats[j]["name"] for j in c] for c in calls],
-        "launch_sets": [[mats[j]["name"] for j in c if (mats[j]["fmt"], mats[j]["K"]) == k]
-                        for c in calls for k in dict.fromkeys((mats[j]["fmt"], mats[j]["K"]) for j in c)],
+        "launch_sets": [[mats[j]["name"] for j in st] for st in sets],
         "kernel": {"launches_per_step": launches, "avg_us": avg_us, "alg_bytes_per_launch": alg_per_launch,
                    "achieved_gbs": alg_per_launch / (avg_us * 1e-6) / 1e9},
         "sum_isolated_us": float(mean_us.sum()),

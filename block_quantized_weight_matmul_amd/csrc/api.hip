@@ -189,29 +189,32 @@ qmm_status qmm_gemv_group(const qmm_matrix* const* hs, const void* const* xs, qm
     if ((s = check_device(hs[i])) != QMM_OK) return s;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int xf = xt == QMM_F16;
-  // the matrices of each (format, K) in sets of up to kGemvGroupMax, in order of first
-  // appearance, one launch per set where the kernels allow it; every other call alone
+  // in order of first appearance: up to kGemvGroupMax not yet launched matrices of
+  // the same K in one launch (the kernels take one format, or Q4_K with Q6_K at one
+  // token), else those of the same format and K, else the matrix alone
   bool done[QMM_GEMV_GROUP_MAX] = {};
   for (int i = 0; i < count; ++i) {
     if (done[i]) continue;
-    const qmm::MatDesc* ms[qmm::kGemvGroupMax];
-    const void* gx[qmm::kGemvGroupMax];
-    float* gy[qmm::kGemvGroupMax];
-    int idx[qmm::kGemvGroupMax];
-    int n = 0;
-    for (int j = i; j < count && n < qmm::kGemvGroupMax; ++j)
-      if (!done[j] && hs[j]->d.fmt == hs[i]->d.fmt && hs[j]->d.K == hs[i]->d.K) {
-        ms[n] = &hs[j]->d;
-        gx[n] = xs[j];
-        gy[n] = ys[j];
-        idx[n++] = j;
-      }
     hipError_t e = hipErrorNotSupported;
-    if (n > 1) e = qmm::launch_gemv_group(ms, gx, gy, n, static_cast<int>(N), xf, st);
-    if (e == hipSuccess) {
-      for (int k = 0; k < n; ++k) done[idx[k]] = true;
-      continue;
+    for (int same_fmt = 0; same_fmt < 2 && e == hipErrorNotSupported; ++same_fmt) {
+      const qmm::MatDesc* ms[qmm::kGemvGroupMax];
+      const void* gx[qmm::kGemvGroupMax];
+      float* gy[qmm::kGemvGroupMax];
+      int idx[qmm::kGemvGroupMax];
+      int n = 0;
+      for (int j = i; j < count && n < qmm::kGemvGroupMax; ++j)
+        if (!done[j] && hs[j]->d.K == hs[i]->d.K && (!same_fmt || hs[j]->d.fmt == hs[i]->d.fmt)) {
+          ms[n] = &hs[j]->d;
+          gx[n] = xs[j];
+          gy[n] = ys[j];
+          idx[n++] = j;
+        }
+      if (n < 2) continue;
+      e = qmm::launch_gemv_group(ms, gx, gy, n, static_cast<int>(N), xf, st);
+      if (e == hipSuccess)
+        for (int k = 0; k < n; ++k) done[idx[k]] = true;
     }
+    if (e == hipSuccess) continue;
     if (e != hipErrorNotSupported) return hip_fail(e, "gemv group launch");
     e = qmm::launch_gemv(hs[i]->d, xs[i], xf, static_cast<int>(N), ys[i], st);
     if (e != hipSuccess) return hip_fail(e, "gemv launch");

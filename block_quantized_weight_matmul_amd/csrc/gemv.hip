@@ -71,6 +71,7 @@ struct GemvGroup {
   int M[kGemvGroupMax];
   int first[kGemvGroupMax + 1];
   int n;
+  int fmt_b;  // k_gemv1_pair: bit i set when matrix i is of its second format
 };
 
 template <int CTRL>
@@ -642,17 +643,13 @@ __device__ __forceinline__ void group_matrix(const GemvArgs& a, const GemvGroup&
   }
 }
 
-// rows_per_wg = RW, chunk_units = G (row groups); the matrices of grp share the
-// launch (one matrix for a single call), each workgroup on rows of one of them
+// rows_per_wg = RW, chunk_units = G (row groups): one workgroup's rows of matrix W
+// (its activations xg, outputs yg, Mg rows; its workgroups start at wg0)
 template <int F, bool XH, int R>
-__global__ __launch_bounds__(512) void k_gemv1(GemvArgs a, GemvGroup grp) {
+__device__ __forceinline__ void gemv1_rows(const GemvArgs& a, const u8* W, const void* xg, float* yg, int Mg,
+                                           int wg0, u32 rb) {
   using It = Item<F>;
   constexpr int RUNS = It::RUNS;
-  const u8* W;
-  const void* xg;
-  float* yg;
-  int Mg, wg0;
-  group_matrix(a, grp, W, xg, yg, Mg, wg0);
   const int RW = a.rows_per_wg;
   const int r0 = (static_cast<int>(blockIdx.x) - wg0) * RW;
   const int rows = min(RW, Mg - r0);
@@ -664,7 +661,6 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a, GemvGroup grp) {
   const int g = tid / ipr;
   const bool active = g < G;
   const int gi = active ? tid - g * ipr : 0;
-  const u32 rb = static_cast<u32>(a.row_bytes);
   float* s_x = s_dyn;
   float* s_part = s_dyn + kXU * (nU + 1);
 
@@ -710,6 +706,42 @@ __global__ __launch_bounds__(512) void k_gemv1(GemvArgs a, GemvGroup grp) {
   __syncthreads();
   const TokMap tm{nullptr, 1, 1};
   reduce_rows(s_part, rows, 1, nU, RW, Mg, r0, tm, yg);
+}
+
+// The one-token kernel: the matrices of grp share the launch (one matrix for a single
+// call), each workgroup on rows of one of them.
+template <int F, bool XH, int R>
+__global__ __launch_bounds__(512) void k_gemv1(GemvArgs a, GemvGroup grp) {
+  const u8* W;
+  const void* xg;
+  float* yg;
+  int Mg, wg0;
+  group_matrix(a, grp, W, xg, yg, Mg, wg0);
+  gemv1_rows<F, XH, R>(a, W, xg, yg, Mg, wg0, static_cast<u32>(a.row_bytes));
+}
+
+// The one-token kernel for a group that mixes two formats of one item width (the
+// K-quant mixes that keep a few tensors in Q6_K beside Q4_K): bit i of grp.fmt_b
+// marks matrix i as format FB, the others are FA.  A workgroup runs its matrix's
+// format, so every output is the single call's.
+template <int FA, int FB, bool XH, int R>
+__global__ __launch_bounds__(512) void k_gemv1_pair(GemvArgs a, GemvGroup grp) {
+  static_assert(Item<FA>::RUNS == Item<FB>::RUNS, "one launch shape for both formats");
+  const u8* W;
+  const void* xg;
+  float* yg;
+  int Mg, wg0;
+  group_matrix(a, grp, W, xg, yg, Mg, wg0);
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvGroupMax; ++i) mi += i < grp.n && static_cast<int>(blockIdx.x) >= grp.first[i] ? 1 : 0;
+  // row bytes of each format at this K: (32 nU / block weights) blocks
+  constexpr u32 ua = FmtInfo<FA>::BW / 32, ub = FmtInfo<FB>::BW / 32;
+  const u32 nU = static_cast<u32>(a.nU);
+  if ((grp.fmt_b >> mi) & 1)
+    gemv1_rows<FB, XH, R>(a, W, xg, yg, Mg, wg0, nU / ub * FmtInfo<FB>::BB);
+  else
+    gemv1_rows<FA, XH, R>(a, W, xg, yg, Mg, wg0, nU / ua * FmtInfo<FA>::BB);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1208,6 +1240,8 @@ struct Tables {
   GemvGroupKernel one[kNumFormats][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
   int one_regs[kNumFormats][2][3];    // their VGPRs per lane (512 when unknown)
   GemvGroupKernel multi[kNumFormats][2];   // [format][fp16 activations], one row per thread
+  GemvGroupKernel pair[2][3];             // k_gemv1_pair<Q4_K, Q6_K>: [fp16 activations][rows per thread]
+  int pair_regs[2][3];
   GemvKernel multi_id[kNumFormats][2];
   GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
   template <int F>
@@ -1231,13 +1265,22 @@ struct Tables {
     fill_format<FMT_Q2_K>();
     fill_format<FMT_Q3_K>();
     fill_format<FMT_Q5_K>();
-    for (int f = 0; f < kNumFormats; ++f)
-      for (int h = 0; h < 2; ++h)
-        for (int r = 0; r < 3; ++r) {
-          hipFuncAttributes at{};
-          const bool ok = hipFuncGetAttributes(&at, reinterpret_cast<const void*>(one[f][h][r])) == hipSuccess;
-          one_regs[f][h][r] = ok && at.numRegs > 0 ? at.numRegs : 512;
-        }
+    pair[0][0] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, false, 1>;
+    pair[0][1] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, false, 2>;
+    pair[0][2] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, false, 4>;
+    pair[1][0] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, true, 1>;
+    pair[1][1] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, true, 2>;
+    pair[1][2] = k_gemv1_pair<FMT_Q4_K, FMT_Q6_K, true, 4>;
+    auto regs = [](GemvGroupKernel k) {
+      hipFuncAttributes at{};
+      const bool ok = hipFuncGetAttributes(&at, reinterpret_cast<const void*>(k)) == hipSuccess;
+      return ok && at.numRegs > 0 ? at.numRegs : 512;
+    };
+    for (int h = 0; h < 2; ++h)
+      for (int r = 0; r < 3; ++r) {
+        for (int f = 0; f < kNumFormats; ++f) one_regs[f][h][r] = regs(one[f][h][r]);
+        pair_regs[h][r] = regs(pair[h][r]);
+      }
   }
 };
 
@@ -1299,7 +1342,7 @@ struct OneShape {
   size_t lds;
 };
 
-bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o) {
+bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o, const int (*fam_regs)[3] = nullptr) {
   const int ipr = nU / kRuns[fmt];
   if (ipr > 512 || ipr < 1) return false;
   const int Gmax = 512 / ipr;
@@ -1308,7 +1351,7 @@ bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o) {
   auto two_fit = [&](int r, int ri) {
     const int G2 = (want + 2 * r - 1) / (2 * r);
     const int thr = (G2 * ipr + 63) / 64 * 64;
-    const int regs = (tables().one_regs[fmt][xh][ri] + 7) / 8 * 8;
+    const int regs = ((fam_regs ? fam_regs[xh][ri] : tables().one_regs[fmt][xh][ri]) + 7) / 8 * 8;
     const int waves_per_simd = (thr / 64 + 3) / 4;  // one workgroup's waves on each SIMD
     return G2 <= Gmax && 4 * G2 * ipr >= 3 * thr && 2 * waves_per_simd * regs <= 512;
   };
@@ -1331,7 +1374,7 @@ bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o) {
 }
 
 hipError_t launch_one(int fmt, int nU, int64_t row_bytes, const OneShape& o, const GemvGroup& grp, int x_f16,
-                      hipStream_t st) {
+                      hipStream_t st, bool pair = false) {
   GemvArgs a{};
   a.W = grp.W[0];  // a single matrix is read from these fields
   a.x = grp.x[0];
@@ -1344,8 +1387,8 @@ hipError_t launch_one(int fmt, int nU, int64_t row_bytes, const OneShape& o, con
   a.chunk_units = o.Ge;
   a.x_f16 = x_f16;
   a.N = 1;
-  hipLaunchKernelGGL(tables().one[fmt][x_f16 ? 1 : 0][o.ri], dim3(grp.first[grp.n]), dim3(o.threads), o.lds, st, a,
-                     grp);
+  GemvGroupKernel k = pair ? tables().pair[x_f16 ? 1 : 0][o.ri] : tables().one[fmt][x_f16 ? 1 : 0][o.ri];
+  hipLaunchKernelGGL(k, dim3(grp.first[grp.n]), dim3(o.threads), o.lds, st, a, grp);
   return hipGetLastError();
 }
 
@@ -1420,16 +1463,26 @@ hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, fl
   if (n < 1 || n > kGemvGroupMax || N < 1) return hipErrorNotSupported;
   const MatDesc& m0 = *ms[0];
   int64_t rows = 0;
+  int fmt_b = 0;
+  bool mixed = false;
   for (int i = 0; i < n; ++i) {
-    if (ms[i]->fmt != m0.fmt || ms[i]->K != m0.K || ms[i]->blocks == nullptr) return hipErrorNotSupported;
+    if (ms[i]->K != m0.K || ms[i]->blocks == nullptr) return hipErrorNotSupported;
+    if (ms[i]->fmt != m0.fmt) mixed = true;
+    if (ms[i]->fmt == FMT_Q6_K) fmt_b |= 1 << i;
     rows += ms[i]->M;
+  }
+  if (mixed) {  // only Q4_K with Q6_K, at one token (k_gemv1_pair)
+    if (N != 1) return hipErrorNotSupported;
+    for (int i = 0; i < n; ++i)
+      if (ms[i]->fmt != FMT_Q4_K && ms[i]->fmt != FMT_Q6_K) return hipErrorNotSupported;
   }
   const int nU = static_cast<int>(m0.K / 32);
   OneShape o;
   MultiShape mo;
   int RW;
   if (N == 1) {
-    if (!one_shape(m0.fmt, nU, rows, x_f16, m0.cus, o)) return hipErrorNotSupported;
+    if (!one_shape(mixed ? FMT_Q4_K : m0.fmt, nU, rows, x_f16, m0.cus, o, mixed ? tables().pair_regs : nullptr))
+      return hipErrorNotSupported;
     RW = o.RW;
   } else {
     if (!multi_shape(m0.fmt, nU, rows, N, x_f16, m0.cus, mo)) return hipErrorNotSupported;
@@ -1448,6 +1501,11 @@ hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, fl
   }
   if (wg > INT_MAX) return hipErrorNotSupported;
   grp.first[n] = static_cast<int>(wg);
+  grp.fmt_b = mixed ? fmt_b : 0;
+  if (mixed) {
+    // (the formats' row bytes differ: the pair kernel derives each from its format)
+    return launch_one(FMT_Q4_K, nU, 0, o, grp, x_f16, st, true);
+  }
   const int64_t rb = static_cast<int64_t>(m0.row_bytes);
   return N == 1 ? launch_one(m0.fmt, nU, rb, o, grp, x_f16, st) : launch_multi(m0.fmt, nU, rb, N, mo, grp, x_f16, st);
 }
