@@ -10,18 +10,21 @@ Headline (one JSON line on stdout): quantized-weight GB/s of the matrix-vector
 path at one token on the seven projections of a Qwen3-Embedding-4B decoder
 layer (Q4_K: 4096x2560, 1024x2560, 2560x4096, 9728x2560 twice; Q6_K:
 1024x2560, 2560x9728; random N(0, 0.02^2) weights, N(0, 1) fp32 activations).
-A step is one pass over the layer: seven GEMV launches.  Weights rotate
+A step is one pass over the layer: the seven projections in four calls as a
+decode step makes them (q+k+v and gate+up read one input each, so they share a
+qmm_gemv_group call; attn_output and ffn_down alone), four launches of the
+one-token GEMV kernel.  Weights rotate
 through copies totalling more than 1 GiB, so each step streams them from HBM
 rather than the 256 MB Infinity Cache.  Steps are timed as replays of HIP
 graphs captured from the library's launches (the graph only removes host
 launch overhead; the kernels are the ones an eager call runs).
 
 Also reported:
-  roofline      the step's kernel: all seven launches are the one-token GEMV
-                kernel (k_gemv1, a Q4_K and a Q6_K instance), run back to back,
-                so its average launch duration is the HIP-event-timed step over
-                seven launches, and its algorithmic bytes per launch the layer's
-                weights + x + y over seven; against 8 TB/s.  "traffic" from the
+  roofline      the step's kernel: all four launches are the one-token GEMV
+                kernel (k_gemv1 and its Q4_K+Q6_K form k_gemv1_pair), run back to
+                back, so its average launch duration is the HIP-event-timed step
+                over four launches, and its algorithmic bytes per launch the
+                layer's weights + x + y over four; against 8 TB/s.  "traffic" from the
                 rocprofv3 counter summary in profiles/ when it was taken on the
                 current kernel source, else null.
   cpu_baseline  the CPU oracle (NumPy dequantization + fp64 matmul) on a bounded
@@ -198,6 +201,15 @@ def launch_sets(mats, call, N):
     return out
 
 
+def headline_launches(W):
+    """Launches of one headline step and the mean algorithmic bytes (quantized weights
+    + fp32 x + fp32 y) per launch."""
+    mats = [{"fmt": f, "K": K, "M": M} for _, M, K, f in W.DECODE_SHAPES]
+    n = sum(len(launch_sets(mats, c, 1)) for c in DECODE_GROUPS)
+    alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M for _, M, K, fmt in W.DECODE_SHAPES)
+    return n, alg / n
+
+
 def decode_layer(torch, q, W, args):
     t0 = time.time()
     mats = [W.decode_weights(i) for i in range(len(W.DECODE_SHAPES))]
@@ -262,8 +274,8 @@ def decode_layer(torch, q, W, args):
                     "isolated_us": round(float(mean_us[j]), 3),
                     "isolated_weight_gbs": round(m["blob"].size / (mean_us[j] * 1e-6) / 1e9, 1)}
                    for j, m in enumerate(mats)]
-    # the roofline's kernel: every launch of the step is k_gemv1 (Q4_K or Q6_K instance)
-    # and they run back to back, so the event-timed step over its launches is their
+    # the roofline's kernel: every launch of the step is the one-token GEMV (k_gemv1, or
+    # k_gemv1_pair for the Q4_K + Q6_K call) and they run back to back, so the event-timed step over its launches is their
     # average duration (the rocprofv3 trace in profiles/ checks this against
     # per-dispatch durations)
     step_us = ev_ms / args.steps * 1e3
@@ -712,16 +724,15 @@ def summarize_trace(root):
     gemv = []
     for (name, grid, wg), ds in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{name}` | {grid} | {wg} | {len(ds)} | {np.median(ds):.2f} | {np.mean(ds):.2f} |")
-        if "k_gemv1<" in name:
+        if "k_gemv1" in name:
             gemv.extend(ds)
     if not gemv:  # another workload: the table only
         print("\n".join(lines))
         return
-    alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M
-              for _, M, K, fmt in W.DECODE_SHAPES) / len(W.DECODE_SHAPES)
+    nl, alg = headline_launches(W)
     mean = float(np.mean(gemv)) if gemv else float("nan")
-    lines += ["", f"All one-token GEMV dispatches (k_gemv1, both instances): {len(gemv)}, mean {mean:.3f} us; "
-              f"{len(W.DECODE_SHAPES)} per step -> {len(W.DECODE_SHAPES) * mean:.2f} us of kernel time per step; "
+    lines += ["", f"All one-token GEMV dispatches (k_gemv1 and k_gemv1_pair): {len(gemv)}, mean {mean:.3f} us; "
+              f"{nl} per step -> {nl * mean:.2f} us of kernel time per step; "
               f"algorithmic bytes per launch {alg:.0f} -> {alg / (mean * 1e-6) / 1e9:.1f} GB/s "
               f"= {alg / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS:.4f} of 8 TB/s.", "",
               "Machine-readable:", "",
@@ -759,7 +770,7 @@ def summarize_sq(dirs, top=8):
 
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     """Markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE passes over this benchmark's
-    headline (kernels k_gemv1) and over --copy-probe (the calibration copy)."""
+    headline (kernels k_gemv1, k_gemv1_pair) and over --copy-probe (the calibration copy)."""
     from qmm_synth import workloads as W
 
     def per_dispatch(root, counter, match):
@@ -771,23 +782,22 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
             vals[key] = vals.get(key, 0.0) + float(_col(r, "Counter_Value"))
         return list(vals.values())
 
-    f = per_dispatch(fetch_dir, "FETCH_SIZE", "k_gemv1<")
-    w = per_dispatch(write_dir, "WRITE_SIZE", "k_gemv1<")
+    f = per_dispatch(fetch_dir, "FETCH_SIZE", "k_gemv1")
+    w = per_dispatch(write_dir, "WRITE_SIZE", "k_gemv1")
     cf = per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     cw = per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     moved_kib = (256 << 20) / 1024
     ff, wf = moved_kib / float(np.mean(cf)), moved_kib / float(np.mean(cw))
     traffic = (float(np.mean(f)) * ff + float(np.mean(w)) * wf) * 1024
-    alg = sum(M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256 + 4 * K + 4 * M
-              for _, M, K, fmt in W.DECODE_SHAPES) / len(W.DECODE_SHAPES)
+    nl, alg = headline_launches(W)
     lines = ["| quantity | value |", "|---|---|",
-             f"| k_gemv1 dispatches (fetch pass / write pass) | {len(f)} / {len(w)} |",
+             f"| k_gemv1 / k_gemv1_pair dispatches (fetch pass / write pass) | {len(f)} / {len(w)} |",
              f"| FETCH_SIZE per dispatch (KiB, raw) | {np.mean(f):.1f} |",
              f"| WRITE_SIZE per dispatch (KiB, raw) | {np.mean(w):.2f} |",
              f"| copy probe: FETCH_SIZE / WRITE_SIZE for {moved_kib:.0f} KiB moved | {np.mean(cf):.1f} / {np.mean(cw):.1f} KiB |",
              f"| calibration factor fetch / write | {ff:.4f} / {wf:.4f} |",
              f"| HBM traffic per launch (bytes, calibrated) | {traffic:.0f} |",
-             f"| algorithmic bytes per launch (weights + x + y, mean of the seven) | {alg:.0f} |",
+             f"| algorithmic bytes per launch (weights + x + y of the layer over its {nl} launches) | {alg:.0f} |",
              f"| traffic / algorithmic | {traffic / alg:.3f} |",
              "", "Machine-readable (read by bench.py; valid only for this kernel source):", "",
              f"- source_digest: {source_digest()}",
@@ -885,7 +895,7 @@ def main():
             "calls": head["calls"],
         },
         "roofline": {
-            "kernel": "qmm::k_gemv1 (one-token GEMV; Q4_K and Q6_K instances; the step's launches: "
+            "kernel": "qmm::k_gemv1 / k_gemv1_pair (one-token GEMV; the step's launches: "
                       + ", ".join("+".join(c) for c in head["launch_sets"]) + ")",
             "bound": "hbm",
             "achieved": round(kern["achieved_gbs"], 1),
