@@ -1488,20 +1488,28 @@ hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, fl
     if (!multi_shape(m0.fmt, nU, rows, N, x_f16, m0.cus, mo)) return hipErrorNotSupported;
     RW = mo.RW;
   }
+  // in a mixed launch the Q6_K matrices (the dearer decode) take the first workgroups,
+  // so they are not the launch's tail (about 1% of the decode step)
+  int order[kGemvGroupMax], k = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int i = 0; i < n; ++i)
+      if (((fmt_b >> i) & 1) == (pass == 0 ? 1 : 0)) order[k++] = i;
   GemvGroup grp{};
   grp.n = n;
+  grp.fmt_b = 0;
   int64_t wg = 0;
-  for (int i = 0; i < n; ++i) {
-    grp.W[i] = ms[i]->blocks;
-    grp.x[i] = xs[i];
-    grp.y[i] = ys[i];
-    grp.M[i] = static_cast<int>(ms[i]->M);
-    grp.first[i] = static_cast<int>(wg);
+  for (int e = 0; e < n; ++e) {
+    const int i = mixed ? order[e] : e;
+    grp.W[e] = ms[i]->blocks;
+    grp.x[e] = xs[i];
+    grp.y[e] = ys[i];
+    grp.M[e] = static_cast<int>(ms[i]->M);
+    grp.first[e] = static_cast<int>(wg);
+    if (mixed && ((fmt_b >> i) & 1)) grp.fmt_b |= 1 << e;
     wg += (ms[i]->M + RW - 1) / RW;
   }
   if (wg > INT_MAX) return hipErrorNotSupported;
   grp.first[n] = static_cast<int>(wg);
-  grp.fmt_b = mixed ? fmt_b : 0;
   if (mixed) {
     // (the formats' row bytes differ: the pair kernel derives each from its format)
     return launch_one(FMT_Q4_K, nU, 0, o, grp, x_f16, st, true);
