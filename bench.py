@@ -688,6 +688,26 @@ def calibrate(torch, W):
         del buf
         torch.cuda.empty_cache()
     out["streaming_read"] = reads
+    # torch's dense fp16 GEMM (hipBLASLt) on the decode-layer shapes: the same products
+    # with the weights already fp16, y = x W^T with W^T stored [K, M] (no transposed view),
+    # two weight copies alternating
+    dense = []
+    for n in (512, 2048):
+        tot_us, tot_fl = 0.0, 0.0
+        for name, M, K, fmt in W.DECODE_SHAPES:
+            wts = [torch.randn(K, M, device="cuda").mul_(0.02).half() for _ in range(2)]
+            x = torch.randn(n, K, device="cuda").half()
+            ys = [torch.empty(n, M, device="cuda", dtype=torch.float16) for _ in range(2)]
+            g = capture(torch, lambda: [torch.mm(x, wts[c % 2], out=ys[c % 2]) for c in range(8)])
+            us = time_graph(torch, g, 5) * 1e3 / 8
+            del g, wts, ys
+            fl = 2.0 * n * M * K
+            tot_us += us
+            tot_fl += fl
+            dense.append({"n": n, "name": name, "us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 1)})
+        dense.append({"n": n, "name": "layer", "us": round(tot_us, 2), "tflops": round(tot_fl / (tot_us * 1e-6) / 1e12, 1)})
+        torch.cuda.empty_cache()
+    out["dense_fp16_gemm"] = dense
     return out
 
 

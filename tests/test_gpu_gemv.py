@@ -173,3 +173,28 @@ def test_gemv_group_edge_cases():
     xa_bad = (ctypes.c_void_p * 1)(x.data_ptr() + 4)
     assert lib.qmm_gemv_group(ha, xa_bad, L.DTYPES["f32"], 1, ya, 1, None) == -4
     assert lib.qmm_gemv_group(ha, xa, L.DTYPES["f32"], 1, ya, 65, None) == -1
+
+
+@pytest.mark.parametrize("scale_log2", [-96, -112])
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0", "q4_k", "q6_k", "a4g64", "q5_k", "q3_k"])
+def test_gemv_small_activations(fmt, scale_log2):
+    """fp32 activations of magnitude 2^-96 and 2^-112 (normal, far below any real
+    activation): the matrix-vector paths multiply codes as fp16 subnormals
+    (code * 2^-24) with coefficients scaled by 2^24, so their products are
+    2^-24-scaled copies of the plain chain's; they stay normal fp32 numbers down to
+    |x| ~ 2^-100, and below that lose only absolute precision of order 2^-149 per
+    product, far inside 1e-5 * S at these scales (one-token, few-token and general
+    paths)."""
+    bw = oracle.block_weights(fmt)
+    K = 2560 if 2560 % bw == 0 else 2048
+    M = 130
+    blob = make_matrix(fmt, M, K, [47, scale_log2])
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    for N in (1, 3, 32):
+        g = np.random.default_rng([48, N, -scale_log2])
+        x = (g.standard_normal((N, K)) * 2.0 ** scale_log2).astype(np.float32)
+        assert np.all(np.abs(x[x != 0]) >= np.finfo(np.float32).tiny)  # normal fp32 inputs
+        y = to_host(qm.gemv(to_dev(x)))
+        assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
+                      f"gemv {fmt} N={N} |x|~2^{scale_log2}")
