@@ -188,12 +188,13 @@ def test_gemv_small_activations(fmt, scale_log2):
     bw = oracle.block_weights(fmt)
     K = 2560 if 2560 % bw == 0 else 2048
     M = 130
-    blob = make_matrix(fmt, M, K, [47, scale_log2])
+    blob = make_matrix(fmt, M, K, [47, -scale_log2])
     w = oracle.dequantize(fmt, blob, M, K)
     qm = q.QMatrix(to_dev(blob), fmt, M, K)
     for N in (1, 3, 32):
         g = np.random.default_rng([48, N, -scale_log2])
-        x = (g.standard_normal((N, K)) * 2.0 ** scale_log2).astype(np.float32)
+        z = g.standard_normal((N, K))
+        x = (np.sign(z) * np.maximum(np.abs(z), 2.0 ** -10) * 2.0 ** scale_log2).astype(np.float32)
         assert np.all(np.abs(x[x != 0]) >= np.finfo(np.float32).tiny)  # normal fp32 inputs
         y = to_host(qm.gemv(to_dev(x)))
         assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
