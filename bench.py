@@ -455,12 +455,30 @@ def extra_small_decode(torch, q, W, args):
         del g
         flops = 2 * n * sum(m["M"] * m["K"] for m in mats)
         tflops = flops / (us * 1e-6) / 1e12
-        res.append({"n": n, "us_per_layer": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
-                    "frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                    "tflops": tflops,
-                    "frac_valu_fma": tflops / VALU_F32_FMA_TFLOPS,
-                    "frac_valu_packed": tflops / VALU_F32_PACKED_TFLOPS,
-                    "binding": "hbm" if n <= 4 else "alu"})
+        row = {"n": n, "us_per_layer": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
+               "frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+               "tflops": tflops,
+               "frac_valu_fma": tflops / VALU_F32_FMA_TFLOPS,
+               "frac_valu_packed": tflops / VALU_F32_PACKED_TFLOPS,
+               "binding": "hbm" if n <= 4 else "alu"}
+        if n >= 4:
+            # the same layer through the matrix cores (qmm_gemm_ws, auto tile; fp16 staging of
+            # the weights, so a looser bound than the matrix-vector path's): the path a caller
+            # may take from a few tokens on
+            wss = []
+            for j in range(len(mats)):
+                nb = q.qmm_gemm_workspace_bytes(hs[0][j].handle, n)
+                wss.append(torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None)
+
+            def fm():
+                for c in range(layers):
+                    for j in range(len(mats)):
+                        q.qmm_gemm_ws(hs[c][j].handle, xs[j], n, ys[j], 0, wss[j])
+            g = capture(torch, fm)
+            us_mm = time_graph(torch, g, args.rounds) * 1e3 / layers
+            del g, wss
+            row["matrix_core_us_per_layer"] = us_mm
+        res.append(row)
     return {"workload": "Qwen3-0.6B layer, A4G64 (group 64), fp16 tokens; q+k+v and gate+up share qmm_gemv_group "
                         "calls (one launch each at one token)", "layer_weight_bytes": wbytes,
             "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
