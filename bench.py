@@ -86,6 +86,8 @@ def parse():
     p.add_argument("--copy-probe", action="store_true", help="only run a 256 MiB device copy (counter calibration)")
     p.add_argument("--calibrate", action="store_true",
                    help="only time an empty kernel and plain streaming reads of the decode-layer projection sizes")
+    p.add_argument("--table-only", action="store_true",
+                   help="with --summarize-trace: the per-kernel table only (a run of another workload)")
     p.add_argument("--summarize-trace", default=None, metavar="DIR",
                    help="print a markdown summary of a rocprofv3 kernel trace of this benchmark (no GPU needed)")
     p.add_argument("--summarize-sq", nargs="+", default=None, metavar="DIR",
@@ -745,8 +747,9 @@ def _col(row, *names):
     raise KeyError(names)
 
 
-def summarize_trace(root):
-    """Markdown summary of a rocprofv3 --kernel-trace run of this benchmark."""
+def summarize_trace(root, table_only=False):
+    """Markdown summary of a rocprofv3 --kernel-trace run of this benchmark (with the
+    headline's one-token GEMV figures unless table_only: a run of another workload)."""
     from qmm_synth import workloads as W
     rows = _csv_rows(root, "kernel_trace.csv")
     if not rows:
@@ -764,7 +767,7 @@ def summarize_trace(root):
         lines.append(f"| `{name}` | {grid} | {wg} | {len(ds)} | {np.median(ds):.2f} | {np.mean(ds):.2f} |")
         if "k_gemv1" in name:
             gemv.extend(ds)
-    if not gemv:  # another workload: the table only
+    if not gemv or table_only:  # another workload: the table only
         print("\n".join(lines))
         return
     nl, alg = headline_launches(W)
@@ -860,7 +863,7 @@ def copy_probe(torch):
 def main():
     args = parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.table_only)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
