@@ -683,7 +683,15 @@ def calibrate(torch, W):
     out["empty_kernel_us"] = time_graph(torch, g, 5) * 1e3 / 1000
     del g
     sizes = [(name, M * {"q4_k": 144, "q6_k": 210}[fmt] * K // 256) for name, M, K, fmt in W.DECODE_SHAPES]
-    sizes.append(("whole layer", sum(b for _, b in sizes)))
+    per = dict(sizes)
+    # the headline step's launch sets (grouped calls) and the whole layer in one launch
+    mats = [{"fmt": f, "K": K, "M": M, "name": n} for n, M, K, f in W.DECODE_SHAPES]
+    for c in DECODE_GROUPS:
+        for st in launch_sets(mats, c, 1):
+            if len(st) > 1:
+                names = [mats[j]["name"] for j in st]
+                sizes.append(("+".join(names), sum(per[n] for n in names)))
+    sizes.append(("whole layer", sum(per.values())))
     reads = []
     for name, nbytes in sizes:
         per = (nbytes + 4095) // 4096 * 4096
