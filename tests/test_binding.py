@@ -115,3 +115,24 @@ def test_host_tensors_are_refused(handle, stack_handle):
     expect(lambda: q.qmm_gemm(handle, f32(9, K).half(), 9, f32(9, M)), "device tensor")
     ids = torch.zeros((2, 2), dtype=torch.int32)
     expect(lambda: q.qmm_gemm_id(stack_handle, f32(2, 2, K), 2, 2, 1, ids, f32(2, 2, M)), "device tensor")
+
+
+def test_gemv_group_checks(handle, stack_handle):
+    f16 = lambda *s: torch.zeros(s, dtype=torch.float16)
+    q.qmm_gemv_group([], [], 1, [])  # nothing to do: no check can fail, nothing is called
+    expect(lambda: q.qmm_gemv_group([handle], [f32(1, K)], 1, []), "same length")
+    expect(lambda: q.qmm_gemv_group([handle, handle], [f32(1, K), f16(1, K)], 1, [f32(1, M), f32(1, M)]),
+           "same dtype")
+    expect(lambda: q.qmm_gemv_group([handle], [f32(2, K)], 1, [f32(1, M)]), r"xs\[0\] has shape")
+    expect(lambda: q.qmm_gemv_group([handle, handle], [f32(1, K), f32(1, K)], 1, [f32(1, M), f32(1, M + 1)]),
+           r"ys\[1\] has shape")
+    expect(lambda: q.qmm_gemv_group([ctypes.c_void_p(0x1234)], [f32(1, K)], 1, [f32(1, M)]), "unknown handle")
+    # a handle on another device
+    other = ctypes.c_void_p(0x5EEE0)
+    q._HANDLES[other.value] = q._Meta(q.TYPES["q4_k"], M, K, 1, 1)
+    try:
+        expect(lambda: q.qmm_gemv_group([handle, other], [f32(1, K)] * 2, 1, [f32(1, M)] * 2), "same device")
+    finally:
+        q._HANDLES.pop(other.value, None)
+    # shapes right, host tensors: refused for placement, still before any C call
+    expect(lambda: q.qmm_gemv_group([handle], [f32(1, K)], 1, [f32(1, M)]), "device tensor")
