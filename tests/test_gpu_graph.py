@@ -25,14 +25,20 @@ def test_graph_replays_match_eager():
     x70 = to_dev(g.standard_normal((70, K)).astype(np.float16))
     ids = to_dev(np.stack([g.choice(E, 4, replace=False) for _ in range(6)]).astype(np.int32))
     xid = to_dev(g.standard_normal((6, 4, Ke)).astype(np.float32))
+    v6 = q.QMatrix(to_dev(make_matrix("q6_k", 200, K, [84])), "q6_k", 200, K)
     outs = [torch.empty((1, M), device="cuda"), torch.empty((5, M), device="cuda"),
-            torch.empty((70, M), device="cuda"), torch.empty((6, 4, Me), device="cuda")]
+            torch.empty((70, M), device="cuda"), torch.empty((6, 4, Me), device="cuda"),
+            torch.empty((1, M), device="cuda"), torch.empty((1, 200), device="cuda"),
+            torch.empty((5, M), device="cuda"), torch.empty((5, M), device="cuda")]
 
     def step():
         q.qmm_gemv(dense.handle, x1, 1, outs[0])
         q.qmm_gemv(dense.handle, x5, 5, outs[1])
         q.qmm_gemm(dense.handle, x70, 70, outs[2], 0)
         q.qmm_gemm_id(stack.handle, xid, 6, 4, 1, ids, outs[3])
+        # grouped: a Q4_K + Q6_K one-token launch and a few-token launch of two Q4_K
+        q.qmm_gemv_group([dense.handle, v6.handle], [x1, x1], 1, [outs[4], outs[5]])
+        q.qmm_gemv_group([dense.handle, dense.handle], [x5, x5], 5, [outs[6], outs[7]])
 
     step()
     eager = [to_host(o).copy() for o in outs]
@@ -55,4 +61,7 @@ def test_graph_replays_match_eager():
         got = [to_host(o) for o in outs]
         for a, b in zip(eager, got):
             assert count_differences(a, b) == 0, f"replay {rep}"
+        # the grouped outputs are the single calls' bits
+        assert count_differences(got[4], got[0]) == 0 and count_differences(got[6], got[1]) == 0
+        assert count_differences(got[7], got[1]) == 0
         _ = (x5 * 2).sum().item()   # unrelated eager work between replays
