@@ -1216,9 +1216,10 @@ constexpr void fill_id(GemvKernel* t, std::integer_sequence<int, BI...>) {
 }
 
 template <int F>
-constexpr void fill_one(GemvGroupKernel (&t)[2][3]) {
+constexpr void fill_one(GemvGroupKernel (&t)[2][4]) {
   t[0][0] = k_gemv1<F, false, 1>; t[0][1] = k_gemv1<F, false, 2>; t[0][2] = k_gemv1<F, false, 4>;
   t[1][0] = k_gemv1<F, true, 1>;  t[1][1] = k_gemv1<F, true, 2>;  t[1][2] = k_gemv1<F, true, 4>;
+  t[0][3] = k_gemv1<F, false, 8>; t[1][3] = k_gemv1<F, true, 8>;
 }
 
 template <int F>
@@ -1237,8 +1238,8 @@ constexpr void fill_multi(GemvGroupKernel (&t)[2], GemvKernel (&ti)[2]) {
 struct Tables {
   GemvKernel dense[kNumFormats][kNumBuckets];
   GemvKernel id[kNumFormats][kIdBuckets];
-  GemvGroupKernel one[kNumFormats][2][3];  // [format][fp16 activations][rows per thread 1, 2, 4]
-  int one_regs[kNumFormats][2][3];    // their VGPRs per lane (512 when unknown)
+  GemvGroupKernel one[kNumFormats][2][4];  // [format][fp16 activations][rows per thread 1, 2, 4, 8]
+  int one_regs[kNumFormats][2][4];    // their VGPRs per lane (512 when unknown)
   GemvGroupKernel multi[kNumFormats][2];   // [format][fp16 activations], one row per thread
   GemvGroupKernel pair[2][3];             // k_gemv1_pair<Q4_K, Q6_K>: [fp16 activations][rows per thread]
   int pair_regs[2][3];
@@ -1277,9 +1278,9 @@ struct Tables {
       return ok && at.numRegs > 0 ? at.numRegs : 512;
     };
     for (int h = 0; h < 2; ++h)
-      for (int r = 0; r < 3; ++r) {
+      for (int r = 0; r < 4; ++r) {
         for (int f = 0; f < kNumFormats; ++f) one_regs[f][h][r] = regs(one[f][h][r]);
-        pair_regs[h][r] = regs(pair[h][r]);
+        if (r < 3) pair_regs[h][r] = regs(pair[h][r]);
       }
   }
 };
@@ -1334,9 +1335,11 @@ namespace {
 // R rows to compute.  Two workgroups per CU when R in {1, 2} makes G * ipr fill at
 // least 3/4 of their waves and the kernel's registers let both sit on the CU at once
 // (the second workgroup's loads and products overlap the first one's reduction);
-// otherwise about one workgroup per CU, R in {1, 2, 4} the smallest that covers
-// M / 256 rows.  False when the activation image and partials do not fit the LDS
-// budget (the general path takes such shapes).
+// otherwise about one workgroup per CU, R in {1, 2, 4, 8} the smallest that covers
+// M / 256 rows (at 8 rows per thread the decode layer's ffn_gate + ffn_up launch takes
+// 244 workgroups instead of 406 at 4, two of which a CU could not hold: the decode
+// step 32.1 -> 31.0 us).  False when the activation image and partials do not fit
+// the LDS budget (the general path takes such shapes).
 struct OneShape {
   int ri, Ge, RW, threads;
   size_t lds;
@@ -1361,8 +1364,9 @@ bool one_shape(int fmt, int nU, int64_t M, int x_f16, int cus, OneShape& o, cons
     o.ri = R - 1;
     Ge = (want + 2 * R - 1) / (2 * R);
   } else {
-    R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : 4);
-    o.ri = R == 1 ? 0 : (R == 2 ? 1 : 2);
+    // (no 8-row form of the mixed-format kernel)
+    R = want <= Gmax ? 1 : (want <= 2 * Gmax ? 2 : (want <= 4 * Gmax || fam_regs ? 4 : 8));
+    o.ri = R == 1 ? 0 : (R == 2 ? 1 : (R == 4 ? 2 : 3));
     Ge = (want + R - 1) / R;
   }
   if (Ge > Gmax) Ge = Gmax;

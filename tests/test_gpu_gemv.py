@@ -199,3 +199,22 @@ def test_gemv_small_activations(fmt, scale_log2):
         y = to_host(qm.gemv(to_dev(x)))
         assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
                       f"gemv {fmt} N={N} |x|~2^{scale_log2}")
+
+
+@pytest.mark.parametrize("fmt,M,K", [("q4_k", 13000, 2560), ("q6_k", 4000, 9728)])
+def test_gemv_eight_rows_per_thread(fmt, M, K):
+    """Tall one-token calls, past four rows per thread at one workgroup per CU: the
+    eight-row kernel, on every row (its results within the bound, sampled rows against
+    the oracle), fp32 and fp16 activations, and a ragged last workgroup."""
+    blob = make_matrix(fmt, M, K, [49, M])
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    rb = oracle.row_bytes(fmt, K)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.random.default_rng([50, M]).integers(0, M, 200),
+                                     np.arange(M - 40, M)]))
+    w = oracle.dequantize(fmt, blob.reshape(M, rb)[rows].reshape(-1), len(rows), K)
+    for xdt in (np.float32, np.float16):
+        x = np.random.default_rng([51, M]).standard_normal((1, K)).astype(np.float32).astype(xdt)
+        y = to_host(qm.gemv(to_dev(x)))
+        assert np.all(np.isfinite(y))
+        assert_within(y[:, rows], oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
+                      f"gemv {fmt} M={M} K={K} {np.dtype(xdt).name}")
