@@ -457,16 +457,22 @@ def extra_small_decode(torch, q, W, args):
         del g
         flops = 2 * n * sum(m["M"] * m["K"] for m in mats)
         tflops = flops / (us * 1e-6) / 1e12
+        # 1..4 tokens: the vector kernels, one fp32 fma per weight and token (fp32 vector
+        # ceiling); 5..32: the matrix-core kernel (codes and activations as exact fp16
+        # operands), whose products take a small share of the fp16 peak: the weight
+        # stream is the roofline there
+        mc = n >= 5
         row = {"n": n, "us_per_layer": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
                "frac_hbm": wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                "tflops": tflops,
-               "frac_valu_fma": tflops / VALU_F32_FMA_TFLOPS,
-               "frac_valu_packed": tflops / VALU_F32_PACKED_TFLOPS,
-               "binding": "hbm" if n <= 4 else "alu"}
+               "path": "matrix cores" if mc else "vector",
+               "frac_valu_fma": None if mc else tflops / VALU_F32_FMA_TFLOPS,
+               "frac_valu_packed": None if mc else tflops / VALU_F32_PACKED_TFLOPS,
+               "frac_mfma_f16": tflops / MFMA_F16_PEAK_TFLOPS if mc else None,
+               "binding": "hbm"}
         if n >= 4:
-            # the same layer through the matrix cores (qmm_gemm_ws, auto tile; fp16 staging of
-            # the weights, so a looser bound than the matrix-vector path's): the path a caller
-            # may take from a few tokens on
+            # the same layer through the matrix-matrix path (qmm_gemm_ws, auto tile; fp16
+            # staging of the weights, so a looser bound than the matrix-vector path's)
             wss = []
             for j in range(len(mats)):
                 nb = q.qmm_gemm_workspace_bytes(hs[0][j].handle, n)
@@ -479,7 +485,7 @@ def extra_small_decode(torch, q, W, args):
             g = capture(torch, fm)
             us_mm = time_graph(torch, g, args.rounds) * 1e3 / layers
             del g, wss
-            row["matrix_core_us_per_layer"] = us_mm
+            row["gemm_us_per_layer"] = us_mm
         res.append(row)
     return {"workload": "Qwen3-0.6B layer, A4G64 (group 64), fp16 tokens; q+k+v and gate+up share qmm_gemv_group "
                         "calls (one launch each at one token)", "layer_weight_bytes": wbytes,

@@ -109,11 +109,12 @@ def test_gemv_tokens_long_rows(fmt, xdtype):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_gemv_tokens_match_single_token_calls(fmt):
-    """Every path sums the same unit partials in the same order, so a call with N
-    tokens returns, bit for bit, what N one-token calls return."""
+    """Every vector path sums the same unit partials in the same order, so a call with N
+    tokens returns, bit for bit, what N one-token calls return (fp16 tokens of 4-bit
+    affine groups at 5..32 tokens take the matrix cores instead: see below)."""
     M, K, N = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048, 11
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [48])), fmt, M, K)
-    for xdtype in (np.float32, np.float16):
+    for xdtype in (np.float32,) if fmt == "a4g64" else (np.float32, np.float16):
         x = to_dev(np.random.default_rng(48).standard_normal((N, K)).astype(xdtype))
         full = to_host(qm.gemv(x))
         for t in range(N):
@@ -218,3 +219,57 @@ def test_gemv_eight_rows_per_thread(fmt, M, K):
         assert np.all(np.isfinite(y))
         assert_within(y[:, rows], oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL,
                       f"gemv {fmt} M={M} K={K} {np.dtype(xdt).name}")
+
+
+# fp16 tokens of 4-bit affine groups at 5..32 tokens take the matrix-core kernel: rows of
+# K = 64 .. 4096 (one to four groups per wave, a last wave with fewer groups, one wave),
+# a K past its range (the vector path), rows that are not a multiple of 16, and one or two
+# 16-token blocks
+@pytest.mark.parametrize("N", [5, 8, 16, 17, 32])
+def test_gemv_matrix_cores_fp16(N):
+    for M, K in ((67, 64), (67, 320), (35, 1024), (16, 2048), (130, 3072), (33, 4096), (20, 4160), (1, 1088)):
+        _run("a4g64", M, K, N, np.float16, [52, M, K, N])
+
+
+def test_gemv_matrix_cores_one_hot_is_exact():
+    """fp16 one-hot tokens through the matrix-core kernel: the code sum is q exactly and
+    the activation sum 1, so each output is round(s * q + b), the fp32 weight."""
+    fmt, M, K = "a4g64", 133, 1024
+    blob = make_matrix(fmt, M, K, [53])
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    for ks in (list(range(0, K, 32)), list(range(31, K, 64))[:16] + [K - 1]):
+        x = np.zeros((len(ks), K), np.float16)
+        for t, k in enumerate(ks):
+            x[t, k] = 1.0
+        y = to_host(qm.gemv(to_dev(x)))
+        for t, k in enumerate(ks):
+            assert np.array_equal(y[t], w[:, k]), f"token {t} (k={k})"
+
+
+def test_gemv_matrix_cores_subnormal_tokens():
+    """fp16 activations in the subnormal range (2^-24 .. 2^-15): exact inputs of the
+    matrix cores, whose products (code * 2^-24 * x, down to 2^-48) stay normal fp32."""
+    fmt, M, K = "a4g64", 96, 2048
+    blob = make_matrix(fmt, M, K, [54])
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    g = np.random.default_rng(54)
+    x = (g.integers(-1023, 1024, (8, K)) * 2.0 ** -24).astype(np.float16)
+    assert np.all(np.abs(x.astype(np.float32)) < 2.0 ** -14)
+    y = to_host(qm.gemv(to_dev(x)))
+    assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL, "gemv a4g64 subnormal fp16 tokens")
+
+
+@pytest.mark.parametrize("N", [11, 32])
+def test_gemv_matrix_cores_match_other_token_counts(N):
+    """On the matrix cores a token's outputs depend on its own activations, K and the
+    kernel's fixed order only: an N-token call returns, bit for bit, what calls on
+    windows of 5 of its tokens return (token blocks of 16 included)."""
+    fmt, M, K = "a4g64", 300, 2048
+    qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [55])), fmt, M, K)
+    x = to_dev(np.random.default_rng([55, N]).standard_normal((N, K)).astype(np.float16))
+    full = to_host(qm.gemv(x))
+    for s0 in range(0, N - 4, 3):
+        part = to_host(qm.gemv(x[s0:s0 + 5].contiguous()))
+        assert np.array_equal(full[s0:s0 + 5].view(np.uint32), part.view(np.uint32)), (N, s0)
