@@ -953,103 +953,133 @@ __global__ __launch_bounds__(512) void k_gemvn(GemvArgs a, GemvGroup grp) {
 // k-slots), and the k-slots of a step are 32 consecutive weights of one half of a group:
 // lane group l / 16 reads code bytes 8 (l / 16) .. +7 of the group (the low nibbles are
 // weights 8 (l / 16) .. +7 of the first half, the high nibbles those of the second) and
-// the matching 16 bytes of each token's activations.  A workgroup owns 16 rows; its KS
-// waves split K, wave w taking GPW groups from group w * GPW, with every load issued
-// before the first product.  The waves' partial outputs are summed in LDS in wave order,
-// so an output's value depends on K and N only (not on M or on the launch's other
-// matrices): grouped and single calls agree bit for bit.
-template <int NTB, int GPW>
+// the matching 16 bytes of each token's activations.  A wave holds RT tiles of 16 rows
+// against the same activation registers (the activations are 2 bytes per weight and
+// token block, four times the codes: RT = 2 halves what a weight costs in loads); a
+// workgroup owns the 16 RT rows, its KS waves split K, wave w taking GPW groups from
+// group w * GPW, with every load issued before the first product.  The waves' partial
+// outputs are summed in LDS in wave order, so an output's value depends on its token's
+// activations and K only (not on M, N, RT or the launch's other matrices): grouped and
+// single calls, and calls with other token counts, agree bit for bit.
+template <int NTB, int GPW, int RT>
 __global__ __launch_bounds__(1024) void k_gemvm_a4(GemvArgs a, GemvGroup grp) {
   const u8* W;
   const void* xv;
   float* y;
   int M, wg0;
   group_matrix(a, grp, W, xv, y, M, wg0);
-  const int r0 = (static_cast<int>(blockIdx.x) - wg0) * 16;
+  const int r0 = (static_cast<int>(blockIdx.x) - wg0) * 16 * RT;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int KS = blockDim.x >> 6;
   const int K = a.K, N = a.N;
   const int G = K >> 6;
   const int kq = lane >> 4;
-  const int row = min(r0 + (lane & 15), M - 1);  // rows past M repeat the last one (never stored)
-  const u32 row_off = static_cast<u32>(row) * static_cast<u32>(a.row_bytes);
   const _Float16* x = static_cast<const _Float16*>(xv);
   const int g0 = w * GPW;
 
-  u32 hdr[GPW], q[GPW][2];
+  u32 hdr[RT][GPW], q[RT][GPW][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = min(r0 + 16 * rt + (lane & 15), M - 1);  // rows past M repeat the last one (never stored)
+    const u32 row_off = static_cast<u32>(row) * static_cast<u32>(a.row_bytes);
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+      const int g = min(g0 + j, G - 1);  // slots past K repeat the last group (never added)
+      const u32* p = reinterpret_cast<const u32*>(W + row_off + 36u * static_cast<u32>(g));
+      hdr[rt][j] = p[0];
+      q[rt][j][0] = p[1 + 2 * kq];
+      q[rt][j][1] = p[2 + 2 * kq];
+    }
+  }
+  // activations of the real tokens only: the lanes of padding rows load nothing (their
+  // zeros give zero outputs, never stored), so below 16 tokens the loads move N / 16 of
+  // a full block's bytes
   uint4 xa[NTB][GPW][2];
 #pragma unroll
-  for (int j = 0; j < GPW; ++j) {
-    const int g = min(g0 + j, G - 1);  // slots past K repeat the last group (never added)
-    const u32* p = reinterpret_cast<const u32*>(W + row_off + 36u * static_cast<u32>(g));
-    hdr[j] = p[0];
-    q[j][0] = p[1 + 2 * kq];
-    q[j][1] = p[2 + 2 * kq];
+  for (int b = 0; b < NTB; ++b) {
 #pragma unroll
-    for (int b = 0; b < NTB; ++b) {
-      const int tok = min(16 * b + (lane & 15), N - 1);  // tokens past N repeat the last (never stored)
-      const uint4* px =
-          reinterpret_cast<const uint4*>(x + static_cast<size_t>(tok) * K + 64 * g + 8 * kq);
-      xa[b][j][0] = px[0];  // weights 8kq .. +7 of the first half
-      xa[b][j][1] = px[4];  // and of the second (32 activations on)
+    for (int j = 0; j < GPW; ++j) xa[b][j][0] = xa[b][j][1] = uint4{0, 0, 0, 0};
+    const int tok = 16 * b + (lane & 15);
+    if (tok < N) {
+#pragma unroll
+      for (int j = 0; j < GPW; ++j) {
+        const int g = min(g0 + j, G - 1);
+        const uint4* px = reinterpret_cast<const uint4*>(x + static_cast<size_t>(tok) * K + 64 * g + 8 * kq);
+        xa[b][j][0] = px[0];  // weights 8kq .. +7 of the first half
+        xa[b][j][1] = px[4];  // and of the second (32 activations on)
+      }
     }
   }
 
   const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-  float acc[NTB][4];
+  float acc[RT][NTB][4];
 #pragma unroll
-  for (int b = 0; b < NTB; ++b)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[b][i] = 0.0f;
+    for (int b = 0; b < NTB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[rt][b][i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < GPW; ++j) {
     // slots past the last group are computed and dropped by a select: a branch would let
     // the compiler sink their loads behind the products of the slots before them
     const bool live = g0 + j < G;
     // bytes (2v, 2v+1) of each code word as an fp16 pair, low and high nibbles apart
-    half8 c[2];
+    half8 c[RT][2];
+    float s24[RT], bias[RT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32 v[4];
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const u32 n = h ? (q[j][e] >> 4) : q[j][e];
-        v[2 * e] = __builtin_amdgcn_perm(0u, n, 0x0C010C00u) & 0x000F000Fu;
-        v[2 * e + 1] = __builtin_amdgcn_perm(0u, n, 0x0C030C02u) & 0x000F000Fu;
+      for (int h = 0; h < 2; ++h) {
+        u32 v[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const u32 n = h ? (q[rt][j][e] >> 4) : q[rt][j][e];
+          v[2 * e] = __builtin_amdgcn_perm(0u, n, 0x0C010C00u) & 0x000F000Fu;
+          v[2 * e + 1] = __builtin_amdgcn_perm(0u, n, 0x0C030C02u) & 0x000F000Fu;
+        }
+        c[rt][h] = __builtin_bit_cast(half8, uint4{v[0], v[1], v[2], v[3]});
       }
-      c[h] = __builtin_bit_cast(half8, uint4{v[0], v[1], v[2], v[3]});
+      s24[rt] = h2f(hdr[rt][j]) * 16777216.0f;  // scale * 2^24, exact
+      bias[rt] = h2f(hdr[rt][j] >> 16);
     }
-    const float s24 = h2f(hdr[j]) * 16777216.0f;  // scale * 2^24, exact
-    const float bias = h2f(hdr[j] >> 16);
 #pragma unroll
     for (int b = 0; b < NTB; ++b) {
       const half8 x0 = __builtin_bit_cast(half8, xa[b][j][0]);
       const half8 x1 = __builtin_bit_cast(half8, xa[b][j][1]);
-      floatx4 sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, c[0], floatx4{0, 0, 0, 0}, 0, 0, 0);
-      sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, c[1], sq, 0, 0, 0);
+      // the activation sums do not depend on the rows: one pair of products for all tiles
       floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, ones, floatx4{0, 0, 0, 0}, 0, 0, 0);
       sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, ones, sx, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float t = fmaf(bias, sx[i], fmaf(s24, sq[i], acc[b][i]));
-        acc[b][i] = live ? t : acc[b][i];
+      for (int rt = 0; rt < RT; ++rt) {
+        floatx4 sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(x0, c[rt][0], floatx4{0, 0, 0, 0}, 0, 0, 0);
+        sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(x1, c[rt][1], sq, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = fmaf(bias[rt], sx[i], fmaf(s24[rt], sq[i], acc[rt][b][i]));
+          acc[rt][b][i] = live ? t : acc[rt][b][i];
+        }
       }
     }
   }
 
-  // D[4 (l / 16) + i][l % 16] of token block b: token 16b + 4 (l / 16) + i, row r0 + l % 16
+  // D[4 (l / 16) + i][l % 16] of token block b, tile rt: token 16b + 4 (l / 16) + i,
+  // row r0 + 16 rt + l % 16
 #pragma unroll
-  for (int b = 0; b < NTB; ++b)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_dyn[((w * NTB + b) * 4 + i) * 64 + lane] = acc[b][i];
+    for (int b = 0; b < NTB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_dyn[(((w * RT + rt) * NTB + b) * 4 + i) * 64 + lane] = acc[rt][b][i];
   __syncthreads();
-  for (int o = threadIdx.x; o < NTB * 256; o += blockDim.x) {
-    const int b = o >> 8, i = (o >> 6) & 3, l = o & 63;
-    float sum = s_dyn[(b * 4 + i) * 64 + l];
-    for (int ww = 1; ww < KS; ++ww) sum += s_dyn[((ww * NTB + b) * 4 + i) * 64 + l];
+  constexpr int kOut = RT * NTB * 256;
+  for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
+    float sum = s_dyn[o];
+    for (int ww = 1; ww < KS; ++ww) sum += s_dyn[ww * kOut + o];
+    const int rt = o / (NTB * 256), b = (o >> 8) % NTB, i = (o >> 6) & 3, l = o & 63;
     const int tok = 16 * b + 4 * (l >> 4) + i;
-    const int r = r0 + (l & 15);
+    const int r = r0 + 16 * rt + (l & 15);
     if (tok < N && r < M) y[static_cast<size_t>(tok) * M + r] = sum;
   }
 }
@@ -1366,7 +1396,7 @@ struct Tables {
   int pair_regs[2][3];
   GemvKernel multi_id[kNumFormats][2];
   GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
-  GemvGroupKernel mma[2][3];  // k_gemvm_a4: [token blocks - 1][groups per wave - 2]
+  GemvGroupKernel mma[2][3][2];  // k_gemvm_a4: [token blocks - 1][groups per wave - 2][row tiles - 1]
   template <int F>
   void fill_format() {
     fill_multi<F>(multi[F], multi_id[F]);
@@ -1375,12 +1405,18 @@ struct Tables {
     fill_id<F>(id[F], std::make_integer_sequence<int, kIdBuckets>{});
   }
   Tables() {
-    mma[0][0] = k_gemvm_a4<1, 2>;
-    mma[0][1] = k_gemvm_a4<1, 3>;
-    mma[0][2] = k_gemvm_a4<1, 4>;
-    mma[1][0] = k_gemvm_a4<2, 2>;
-    mma[1][1] = k_gemvm_a4<2, 3>;
-    mma[1][2] = k_gemvm_a4<2, 4>;
+    mma[0][0][0] = k_gemvm_a4<1, 2, 1>;
+    mma[0][1][0] = k_gemvm_a4<1, 3, 1>;
+    mma[0][2][0] = k_gemvm_a4<1, 4, 1>;
+    mma[1][0][0] = k_gemvm_a4<2, 2, 1>;
+    mma[1][1][0] = k_gemvm_a4<2, 3, 1>;
+    mma[1][2][0] = k_gemvm_a4<2, 4, 1>;
+    mma[0][0][1] = k_gemvm_a4<1, 2, 2>;
+    mma[0][1][1] = k_gemvm_a4<1, 3, 2>;
+    mma[0][2][1] = k_gemvm_a4<1, 4, 2>;
+    mma[1][0][1] = k_gemvm_a4<2, 2, 2>;
+    mma[1][1][1] = k_gemvm_a4<2, 3, 2>;
+    mma[1][2][1] = k_gemvm_a4<2, 4, 2>;
     narrow_id[0] = k_gemv_id_narrow<false>;
     narrow_id[1] = k_gemv_id_narrow<true>;
     fill_format<FMT_Q4_0>();
@@ -1588,17 +1624,18 @@ hipError_t launch_multi(int fmt, int nU, int64_t row_bytes, int N, const MultiSh
   return hipGetLastError();
 }
 
-// Few fp16 tokens of 4-bit affine groups on the matrix cores (k_gemvm_a4): one workgroup
-// per 16 rows, KS = ceil(G / GPW) waves over the G = K / 64 groups, GPW the smallest of
-// 2, 3, 4 that keeps KS <= 16.  A function of K and N only, so the waves' partial sums
-// of an output are added in the same order whichever launch the matrix is in.
+// Few fp16 tokens of 4-bit affine groups on the matrix cores (k_gemvm_a4): KS =
+// ceil(G / GPW) waves over the G = K / 64 groups, GPW the smallest of 2, 3, 4 that
+// keeps KS <= 16 -- a function of K alone, so the waves' partial sums of an output are
+// added in the same order whichever launch the matrix is in -- and RT row tiles of 16 per
+// wave (RT changes which wave computes a row, not how).
 constexpr int kMmaMinTokens = 5;  // below it the vector kernel is as fast (4 tokens) or faster
 struct MmaShape {
-  int gpw, ks, ntb;
+  int gpw, ks, ntb, rt;
   size_t lds;
 };
 
-bool mma_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
+bool mma_shape(int fmt, int64_t K, int N, int x_f16, int64_t M, int cus, MmaShape& o) {
   if (fmt != FMT_A4G64 || !x_f16 || N < kMmaMinTokens || N > 32 || K % 64 != 0 || K < 64) return false;
   const int64_t G = K / 64;
   int gpw = 2;
@@ -1607,7 +1644,12 @@ bool mma_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
   o.gpw = gpw;
   o.ks = static_cast<int>((G + gpw - 1) / gpw);
   o.ntb = N > 16 ? 2 : 1;
-  o.lds = static_cast<size_t>(o.ks) * o.ntb * 256 * sizeof(float);
+  // two row tiles per wave (half the activation bytes per weight) when one-tile
+  // workgroups would be more than one per CU: the 6144-row ffn_gate + ffn_up launch at
+  // 16 tokens 6.97 -> 5.79 us; with fewer rows the halved workgroup count loses more
+  // (q+k+v, 4096 rows: 5.05 -> 5.70 us)
+  o.rt = (M + 15) / 16 > cus ? 2 : 1;
+  o.lds = static_cast<size_t>(o.ks) * o.rt * o.ntb * 256 * sizeof(float);
   return true;
 }
 
@@ -1620,10 +1662,10 @@ hipError_t launch_mma(int64_t row_bytes, int64_t K, int N, const MmaShape& o, co
   a.row_bytes = row_bytes;
   a.nU = static_cast<int>(K / 32);
   a.K = static_cast<int>(K);
-  a.rows_per_wg = 16;
+  a.rows_per_wg = 16 * o.rt;
   a.x_f16 = 1;
   a.N = N;
-  hipLaunchKernelGGL(tables().mma[o.ntb - 1][o.gpw - 2], dim3(grp.first[grp.n]), dim3(64 * o.ks), o.lds, st, a,
+  hipLaunchKernelGGL(tables().mma[o.ntb - 1][o.gpw - 2][o.rt - 1], dim3(grp.first[grp.n]), dim3(64 * o.ks), o.lds, st, a,
                      grp);
   return hipGetLastError();
 }
@@ -1652,10 +1694,10 @@ hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, fl
   OneShape o;
   MultiShape mo;
   MmaShape mm;
-  const bool mma = !mixed && mma_shape(m0.fmt, m0.K, N, x_f16, mm);
+  const bool mma = !mixed && mma_shape(m0.fmt, m0.K, N, x_f16, rows, m0.cus, mm);
   int RW;
   if (mma) {
-    RW = 16;
+    RW = 16 * mm.rt;
   } else if (N == 1) {
     if (!one_shape(mixed ? FMT_Q4_K : m0.fmt, nU, rows, x_f16, m0.cus, o, mixed ? tables().pair_regs : nullptr))
       return hipErrorNotSupported;
@@ -1714,7 +1756,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     return launch_one(m.fmt, nU, static_cast<int64_t>(m.row_bytes), o, grp, x_f16, st);
   }
   MmaShape mm;
-  if (mma_shape(m.fmt, m.K, N, x_f16, mm)) {
+  if (mma_shape(m.fmt, m.K, N, x_f16, M, cus, mm)) {
     GemvGroup grp{};
     grp.n = 1;
     grp.W[0] = m.blocks;
@@ -1722,7 +1764,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     grp.y[0] = y;
     grp.M[0] = M;
     grp.first[0] = 0;
-    grp.first[1] = (M + 15) / 16;
+    grp.first[1] = (M + 16 * mm.rt - 1) / (16 * mm.rt);
     return launch_mma(static_cast<int64_t>(m.row_bytes), m.K, N, mm, grp, st);
   }
   if (N >= 2) {

@@ -273,3 +273,23 @@ def test_gemv_matrix_cores_match_other_token_counts(N):
     for s0 in range(0, N - 4, 3):
         part = to_host(qm.gemv(x[s0:s0 + 5].contiguous()))
         assert np.array_equal(full[s0:s0 + 5].view(np.uint32), part.view(np.uint32)), (N, s0)
+
+
+def test_gemv_matrix_cores_two_row_tiles():
+    """Tall enough (more 16-row tiles than CUs) for two row tiles per wave: ragged last
+    workgroup, one and two token blocks, and one-hot tokens exact."""
+    fmt, M, K = "a4g64", 4100, 1024
+    blob = make_matrix(fmt, M, K, [56])
+    w = oracle.dequantize(fmt, blob, M, K)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    for N in (5, 17):
+        x = np.random.default_rng([56, N]).standard_normal((N, K)).astype(np.float16)
+        y = to_host(qm.gemv(to_dev(x)))
+        assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL, f"gemv a4g64 M={M} N={N}")
+    ks = [0, 63, 64, 511, 777, 1023]
+    x = np.zeros((len(ks), K), np.float16)
+    for t, k in enumerate(ks):
+        x[t, k] = 1.0
+    y = to_host(qm.gemv(to_dev(x)))
+    for t, k in enumerate(ks):
+        assert np.array_equal(y[t], w[:, k]), f"token {t} (k={k})"
