@@ -240,7 +240,7 @@ qmm_status qmm_gemm(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t N,
   if ((s = check_device(h)) != QMM_OK) return s;
   const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
   const hipError_t e =
-      qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, nullptr, reinterpret_cast<hipStream_t>(stream));
+      qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, nullptr, false, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }
@@ -272,7 +272,7 @@ qmm_status qmm_gemm_ws(const qmm_matrix* h, const void* x, qmm_dtype xt, int64_t
   }
   if ((s = check_device(h)) != QMM_OK) return s;
   const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
-  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, need > 0 ? static_cast<float*>(ws) : nullptr,
+  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, need > 0 ? static_cast<float*>(ws) : nullptr, true,
                                         reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
@@ -305,7 +305,7 @@ qmm_status qmm_gemm_noalloc(const qmm_matrix* h, const void* x, qmm_dtype xt, in
     scratch = qmm::gemm_scratch(h->device);
   }
   const int T = tile == QMM_TILE_AUTO ? qmm_tile_for_tokens(N) : static_cast<int>(tile);
-  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, scratch, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = qmm::launch_gemm(h->d, x, xt == QMM_F16, N, y, T, scratch, true, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return ok();
 }

@@ -63,6 +63,7 @@ struct GemmArgs {
 };
 
 constexpr int kKS = 64;  // K per stage: two 32-deep MFMA steps (two units)
+constexpr int64_t kSkMaxTokens = 16;  // split calls of up to this many tokens take k_gemm_sk
 
 // LDS slot (in halves) of k-chunk c (8 values) of token row r of a stage buffer:
 // 128-byte rows, so rows 2i and 2i+1 share one 256-byte line of the 64 four-byte
@@ -1068,6 +1069,165 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Few tokens (1 .. 16) with the K split inside a workgroup (the split entry points,
+// qmm_gemm_ws and qmm_gemm_noalloc).  The same fp16 operands as k_gemm -- the A
+// operands of AStage (the exact fp32 weight rounded to fp16), the activations as fp16
+// (fp32 input rounded to nearest even) in the same chunk order -- but no LDS staging:
+// a wave owns 16 rows (A rows) against one 16-token block (B columns; lanes of tokens
+// past N load nothing and multiply zeros) and a run of SPW consecutive K stages,
+// its loads kept D stages ahead of its products in registers.  At a few tokens a weight
+// meets at most 16 tokens, so what bounds a call is bringing its bytes in: a stage of
+// 16 rows x 64 weights is one load per lane for the weights and one per token block for
+// the activations, and every wave of the chip has D of them in flight.  KS waves cover K;
+// their partial outputs are summed in LDS in wave order, so an output depends on K (which
+// fixes SPW and KS) and not on N, M or the token tile: both tiles give the same bits.
+// Activations of a stage through buffer loads: a lane of a token past N, or of a chunk
+// past K, gets an offset past the buffer's end, which the hardware answers with zeros
+// without touching memory -- no branch, so the loads of every stage are counted alike
+// and each product waits for its own stage only.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const void* p, u32 bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <bool XF16, int NTB> struct SkX;
+template <int NTB> struct SkX<true, NTB> {
+  uint4 v[NTB][2];
+  __device__ __forceinline__ void load(int b, int j, __amdgpu_buffer_rsrc_t rs, u32 off) {
+    v[b][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+  __device__ __forceinline__ half8 op(int b, int j) const { return __builtin_bit_cast(half8, v[b][j]); }
+};
+template <int NTB> struct SkX<false, NTB> {
+  uint4 v[NTB][2][2];
+  __device__ __forceinline__ void load(int b, int j, __amdgpu_buffer_rsrc_t rs, u32 off) {
+    v[b][j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    v[b][j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, 0));
+  }
+  __device__ __forceinline__ half8 op(int b, int j) const {
+    const float4 f0 = __builtin_bit_cast(float4, v[b][j][0]), f1 = __builtin_bit_cast(float4, v[b][j][1]);
+    return half8{static_cast<_Float16>(f0.x), static_cast<_Float16>(f0.y), static_cast<_Float16>(f0.z),
+                 static_cast<_Float16>(f0.w), static_cast<_Float16>(f1.x), static_cast<_Float16>(f1.y),
+                 static_cast<_Float16>(f1.z), static_cast<_Float16>(f1.w)};
+  }
+};
+
+// Stages in flight per wave, and waves per workgroup: 16 waves (four per SIMD, 128
+// registers per lane) where the loads of four (fp16 activations) or three (fp32) stages
+// fit beside the rest; 8 waves (256 registers) for the formats with the widest decode
+// state and for fp32 activations of two token blocks, which spill at 128.
+constexpr bool sk_wide(int F, bool xf16, int ntb) {
+  return F == FMT_Q6_K || F == FMT_Q3_K || F == FMT_Q5_0 || F == FMT_Q5_K || (!xf16 && ntb == 2);
+}
+constexpr int sk_depth(bool xf16, int ntb) { return xf16 ? (ntb == 1 ? 4 : 3) : (ntb == 1 ? 3 : 2); }
+constexpr int sk_max_waves(int F, bool xf16, int ntb) { return sk_wide(F, xf16, ntb) ? 8 : 16; }
+
+// split_stages = SPW (stages per wave), a multiple of the depth; blockDim = 64 * KS
+template <int F, bool XF16, int NTB>
+__global__ __launch_bounds__(64 * sk_max_waves(F, XF16, NTB)) void k_gemm_sk(GemmArgs a) {
+  constexpr int D = sk_depth(XF16, NTB);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int KS = blockDim.x >> 6;
+  const int r0 = static_cast<int>(blockIdx.x) * 16;
+  const int nst = (a.nU + 1) >> 1;
+  const int sb = w * a.split_stages;
+  const int r = min(r0 + (lane & 15), a.M - 1);  // rows past M repeat the last one (never stored)
+  const u32 row_off = static_cast<u32>(r) * a.row_bytes;
+
+  AStage<F> ws[D];
+  SkX<XF16, NTB> xs[D];
+  constexpr u32 ES = XF16 ? 2 : 4;
+  const u32 xbytes = static_cast<u32>(a.N) * static_cast<u32>(a.K) * ES;
+  const __amdgpu_buffer_rsrc_t rs = sk_rsrc(a.x, xbytes);
+  // stage s into slot d: the weights of the wave's 16 rows (clamped to the last stage,
+  // so every address is inside the matrix) and each token block's two k-chunks 2g, 2g + 1
+  // (zeros for tokens past N and for K past the end)
+  auto fetch = [&](int s, int d) {
+    const int sc = min(s, nst - 1);
+    ws[d].load(a.W, row_off, 2 * sc, a.nU, g);
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) {
+      const int tok = 16 * b + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int k = kKS * sc + 8 * (2 * g + j);
+        const bool in = tok < a.N && k < a.K && s < nst;
+        const u32 off = in ? (static_cast<u32>(tok) * static_cast<u32>(a.K) + k) * ES : xbytes;
+        xs[d].load(b, j, rs, off);
+      }
+    }
+  };
+  // one accumulator per slot: a stage's products depend on the slot's previous stage
+  // only (D stages back), never on a result of the stage before it
+  floatx4 acc[D][NTB];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) acc[d][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // a stage past K (the last wave's run may end past it) multiplies zero weights by
+  // zero activations; a last stage whose second unit lies past K has that unit's
+  // weights zeroed (zero_second zeroes the coefficients of lane groups >= 2)
+  auto compute = [&](int s, int d) {
+    const int zg = s >= nst ? 2 : (2 * s + 1 == a.nU ? g : 0);
+    ws[d].zero_second(zg);
+    half8 A[2];
+    ws[d].operands(g, A);
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) {
+      acc[d][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], xs[d].op(b, 0), acc[d][b], 0, 0, 0);
+      acc[d][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], xs[d].op(b, 1), acc[d][b], 0, 0, 0);
+    }
+  };
+  // SPW / D turns of the ring, the last one peeled (it fetches nothing): no branch
+  // around a load, so before each product the wait is for that stage's loads only.
+  // The last wave's stages past K re-read the last stage (clamped) and are dropped.
+#pragma unroll
+  for (int d = 0; d < D; ++d) fetch(sb + d, d);
+  // (scheduling barriers keep each stage's decode behind its own wait: the scheduler
+  // would otherwise hoist the next stages' decode, and with it their waits, forward;
+  // the matrix cores still run a stage's products while the next one decodes)
+  int s = sb;
+  for (int turn = D; turn < a.split_stages; turn += D, s += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(s + d, d);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(s + d + D, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    compute(s + d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // D[4g + i][l % 16] of token block b: row r0 + 4g + i, token 16b + l % 16; the
+  // slots' sums added in slot order
+  extern __shared__ float s_sk[];
+#pragma unroll
+  for (int b = 0; b < NTB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[0][b][i];
+#pragma unroll
+      for (int d = 1; d < D; ++d) v += acc[d][b][i];
+      s_sk[((w * NTB + b) * 4 + i) * 64 + lane] = v;
+    }
+  __syncthreads();
+  constexpr int kOut = NTB * 256;
+  for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
+    // o = (block b, token t, row rr): consecutive threads store consecutive rows
+    const int b = o >> 8, t = (o >> 4) & 15, rr = o & 15;
+    const int src = (b * 4 + (rr & 3)) * 64 + 16 * (rr >> 2) + t;
+    float sum = s_sk[src];
+    for (int ww = 1; ww < KS; ++ww) sum += s_sk[ww * kOut + src];
+    const int tok = 16 * b + t, row = r0 + rr;
+    if (tok < a.N && row < a.M) a.y[static_cast<u64>(tok) * a.M + row] = sum;
+  }
+}
+
 // y = sum of the S partial slabs of a split call, in split order (so the result
 // does not depend on which workgroup finished first).
 __global__ __launch_bounds__(256) void k_split_sum(const float* ws, int S, u64 stride, u64 count, int vec,
@@ -1224,6 +1384,7 @@ namespace {
 GemmSplit split_for(const MatDesc& m, int64_t N, bool xf16) {
   const int64_t cus = m.cus;
   GemmSplit sp{1, static_cast<int>((m.K / 32 + 1) / 2)};
+  if (N >= 1 && N <= kSkMaxTokens) return sp;  // k_gemm_sk: the split is inside the workgroup
   if (N > 64) {
     const WidePlan p = wide_plan(m, N, xf16);
     return GemmSplit{p.splits, p.stages};
@@ -1353,10 +1514,71 @@ float* gemm_scratch(int dev) {
   return static_cast<float*>(g_scratch_ptr[dev]);
 }
 
+namespace {
+template <int F>
+void sk_kernels(GemmKernel (&t)[2]) {
+  t[0] = k_gemm_sk<F, false, 1>;
+  t[1] = k_gemm_sk<F, true, 1>;
+}
+struct SkTable {
+  GemmKernel k[kNumFormats][2];  // [format][fp16 activations]
+  SkTable() {
+    sk_kernels<FMT_Q4_0>(k[FMT_Q4_0]);
+    sk_kernels<FMT_Q8_0>(k[FMT_Q8_0]);
+    sk_kernels<FMT_Q4_K>(k[FMT_Q4_K]);
+    sk_kernels<FMT_Q6_K>(k[FMT_Q6_K]);
+    sk_kernels<FMT_A4G64>(k[FMT_A4G64]);
+    sk_kernels<FMT_Q4_1>(k[FMT_Q4_1]);
+    sk_kernels<FMT_Q5_0>(k[FMT_Q5_0]);
+    sk_kernels<FMT_Q5_1>(k[FMT_Q5_1]);
+    sk_kernels<FMT_Q2_K>(k[FMT_Q2_K]);
+    sk_kernels<FMT_Q3_K>(k[FMT_Q3_K]);
+    sk_kernels<FMT_Q5_K>(k[FMT_Q5_K]);
+  }
+};
+
+// k_gemm_sk's shape: KS waves per workgroup, each with SPW stages (a multiple of the
+// depth) -- a function of the format, M, K, the activation type and the token blocks,
+// never of the tile.
+hipError_t launch_gemm_sk(const MatDesc& m, const void* x, bool xf16, int64_t N, float* y, hipStream_t st) {
+  static const SkTable tab;
+  const int ntb = 1;
+  const int D = sk_depth(xf16, ntb);
+  const int64_t nst = (m.K / 32 + 1) / 2;
+  const int cap = sk_max_waves(m.fmt, xf16, ntb);
+  // waves per workgroup: about 16 per CU over the launch's row tiles (so every
+  // workgroup is resident at once and each wave streams its run through the ring),
+  // within the kernel's cap
+  const int64_t tiles = (m.M + 15) / 16;
+  int64_t want = (16 * static_cast<int64_t>(m.cus) + tiles - 1) / tiles;
+  want = want < 1 ? 1 : (want > cap ? cap : want);
+  const int64_t per = (nst + want - 1) / want;
+  const int64_t spw = (per + D - 1) / D * D;
+  const int64_t KS = (nst + spw - 1) / spw;
+  GemmArgs a{};
+  a.W = m.blocks;
+  a.row_bytes = static_cast<u32>(m.row_bytes);
+  a.M = static_cast<int>(m.M);
+  a.nU = static_cast<int>(m.K / 32);
+  a.K = static_cast<int>(m.K);
+  a.x = x;
+  a.N = static_cast<int>(N);
+  a.y = y;
+  a.split_stages = static_cast<int>(spw);
+  const int64_t blocks = (m.M + 15) / 16;
+  if (blocks > INT_MAX || spw > INT_MAX) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(KS) * ntb * 256 * sizeof(float);
+  hipLaunchKernelGGL(tab.k[m.fmt][xf16 ? 1 : 0], dim3(static_cast<unsigned>(blocks)),
+                     dim3(static_cast<unsigned>(64 * KS)), lds, st, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
-                       hipStream_t st) {
+                       bool split_ok, hipStream_t st) {
   const int64_t cus = m.cus;
-  const GemmSplit sp = ws ? split_for(m, N, x_f16 != 0) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
+  if (split_ok && N >= 1 && N <= kSkMaxTokens) return launch_gemm_sk(m, x, x_f16 != 0, N, y, st);
+  const GemmSplit sp = split_ok ? split_for(m, N, x_f16 != 0) : GemmSplit{1, static_cast<int>((m.K / 32 + 1) / 2)};
   GemmArgs a{};
   a.W = m.blocks;
   a.row_bytes = static_cast<u32>(m.row_bytes);

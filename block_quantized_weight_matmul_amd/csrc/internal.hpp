@@ -46,10 +46,12 @@ struct GemmSplit {
 };
 GemmSplit gemm_split(const MatDesc& m, int64_t N);
 size_t gemm_workspace_bytes(const MatDesc& m, int64_t N);
-// ws: workspace of gemm_workspace_bytes(m, N) bytes for a split call, or nullptr
-// (unsplit)
+// split_ok: the call may divide K (qmm_gemm_ws, qmm_gemm_noalloc): among the waves of
+// a workgroup up to 16 tokens, among workgroups above (ws: workspace of
+// gemm_workspace_bytes(m, N) bytes when that is not 0); otherwise every K stage runs in
+// one workgroup (qmm_gemm)
 hipError_t launch_gemm(const MatDesc& m, const void* x, int x_f16, int64_t N, float* y, int tile, float* ws,
-                       hipStream_t s);
+                       bool split_ok, hipStream_t s);
 // The allocation-free entry point's scratch: its size, the once-per-device lookup of its
 // device address (call with dev current), and that address (nullptr before the lookup).
 size_t gemm_scratch_bytes();

@@ -203,21 +203,24 @@ qmm_status qmm_gemm(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
 /*
  * qmm_gemm_workspace_bytes -- device bytes qmm_gemm_ws needs for N tokens on this
  * handle, with either activation type (the larger of the two needs); 0 when it
- * needs none (then qmm_gemm_ws computes exactly as qmm_gemm).  Also 0 for a NULL
- * or expert handle and for N outside 1..2^24.
+ * needs none: up to 16 tokens (K is divided among the waves of a workgroup), and
+ * above when the call is not split (then qmm_gemm_ws computes exactly as qmm_gemm).
+ * Also 0 for a NULL or expert handle and for N outside 1..2^24.
  */
 size_t qmm_gemm_workspace_bytes(const qmm_matrix *h, int64_t N);
 
 /*
  * qmm_gemm_ws -- qmm_gemm with a caller-owned workspace (same operation, tile
- * rule and arguments; candle pull request above).  When N tokens make too few
- * (row, token) tiles to fill the GPU, or the GPU is filled better that way, the
- * K range is divided among more workgroups: each writes its partial products to
- * its own [N, M] fp32 slab of `ws`, and a second kernel sums the slabs in split
- * order into y.  The split depends only on the handle's shape, N and the
- * activation type, so the result is deterministic and bit-identical for either
- * tile; it can differ from qmm_gemm's in rounding (both within the same error
- * bound).
+ * rule and arguments; candle pull request above).  Up to 16 tokens the K range is
+ * divided among the waves of a workgroup of 16 weight rows, which sum their partial
+ * products in LDS (no workspace).  Above, when N tokens make too few (row, token)
+ * tiles to fill the GPU, or the GPU is filled better that way, the K range is divided
+ * among more workgroups: each writes its partial products to its own [N, M] fp32 slab
+ * of `ws`, and a second kernel sums the slabs in split order into y.  Either split
+ * depends only on the handle's shape, N and the activation type, so the result is
+ * deterministic and bit-identical for either tile; it can differ from qmm_gemm's in
+ * rounding (both within the same error bound).  The staged operands are qmm_gemm's:
+ * the fp16 weights and activations, so one-hot tokens give the staged weights.
  *   ws        DEVICE, 16-byte aligned, ws_bytes >= qmm_gemm_workspace_bytes(h, N)
  *             (QMM_E_ARG otherwise; may be NULL when that is 0).  Borrowed until
  *             the stream passes the call; must not alias x, y or the blocks.

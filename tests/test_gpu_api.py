@@ -53,20 +53,21 @@ def test_call_errors():
     assert L.lib.qmm_gemm(h, xp, 0, 1, yp, 48, s) == -1         # bad tile
     assert L.lib.qmm_gemm(h, xp, 0, -5, yp, 0, s) == -3
     # a split call needs its workspace: missing, too small or misaligned is refused
-    # (K = 2048 gives the few-token call K stages to split)
+    # (K = 2048 gives a 40-token call K stages to split among workgroups)
     long_rows = q.QMatrix(to_dev(make_matrix(fmt, M, 2048, [74])), fmt, M, 2048)
     h = long_rows.handle
-    xl = torch.zeros((7, 2048), device="cuda")
+    xl = torch.zeros((40, 2048), device="cuda")
     xp = ctypes.c_void_p(xl.data_ptr())
-    need = L.lib.qmm_gemm_workspace_bytes(h, 7)
+    need = L.lib.qmm_gemm_workspace_bytes(h, 40)
     assert need > 0
+    assert L.lib.qmm_gemm_workspace_bytes(h, 7) == 0   # the waves of a workgroup split K
     ws = torch.zeros(need // 4 + 8, device="cuda")
     wp = ctypes.c_void_p(ws.data_ptr())
-    assert L.lib.qmm_gemm_ws(h, xp, 0, 7, yp, 0, None, 0, s) == -1
-    assert L.lib.qmm_gemm_ws(h, xp, 0, 7, yp, 0, wp, need - 4, s) == -1
+    assert L.lib.qmm_gemm_ws(h, xp, 0, 40, yp, 0, None, 0, s) == -1
+    assert L.lib.qmm_gemm_ws(h, xp, 0, 40, yp, 0, wp, need - 4, s) == -1
     assert "needs" in L.lib.qmm_last_error().decode()
-    assert L.lib.qmm_gemm_ws(h, xp, 0, 7, yp, 0, ctypes.c_void_p(ws.data_ptr() + 4), need, s) == -4
-    assert L.lib.qmm_gemm_ws(h, xp, 0, 7, yp, 48, wp, need, s) == -1   # bad tile
+    assert L.lib.qmm_gemm_ws(h, xp, 0, 40, yp, 0, ctypes.c_void_p(ws.data_ptr() + 4), need, s) == -4
+    assert L.lib.qmm_gemm_ws(h, xp, 0, 40, yp, 48, wp, need, s) == -1   # bad tile
     h, xp = qm.handle, ctypes.c_void_p(x.data_ptr())
     assert L.lib.qmm_dequantize(h, 1, yp, 0, s) == -3           # expert out of range
     ids = torch.zeros((2, 2), dtype=torch.int32, device="cuda")

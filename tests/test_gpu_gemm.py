@@ -122,9 +122,9 @@ def test_gemm_deterministic_and_zero_tokens():
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_gemm_split_and_unsplit(fmt):
     """qmm_gemm runs every K stage in one workgroup; qmm_gemm_ws (what QMatrix.gemm
-    calls) divides K among workgroups for few tokens and sums the partial slabs in
-    split order.  Both meet the bound, both are tile-identical, and the split call
-    is deterministic."""
+    calls) divides K among the waves of a workgroup up to 16 tokens (no workspace) and
+    among workgroups above, for few tokens, summing the partial slabs in split order.
+    Both meet the bound, both are tile-identical, and the split call is deterministic."""
     bw = oracle.block_weights(fmt)
     K = 2560 if 2560 % bw == 0 else 2048
     M = 200
@@ -132,7 +132,8 @@ def test_gemm_split_and_unsplit(fmt):
         blob, w, x = _data(fmt, N, M, K, np.float16, [56, N])
         qm = q.QMatrix(to_dev(blob), fmt, M, K)
         xd = to_dev(x)
-        assert q.qmm_gemm_workspace_bytes(qm.handle, N) > 0, "few tokens should split K"
+        nb = q.qmm_gemm_workspace_bytes(qm.handle, N)
+        assert (nb == 0) if N <= 16 else (nb > 0), (N, nb)
         y_ref, S = oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w)
         outs = {}
         for t in (32, 64):
@@ -151,5 +152,45 @@ def test_gemm_workspace_is_zero_for_many_tokens():
     fmt, M, K = "q4_k", 4096, 2560
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [57])), fmt, M, K)
     assert q.qmm_gemm_workspace_bytes(qm.handle, 2048) == 0
-    assert q.qmm_gemm_workspace_bytes(qm.handle, 7) > 0
+    assert q.qmm_gemm_workspace_bytes(qm.handle, 7) == 0   # the waves of a workgroup split K
+    assert q.qmm_gemm_workspace_bytes(qm.handle, 33) > 0  # workgroups split K
     assert q.qmm_gemm_workspace_bytes(qm.handle, 0) == 0
+
+
+SK_SHAPES = [(1, 67, 768), (7, 300, 2560), (16, 33, 9728), (11, 130, 4096), (5, 20, 96)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("xdtype", [np.float16, np.float32])
+def test_gemm_few_tokens_workgroup_split(fmt, xdtype):
+    """Up to 16 tokens the split entry points divide K among the waves of one workgroup:
+    the oracle's bounds, both tiles and the rule's choice bit-identical; K of one to
+    152 stages, an odd count of 32-weight units (a last
+    stage half past K), rows that are not a multiple of 16."""
+    bw = oracle.block_weights(fmt)
+    for N, M, K in SK_SHAPES:
+        if K % bw:
+            K = (K + bw - 1) // bw * bw
+        ys = _check(fmt, N, M, K, xdtype, [57, N, M, K])
+        assert count_differences(ys[32], ys[64]) == 0, (fmt, N, K)
+        assert count_differences(ys["auto"], ys[32]) == 0, (fmt, N, K)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gemm_few_tokens_one_hot_is_staged_weight(fmt):
+    """One-hot tokens through the workgroup split: y[t] equals the staged weights
+    w16[:, k] exactly (one nonzero product, the other waves adding zeros)."""
+    bw = oracle.block_weights(fmt)
+    K = 2560 if 2560 % bw == 0 else 2048
+    M = 70
+    blob = make_matrix(fmt, M, K, [58])
+    w16 = oracle.staged_fp16(oracle.dequantize(fmt, blob, M, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K)
+    ks = [0, 31, 32, 63, 64, 255, 256, 777, 1023, 1024, 1500, K - 33, K - 1]
+    for xdt in (np.float16, np.float32):
+        x = np.zeros((len(ks), K), xdt)
+        for t, k in enumerate(ks):
+            x[t, k] = 1.0
+        y = to_host(qm.gemm(to_dev(x), tile=32))
+        for t, k in enumerate(ks):
+            assert np.array_equal(y[t], w16[:, k]), f"{fmt} {np.dtype(xdt).name}: token {t} (k={k})"

@@ -43,15 +43,18 @@ def test_noalloc_equals_workspace_entry(fmt):
     w = oracle.dequantize(fmt, blob, M, K)
     qm = q.QMatrix(to_dev(blob), fmt, M, K)
     g = np.random.default_rng([92, FORMATS.index(fmt)])
-    # two calls in a row, the second smaller: 33 fp16 tokens, then 7 fp32 tokens (both K-split),
-    # then 130 and 96 tokens (the plan of the wide calls)
+    # two calls in a row, the second smaller: 33 fp16 tokens (K split among workgroups), then
+    # 7 fp32 tokens (among the waves of a workgroup), then 130 and 96 tokens (the plan of the
+    # wide calls)
     for N, dt in ((33, np.float16), (7, np.float32), (130, np.float16), (96, np.float32)):
         x = g.standard_normal((N, K)).astype(dt)
         xd = to_dev(x)
         for tile in (0, 32, 64):
             ref, nb = _with_workspace(qm, xd, N, tile)
-            if N <= 64:
-                assert nb > 0, "the few-token call should split K"
+            if 16 < N <= 64:
+                assert nb > 0, "the few-token call should split K among workgroups"
+            if N <= 16:
+                assert nb == 0, "up to 16 tokens the waves of a workgroup split K"
             y = torch.full((N, M), float("nan"), device="cuda")
             assert _noalloc(qm.handle, xd, N, y, tile) == 0, L.lib.qmm_last_error().decode()
             got = to_host(y)
