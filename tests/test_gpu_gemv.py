@@ -293,3 +293,27 @@ def test_gemv_matrix_cores_two_row_tiles():
     y = to_host(qm.gemv(to_dev(x)))
     for t, k in enumerate(ks):
         assert np.array_equal(y[t], w[:, k]), f"token {t} (k={k})"
+
+
+@pytest.mark.parametrize("N", [5, 16, 20])
+def test_gemv_group_matrix_cores_match_single_calls(N):
+    """fp16 tokens of 4-bit affine groups in grouped calls: a launch of the group's total
+    rows (5200 here, more 16-row tiles than CUs: two row tiles per wave) gives every output
+    the bits of its own single call (fewer rows: one tile per wave), within the bound."""
+    shapes = [("a4g64", 2048, 1024), ("a4g64", 1024, 1024), ("a4g64", 2128, 1024), ("a4g64", 37, 2048)]
+    qms, xs, ws, xh = [], [], [], []
+    for i, (fmt, M, K) in enumerate(shapes):
+        blob = make_matrix(fmt, M, K, [59, i])
+        ws.append(oracle.dequantize(fmt, blob, M, K))
+        qms.append(q.QMatrix(to_dev(blob), fmt, M, K))
+        x = np.random.default_rng([60, i, N]).standard_normal((N, K)).astype(np.float16)
+        xh.append(x)
+        xs.append(to_dev(x))
+    ys = [torch.full((N, qm.M), float("nan"), device="cuda") for qm in qms]
+    q.qmm_gemv_group([qm.handle for qm in qms], xs, N, ys)
+    for i, (qm, x, y) in enumerate(zip(qms, xs, ys)):
+        single = to_host(qm.gemv(x))
+        got = to_host(y)
+        assert np.array_equal(got.view(np.uint32), single.view(np.uint32)), (shapes[i], N)
+        assert_within(got, oracle.matmul_ref(xh[i], ws[i]), oracle.tolerance_scale(xh[i], ws[i]), TOL,
+                      f"gemv_group {shapes[i]} N={N}")
