@@ -1084,6 +1084,169 @@ __global__ __launch_bounds__(1024) void k_gemvm_a4(GemvArgs a, GemvGroup grp) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The same matrix-core arithmetic for the other formats whose codes carry no large bias
+// (all but Q8_0 and the 4-bit groups above), unit by unit: a unit's 32 weights share one
+// (a, b) pair, or one per 16-weight half (Q6_K, Q2_K, Q3_K), and each output takes
+// a * (sum of q_k x_k) + b * (sum of x_k) per unit or half, both sums on the matrix
+// cores with exact operands (codes as fp16 subnormals, fp16 activations, fp32 sums):
+// a 32-deep v_mfma_f32_16x16x32_f16 step per unit, or a 16-deep v_mfma_f32_16x16x16_f16
+// step per half.  Lane group l / 16 holds the unit's weights 8 (l / 16) .. +7 (or 4 (l / 16)
+// .. +3 of each half); every lane loads and decodes its row's whole unit with the
+// format's unit decoder and takes its words by a select.  A wave runs UPW consecutive
+// units of its 16 rows with D units of loads in flight (a ring, its last turn peeled,
+// units past K multiplying zero coefficients by zero activations), one accumulator per
+// ring slot; the KS waves of a workgroup cover K and their sums are added in LDS in wave
+// order, so an output depends on its token's activations and K only.
+template <int F> constexpr bool unit_halves() { return F == FMT_Q6_K || F == FMT_Q2_K || F == FMT_Q3_K; }
+// at most 8 waves per workgroup (256 registers: the widest decoders' raw units, and two
+// token blocks, spill at 128), for one token block as for two, so that the split of K --
+// and with it every output's bits -- does not depend on the token count
+constexpr int kUnitMaxWaves = 8;
+constexpr int kUnitRing = 4;
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// codes of bytes 0, 1 and 2, 3 of w as fp16 subnormal pairs (code * 2^-24, exact)
+__device__ __forceinline__ uint2 code_pairs(u32 w) {
+  return uint2{__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u)};
+}
+__device__ __forceinline__ u32 pick4(int kq, u32 w0, u32 w1, u32 w2, u32 w3) {
+  return kq == 0 ? w0 : (kq == 1 ? w1 : (kq == 2 ? w2 : w3));
+}
+
+template <int F, int NTB>
+__global__ __launch_bounds__(64 * kUnitMaxWaves) void k_gemvm(GemvArgs a, GemvGroup grp) {
+  using Dec = Decoder<F>;
+  constexpr int D = kUnitRing;
+  constexpr bool H = unit_halves<F>();
+  const u8* W;
+  const void* xv;
+  float* y;
+  int M, wg0;
+  group_matrix(a, grp, W, xv, y, M, wg0);
+  const int r0 = (static_cast<int>(blockIdx.x) - wg0) * 16;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int KS = blockDim.x >> 6;
+  const int K = a.K, N = a.N, nU = a.nU;
+  const int kq = lane >> 4;
+  const int upw = a.chunk_units;  // units per wave, a multiple of D
+  const int ub = w * upw;
+  const int row = min(r0 + (lane & 15), M - 1);  // rows past M repeat the last one (never stored)
+  const u32 row_off = static_cast<u32>(row) * static_cast<u32>(a.row_bytes);
+  const u32 xbytes = static_cast<u32>(N) * static_cast<u32>(K) * 2u;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(xv), 0, static_cast<int>(xbytes), 0x00020000);
+
+  typename Dec::Raw rw[D];
+  uint4 xs[D][NTB];
+  // unit u into slot d: the row's unit (clamped to the last one) and, per token block,
+  // the lane's 8 activations (4 of each half): zeros for tokens past N and units past K,
+  // which the buffer loads return for an offset past the end, with no branch
+  auto fetch = [&](int u, int d) {
+    const int uc = min(u, nU - 1);
+    Dec::load(W, row_off, uc, rw[d]);
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) {
+      const int tok = 16 * b + (lane & 15);
+      const bool in = tok < N && u < nU;
+      const u32 base = (static_cast<u32>(tok) * static_cast<u32>(K) + 32u * static_cast<u32>(uc)) * 2u;
+      if constexpr (H) {
+        const u32 o0 = in ? base + 8u * kq : xbytes, o1 = in ? base + 32u + 8u * kq : xbytes;
+        const uint2 v0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, 0));
+        const uint2 v1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, 0));
+        xs[d][b] = uint4{v0.x, v0.y, v1.x, v1.y};
+      } else {
+        xs[d][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, in ? base + 16u * kq : xbytes, 0, 0));
+      }
+    }
+  };
+  floatx4 acc[D][NTB];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) acc[d][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int u, int d) {
+    const bool live = u < nU;
+    Unit o;
+    Dec::unpack(rw[d], o);
+    const float a0 = live ? o.a0 * 16777216.0f : 0.0f, b0 = live ? o.b0 : 0.0f;  // a * 2^24, exact
+    if constexpr (H) {
+      const float a1 = live ? o.a1 * 16777216.0f : 0.0f, b1 = live ? o.b1 : 0.0f;
+      const uint2 p0 = code_pairs(pick4(kq, o.c[0], o.c[1], o.c[2], o.c[3]));
+      const uint2 p1 = code_pairs(pick4(kq, o.c[4], o.c[5], o.c[6], o.c[7]));
+      const half4 c0 = __builtin_bit_cast(half4, p0), c1 = __builtin_bit_cast(half4, p1);
+      const half4 ones = {1, 1, 1, 1};
+#pragma unroll
+      for (int b = 0; b < NTB; ++b) {
+        const half4 x0 = __builtin_bit_cast(half4, uint2{xs[d][b].x, xs[d][b].y});
+        const half4 x1 = __builtin_bit_cast(half4, uint2{xs[d][b].z, xs[d][b].w});
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        const floatx4 q0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, c0, z, 0, 0, 0);
+        const floatx4 s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, ones, z, 0, 0, 0);
+        const floatx4 q1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, c1, z, 0, 0, 0);
+        const floatx4 s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, ones, z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[d][b][i] = fmaf(b1, s1[i], fmaf(a1, q1[i], fmaf(b0, s0[i], fmaf(a0, q0[i], acc[d][b][i]))));
+      }
+    } else {
+      const uint2 p0 = code_pairs(pick4(kq, o.c[0], o.c[2], o.c[4], o.c[6]));
+      const uint2 p1 = code_pairs(pick4(kq, o.c[1], o.c[3], o.c[5], o.c[7]));
+      const half8 c = __builtin_bit_cast(half8, uint4{p0.x, p0.y, p1.x, p1.y});
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+      for (int b = 0; b < NTB; ++b) {
+        const half8 xh = __builtin_bit_cast(half8, xs[d][b]);
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, c, z, 0, 0, 0);
+        const floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ones, z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d][b][i] = fmaf(b0, sx[i], fmaf(a0, q[i], acc[d][b][i]));
+      }
+    }
+  };
+  // (scheduling barriers keep each unit's decode behind its own wait)
+#pragma unroll
+  for (int d = 0; d < D; ++d) fetch(ub + d, d);
+  int u = ub;
+  for (int turn = D; turn < upw; turn += D, u += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(u + d, d);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(u + d + D, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    compute(u + d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // D[4 (l / 16) + i][l % 16] of token block b: token 16b + 4 (l / 16) + i, row r0 + l % 16;
+  // the slots' sums added in slot order, then the waves' in wave order
+#pragma unroll
+  for (int b = 0; b < NTB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[0][b][i];
+#pragma unroll
+      for (int d = 1; d < D; ++d) v += acc[d][b][i];
+      s_dyn[((w * NTB + b) * 4 + i) * 64 + lane] = v;
+    }
+  __syncthreads();
+  constexpr int kOut = NTB * 256;
+  for (int oi = threadIdx.x; oi < kOut; oi += blockDim.x) {
+    float sum = s_dyn[oi];
+    for (int ww = 1; ww < KS; ++ww) sum += s_dyn[ww * kOut + oi];
+    const int b = oi >> 8, i = (oi >> 6) & 3, l = oi & 63;
+    const int tok = 16 * b + 4 * (l >> 4) + i;
+    const int r = r0 + (l & 15);
+    if (tok < N && r < M) y[static_cast<size_t>(tok) * M + r] = sum;
+  }
+}
+
 // LDS floats of the multi-token kernel: TP token images and a spare unit, then
 // TP * RW * nU partial sums and a spare slot
 inline size_t multi_lds_floats(bool xh, int nU, int RW, int TP) {
@@ -1397,8 +1560,15 @@ struct Tables {
   GemvKernel multi_id[kNumFormats][2];
   GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
   GemvGroupKernel mma[2][3][2];  // k_gemvm_a4: [token blocks - 1][groups per wave - 2][row tiles - 1]
+  GemvGroupKernel gm[kNumFormats][2];  // k_gemvm: [format][token blocks - 1] (null: not on that path)
   template <int F>
   void fill_format() {
+    if constexpr (F == FMT_Q8_0 || F == FMT_A4G64) {
+      gm[F][0] = gm[F][1] = nullptr;
+    } else {
+      gm[F][0] = k_gemvm<F, 1>;
+      gm[F][1] = k_gemvm<F, 2>;
+    }
     fill_multi<F>(multi[F], multi_id[F]);
     fill_one<F>(one[F]);
     fill_dense<F>(dense[F], std::make_integer_sequence<int, kNumBuckets>{});
@@ -1632,11 +1802,40 @@ hipError_t launch_multi(int fmt, int nU, int64_t row_bytes, int N, const MultiSh
 constexpr int kMmaMinTokens = 5;  // below it the vector kernel is as fast (4 tokens) or faster
 struct MmaShape {
   int gpw, ks, ntb, rt;
+  int upw;  // k_gemvm (the formats other than A4G64): units per wave; 0 for k_gemvm_a4
   size_t lds;
 };
 
+// k_gemvm's shape: KS = ceil(units / UPW) waves (at most 8), UPW a multiple of the ring
+// depth -- a function of K alone.
+// Fewest tokens at which k_gemvm takes a format's calls: from there it was the faster
+// of the two on a 4096 x 4096 matrix (fp16 tokens, weights rotated over 32 copies; us at
+// 8 / 16 / 32 tokens, vector kernel -> matrix cores: Q4_0 17.4/27.8/50.6 -> 16.0/17.4/21.4,
+// Q4_K 14.0/22.9/39.2 -> 16.4/17.7/21.3, Q6_K 19.7/31.3/55.3 -> 26.3/28.6/35.7).  Each
+// lane decodes its row's whole unit, so the kernel's fixed cost grows with the decoder's.
+constexpr int kUnitMinTokens[kNumFormats] = {
+    /* Q4_0 */ 8, /* Q8_0 */ 33, /* Q4_K */ 12, /* Q6_K */ 16, /* A4G64 */ 33, /* Q4_1 */ 5,
+    /* Q5_0 */ 12, /* Q5_1 */ 5, /* Q2_K */ 12, /* Q3_K */ 24, /* Q5_K */ 16};
+
+bool mma_unit_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
+  if (!x_f16 || N < kUnitMinTokens[fmt] || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
+  const int64_t nU = K / 32;
+  const int64_t per = (nU + kUnitMaxWaves - 1) / kUnitMaxWaves;
+  const int64_t upw = (per + kUnitRing - 1) / kUnitRing * kUnitRing;
+  if (upw > INT_MAX) return false;
+  o.upw = static_cast<int>(upw);
+  o.ks = static_cast<int>((nU + upw - 1) / upw);
+  o.gpw = 0;
+  o.ntb = N > 16 ? 2 : 1;
+  o.rt = 1;
+  o.lds = static_cast<size_t>(o.ks) * o.ntb * 256 * sizeof(float);
+  return true;
+}
+
 bool mma_shape(int fmt, int64_t K, int N, int x_f16, int64_t M, int cus, MmaShape& o) {
-  if (fmt != FMT_A4G64 || !x_f16 || N < kMmaMinTokens || N > 32 || K % 64 != 0 || K < 64) return false;
+  if (fmt != FMT_A4G64) return mma_unit_shape(fmt, K, N, x_f16, o);
+  o.upw = 0;
+  if (!x_f16 || N < kMmaMinTokens || N > 32 || K % 64 != 0 || K < 64) return false;
   const int64_t G = K / 64;
   int gpw = 2;
   while (gpw <= 4 && (G + gpw - 1) / gpw > 16) ++gpw;
@@ -1653,7 +1852,8 @@ bool mma_shape(int fmt, int64_t K, int N, int x_f16, int64_t M, int cus, MmaShap
   return true;
 }
 
-hipError_t launch_mma(int64_t row_bytes, int64_t K, int N, const MmaShape& o, const GemvGroup& grp, hipStream_t st) {
+hipError_t launch_mma(int fmt, int64_t row_bytes, int64_t K, int N, const MmaShape& o, const GemvGroup& grp,
+                      hipStream_t st) {
   GemvArgs a{};
   a.W = grp.W[0];  // a single matrix is read from these fields
   a.x = grp.x[0];
@@ -1665,7 +1865,9 @@ hipError_t launch_mma(int64_t row_bytes, int64_t K, int N, const MmaShape& o, co
   a.rows_per_wg = 16 * o.rt;
   a.x_f16 = 1;
   a.N = N;
-  hipLaunchKernelGGL(tables().mma[o.ntb - 1][o.gpw - 2][o.rt - 1], dim3(grp.first[grp.n]), dim3(64 * o.ks), o.lds, st, a,
+  a.chunk_units = o.upw;
+  GemvGroupKernel k = o.upw > 0 ? tables().gm[fmt][o.ntb - 1] : tables().mma[o.ntb - 1][o.gpw - 2][o.rt - 1];
+  hipLaunchKernelGGL(k, dim3(grp.first[grp.n]), dim3(64 * o.ks), o.lds, st, a,
                      grp);
   return hipGetLastError();
 }
@@ -1733,7 +1935,7 @@ hipError_t launch_gemv_group(const MatDesc* const* ms, const void* const* xs, fl
     return launch_one(FMT_Q4_K, nU, 0, o, grp, x_f16, st, true);
   }
   const int64_t rb = static_cast<int64_t>(m0.row_bytes);
-  if (mma) return launch_mma(rb, m0.K, N, mm, grp, st);
+  if (mma) return launch_mma(m0.fmt, rb, m0.K, N, mm, grp, st);
   return N == 1 ? launch_one(m0.fmt, nU, rb, o, grp, x_f16, st) : launch_multi(m0.fmt, nU, rb, N, mo, grp, x_f16, st);
 }
 
@@ -1765,7 +1967,7 @@ hipError_t launch_gemv(const MatDesc& m, const void* x, int x_f16, int N, float*
     grp.M[0] = M;
     grp.first[0] = 0;
     grp.first[1] = (M + 16 * mm.rt - 1) / (16 * mm.rt);
-    return launch_mma(static_cast<int64_t>(m.row_bytes), m.K, N, mm, grp, st);
+    return launch_mma(m.fmt, static_cast<int64_t>(m.row_bytes), m.K, N, mm, grp, st);
   }
   if (N >= 2) {
     MultiShape ms;

@@ -31,6 +31,13 @@ def _run(fmt, M, K, N, xdtype, seed):
                          f"gemv {fmt} M={M} K={K} N={N} {np.dtype(xdtype).name}")
 
 
+# formats whose fp16 tokens take the matrix cores (Q8_0's codes carry a bias of 128: it
+# stays on the vector path), and from how many tokens on (the library's dispatch)
+MC_FORMATS = [f for f in FORMATS if f != "q8_0"]
+MC_MIN_TOKENS = {"q4_0": 8, "q4_k": 12, "q6_k": 16, "a4g64": 5, "q4_1": 5, "q5_0": 12, "q5_1": 5,
+                 "q2_k": 12, "q3_k": 24, "q5_k": 16}
+
+
 def _ks(fmt):
     bw = oracle.block_weights(fmt)
     return sorted({k for k in (bw, 256, 512, 768, 1024, 2560) if k % bw == 0})
@@ -110,11 +117,11 @@ def test_gemv_tokens_long_rows(fmt, xdtype):
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_gemv_tokens_match_single_token_calls(fmt):
     """Every vector path sums the same unit partials in the same order, so a call with N
-    tokens returns, bit for bit, what N one-token calls return (fp16 tokens of 4-bit
-    affine groups at 5..32 tokens take the matrix cores instead: see below)."""
+    tokens returns, bit for bit, what N one-token calls return (fp16 tokens from a few
+    on take the matrix cores instead, every format but Q8_0: see below)."""
     M, K, N = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048, 11
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [48])), fmt, M, K)
-    for xdtype in (np.float32,) if fmt == "a4g64" else (np.float32, np.float16):
+    for xdtype in (np.float32,) if fmt in MC_FORMATS and N >= MC_MIN_TOKENS[fmt] else (np.float32, np.float16):
         x = to_dev(np.random.default_rng(48).standard_normal((N, K)).astype(xdtype))
         full = to_host(qm.gemv(x))
         for t in range(N):
@@ -221,20 +228,25 @@ def test_gemv_eight_rows_per_thread(fmt, M, K):
                       f"gemv {fmt} M={M} K={K} {np.dtype(xdt).name}")
 
 
-# fp16 tokens of 4-bit affine groups at 5..32 tokens take the matrix-core kernel: rows of
-# K = 64 .. 4096 (one to four groups per wave, a last wave with fewer groups, one wave),
-# a K past its range (the vector path), rows that are not a multiple of 16, and one or two
-# 16-token blocks
-@pytest.mark.parametrize("N", [5, 8, 16, 17, 32])
-def test_gemv_matrix_cores_fp16(N):
-    for M, K in ((67, 64), (67, 320), (35, 1024), (16, 2048), (130, 3072), (33, 4096), (20, 4160), (1, 1088)):
-        _run("a4g64", M, K, N, np.float16, [52, M, K, N])
+# fp16 tokens at 5..32 take the matrix-core kernels: rows of one block up to long K (one
+# to several units or groups per wave, a last wave with fewer, one wave), for 4-bit groups
+# a K past the kernel's range (the vector path), rows that are not a multiple of 16, and one
+# or two 16-token blocks
+@pytest.mark.parametrize("fmt", MC_FORMATS)
+@pytest.mark.parametrize("N", [5, 16, 17, 32])
+def test_gemv_matrix_cores_fp16(fmt, N):
+    bw = oracle.block_weights(fmt)
+    shapes = ((67, 64), (67, 320), (35, 1024), (16, 2048), (130, 3072), (33, 4096), (20, 4160), (1, 1088), (9, 9728))
+    for M, K in shapes:
+        K = (K + bw - 1) // bw * bw
+        _run(fmt, M, K, N, np.float16, [52, M, K, N])
 
 
-def test_gemv_matrix_cores_one_hot_is_exact():
-    """fp16 one-hot tokens through the matrix-core kernel: the code sum is q exactly and
-    the activation sum 1, so each output is round(s * q + b), the fp32 weight."""
-    fmt, M, K = "a4g64", 133, 1024
+@pytest.mark.parametrize("fmt", MC_FORMATS)
+def test_gemv_matrix_cores_one_hot_is_exact(fmt):
+    """fp16 one-hot tokens through the matrix-core kernels: the code sum is q exactly and
+    the activation sum 1, so each output is round(a * q + b), the fp32 weight."""
+    M, K = 133, 1024
     blob = make_matrix(fmt, M, K, [53])
     w = oracle.dequantize(fmt, blob, M, K)
     qm = q.QMatrix(to_dev(blob), fmt, M, K)
@@ -247,32 +259,35 @@ def test_gemv_matrix_cores_one_hot_is_exact():
             assert np.array_equal(y[t], w[:, k]), f"token {t} (k={k})"
 
 
-def test_gemv_matrix_cores_subnormal_tokens():
+@pytest.mark.parametrize("fmt", MC_FORMATS)
+def test_gemv_matrix_cores_subnormal_tokens(fmt):
     """fp16 activations in the subnormal range (2^-24 .. 2^-15): exact inputs of the
     matrix cores, whose products (code * 2^-24 * x, down to 2^-48) stay normal fp32."""
-    fmt, M, K = "a4g64", 96, 2048
+    M, K = 96, 2048
     blob = make_matrix(fmt, M, K, [54])
     w = oracle.dequantize(fmt, blob, M, K)
     qm = q.QMatrix(to_dev(blob), fmt, M, K)
     g = np.random.default_rng(54)
-    x = (g.integers(-1023, 1024, (8, K)) * 2.0 ** -24).astype(np.float16)
+    x = (g.integers(-1023, 1024, (32, K)) * 2.0 ** -24).astype(np.float16)
     assert np.all(np.abs(x.astype(np.float32)) < 2.0 ** -14)
     y = to_host(qm.gemv(to_dev(x)))
     assert_within(y, oracle.matmul_ref(x, w), oracle.tolerance_scale(x, w), TOL, "gemv a4g64 subnormal fp16 tokens")
 
 
-@pytest.mark.parametrize("N", [11, 32])
-def test_gemv_matrix_cores_match_other_token_counts(N):
+@pytest.mark.parametrize("fmt", MC_FORMATS)
+def test_gemv_matrix_cores_match_other_token_counts(fmt):
     """On the matrix cores a token's outputs depend on its own activations, K and the
-    kernel's fixed order only: an N-token call returns, bit for bit, what calls on
-    windows of 5 of its tokens return (token blocks of 16 included)."""
-    fmt, M, K = "a4g64", 300, 2048
+    kernel's fixed order only: a 32-token call returns, bit for bit, what calls on
+    windows of its tokens return, down to the fewest the matrix cores take (one and two
+    16-token blocks)."""
+    M, K, N = 300, 2048, 32
+    w_ = MC_MIN_TOKENS[fmt]
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [55])), fmt, M, K)
     x = to_dev(np.random.default_rng([55, N]).standard_normal((N, K)).astype(np.float16))
     full = to_host(qm.gemv(x))
-    for s0 in range(0, N - 4, 3):
-        part = to_host(qm.gemv(x[s0:s0 + 5].contiguous()))
-        assert np.array_equal(full[s0:s0 + 5].view(np.uint32), part.view(np.uint32)), (N, s0)
+    for s0, n in {(0, w_), (N - w_, w_), (3, max(w_, 17)), (5, max(w_, 20))}:
+        part = to_host(qm.gemv(x[s0:s0 + n].contiguous()))
+        assert np.array_equal(full[s0:s0 + n].view(np.uint32), part.view(np.uint32)), (s0, n)
 
 
 def test_gemv_matrix_cores_two_row_tiles():
@@ -295,12 +310,14 @@ def test_gemv_matrix_cores_two_row_tiles():
         assert np.array_equal(y[t], w[:, k]), f"token {t} (k={k})"
 
 
-@pytest.mark.parametrize("N", [5, 16, 20])
+@pytest.mark.parametrize("N", [5, 16, 24])
 def test_gemv_group_matrix_cores_match_single_calls(N):
-    """fp16 tokens of 4-bit affine groups in grouped calls: a launch of the group's total
-    rows (5200 here, more 16-row tiles than CUs: two row tiles per wave) gives every output
-    the bits of its own single call (fewer rows: one tile per wave), within the bound."""
-    shapes = [("a4g64", 2048, 1024), ("a4g64", 1024, 1024), ("a4g64", 2128, 1024), ("a4g64", 37, 2048)]
+    """fp16 tokens on the matrix cores in grouped calls: a launch of the group's total rows
+    (5200 4-bit-group rows here, more 16-row tiles than CUs: two row tiles per wave; Q4_K
+    and Q6_K rows together, Q3_K alone) gives every output the bits of its own single call,
+    within the bound."""
+    shapes = [("a4g64", 2048, 1024), ("a4g64", 1024, 1024), ("a4g64", 2128, 1024), ("a4g64", 37, 2048),
+              ("q4_k", 300, 2560), ("q4_k", 77, 2560), ("q6_k", 100, 2560), ("q3_k", 50, 1024)]
     qms, xs, ws, xh = [], [], [], []
     for i, (fmt, M, K) in enumerate(shapes):
         blob = make_matrix(fmt, M, K, [59, i])
