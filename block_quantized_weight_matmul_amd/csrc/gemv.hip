@@ -46,6 +46,7 @@
 namespace qmm {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 struct GemvArgs {
@@ -306,6 +307,27 @@ struct MixPairs<FMT_Q6_K> {
       ev[1][k] = (ql & 0x00F000F0u) | (t & 0x03000300u);
       od[0][k] = (qlo & 0x000F000Fu) | (tod & 0x00300030u);
       od[1][k] = (qlo & 0x00F000F0u) | (tod & 0x03000300u);
+    }
+  }
+};
+
+// Q8_0: signed byte codes.  A pair is built as the fp16 normals 1024 + (q + 128), from
+// which 1152 is subtracted in packed fp16 -- exact, all integers below 2048 -- so it holds
+// q itself (sh = 24: no 2^-24 scaling), and every product and partial sum is item_partial's
+// with the codes as signed floats, bit for bit.
+template <>
+struct MixPairs<FMT_Q8_0> {
+  u32 ev[1][8], od[1][8];
+  static constexpr int sh(int) { return 24; }
+  __device__ __forceinline__ void make(const Item<FMT_Q8_0>::Raw& w, const Unit (&)[1]) {
+    const half2v off = {1152, 1152};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const u32 c = w.q.word(k) ^ 0x80808080u;  // q + 128
+      const half2v e = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, c, 0x04020400u)) - off;
+      const half2v o = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, c, 0x04030401u)) - off;
+      ev[0][k] = __builtin_bit_cast(u32, e);
+      od[0][k] = __builtin_bit_cast(u32, o);
     }
   }
 };
@@ -785,7 +807,12 @@ __device__ __forceinline__ void multi_run(const MixPairs<F> (&pk)[R], const Unit
 #pragma unroll
   for (int q = 0; q < R; ++q) {
     const Unit& u = o[q][r];
-    v[q] = __builtin_fmaf(u.a0 * sc, s[q][0], __builtin_fmaf(u.b0, sx0, __builtin_fmaf(u.a1 * sc, s[q][1], u.b1 * sx1)));
+    if constexpr (F == FMT_Q8_0) {  // item_partial's expression (no b terms)
+      v[q] = __builtin_fmaf(u.a0, s[q][0], u.a1 * s[q][1]);
+    } else {
+      v[q] = __builtin_fmaf(u.a0 * sc, s[q][0],
+                            __builtin_fmaf(u.b0, sx0, __builtin_fmaf(u.a1 * sc, s[q][1], u.b1 * sx1)));
+    }
   }
 }
 
@@ -1538,15 +1565,10 @@ constexpr void fill_one(GemvGroupKernel (&t)[2][4]) {
 
 template <int F>
 constexpr void fill_multi(GemvGroupKernel (&t)[2], GemvKernel (&ti)[2]) {
-  if constexpr (F == FMT_Q8_0) {  // its codes carry a bias: the general path takes it
-    t[0] = t[1] = nullptr;
-    ti[0] = ti[1] = nullptr;
-  } else {
-    t[0] = k_gemvn<F, false, 1>;
-    t[1] = k_gemvn<F, true, 1>;
-    ti[0] = k_gemvn_id<F, false>;
-    ti[1] = k_gemvn_id<F, true>;
-  }
+  t[0] = k_gemvn<F, false, 1>;
+  t[1] = k_gemvn<F, true, 1>;
+  ti[0] = k_gemvn_id<F, false>;
+  ti[1] = k_gemvn_id<F, true>;
 }
 
 struct Tables {
@@ -1736,15 +1758,13 @@ hipError_t launch_one(int fmt, int nU, int64_t row_bytes, const OneShape& o, con
 // 4-bit-group layer at 16 tokens 53.6 -> 50.5 us, while 2 and 4 tokens lose 4-5%),
 // TGN token groups filling up to 512 threads, TP tokens per pass as the LDS budget
 // and kXNRounds staging rounds allow.  M: the rows of the launch (of one matrix or
-// of a group).  False for Q8_0 (its codes carry a bias: the general path takes it)
-// and for shapes that do not fit.
+// of a group).  False for shapes that do not fit.
 struct MultiShape {
   int Ge, RW, TGN, TP, threads;
   size_t lds;
 };
 
 bool multi_shape(int fmt, int nU, int64_t M, int N, int x_f16, int cus, MultiShape& o) {
-  if (fmt == FMT_Q8_0) return false;
   const int ipr2 = nU / kRuns[fmt];
   if (ipr2 < 1 || ipr2 > 512) return false;
   const int Gmax = 512 / ipr2;
@@ -2044,7 +2064,7 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
     hipLaunchKernelGGL(tables().narrow_id[x_f16 ? 1 : 0], dim3((M + RW - 1) / RW, ranks), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  if (m.fmt != FMT_Q8_0) {
+  {
     // the few-token layout per expert: about two workgroups per CU over the
     // active experts, each G row groups x id_rows rows per thread, the pairs
     // staged TP at a time in one round
