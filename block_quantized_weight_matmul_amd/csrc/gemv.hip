@@ -1112,8 +1112,8 @@ __global__ __launch_bounds__(1024) void k_gemvm_a4(GemvArgs a, GemvGroup grp) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// The same matrix-core arithmetic for the other formats whose codes carry no large bias
-// (all but Q8_0 and the 4-bit groups above), unit by unit: a unit's 32 weights share one
+// The same matrix-core arithmetic for the other formats, unit by unit (Q8_0's signed
+// codes as exact fp16 normals, with no bias term): a unit's 32 weights share one
 // (a, b) pair, or one per 16-weight half (Q6_K, Q2_K, Q3_K), and each output takes
 // a * (sum of q_k x_k) + b * (sum of x_k) per unit or half, both sums on the matrix
 // cores with exact operands (codes as fp16 subnormals, fp16 activations, fp32 sums):
@@ -1215,6 +1215,25 @@ __global__ __launch_bounds__(64 * kUnitMaxWaves) void k_gemvm(GemvArgs a, GemvGr
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[d][b][i] = fmaf(b1, s1[i], fmaf(a1, q1[i], fmaf(b0, s0[i], fmaf(a0, q0[i], acc[d][b][i]))));
+      }
+    } else if constexpr (F == FMT_Q8_0) {
+      // signed codes as exact fp16 normals (1024 + (q + 128), less 1152): y += d * sum q x
+      const float dq = live ? o.a0 : 0.0f;
+      const u32 w0 = pick4(kq, o.c[0], o.c[2], o.c[4], o.c[6]), w1 = pick4(kq, o.c[1], o.c[3], o.c[5], o.c[7]);
+      const half2v off = {1152, 1152};
+      half2v h[4] = {__builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)),
+                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)),
+                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)),
+                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u))};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = h[i] - off;
+      const half8 c = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+#pragma unroll
+      for (int b = 0; b < NTB; ++b) {
+        const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xs[d][b]), c,
+                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d][b][i] = fmaf(dq, q[i], acc[d][b][i]);
       }
     } else {
       const uint2 p0 = code_pairs(pick4(kq, o.c[0], o.c[2], o.c[4], o.c[6]));
@@ -1585,7 +1604,7 @@ struct Tables {
   GemvGroupKernel gm[kNumFormats][2];  // k_gemvm: [format][token blocks - 1] (null: not on that path)
   template <int F>
   void fill_format() {
-    if constexpr (F == FMT_Q8_0 || F == FMT_A4G64) {
+    if constexpr (F == FMT_A4G64) {
       gm[F][0] = gm[F][1] = nullptr;
     } else {
       gm[F][0] = k_gemvm<F, 1>;
@@ -1834,7 +1853,7 @@ struct MmaShape {
 // Q4_K 14.0/22.9/39.2 -> 16.4/17.7/21.3, Q6_K 19.7/31.3/55.3 -> 26.3/28.6/35.7).  Each
 // lane decodes its row's whole unit, so the kernel's fixed cost grows with the decoder's.
 constexpr int kUnitMinTokens[kNumFormats] = {
-    /* Q4_0 */ 8, /* Q8_0 */ 33, /* Q4_K */ 12, /* Q6_K */ 16, /* A4G64 */ 33, /* Q4_1 */ 5,
+    /* Q4_0 */ 8, /* Q8_0 */ 12, /* Q4_K */ 12, /* Q6_K */ 16, /* A4G64 */ 33, /* Q4_1 */ 5,
     /* Q5_0 */ 12, /* Q5_1 */ 5, /* Q2_K */ 12, /* Q3_K */ 24, /* Q5_K */ 16};
 
 bool mma_unit_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {

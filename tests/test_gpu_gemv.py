@@ -31,10 +31,9 @@ def _run(fmt, M, K, N, xdtype, seed):
                          f"gemv {fmt} M={M} K={K} N={N} {np.dtype(xdtype).name}")
 
 
-# formats whose fp16 tokens take the matrix cores (Q8_0's codes carry a bias of 128: it
-# stays on the vector path), and from how many tokens on (the library's dispatch)
-MC_FORMATS = [f for f in FORMATS if f != "q8_0"]
-MC_MIN_TOKENS = {"q4_0": 8, "q4_k": 12, "q6_k": 16, "a4g64": 5, "q4_1": 5, "q5_0": 12, "q5_1": 5,
+# fp16 tokens take the matrix cores from a format's token count on (the library's dispatch)
+MC_FORMATS = list(FORMATS)
+MC_MIN_TOKENS = {"q4_0": 8, "q8_0": 12, "q4_k": 12, "q6_k": 16, "a4g64": 5, "q4_1": 5, "q5_0": 12, "q5_1": 5,
                  "q2_k": 12, "q3_k": 24, "q5_k": 16}
 
 
@@ -118,7 +117,7 @@ def test_gemv_tokens_long_rows(fmt, xdtype):
 def test_gemv_tokens_match_single_token_calls(fmt):
     """Every vector path sums the same unit partials in the same order, so a call with N
     tokens returns, bit for bit, what N one-token calls return (fp16 tokens from a few
-    on take the matrix cores instead, every format but Q8_0: see below)."""
+    on take the matrix cores instead: see below)."""
     M, K, N = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048, 11
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [48])), fmt, M, K)
     for xdtype in (np.float32,) if fmt in MC_FORMATS and N >= MC_MIN_TOKENS[fmt] else (np.float32, np.float16):
