@@ -576,9 +576,9 @@ def extra_prefill_batch(torch, q, W, args):
 
 
 def extra_formats(torch, q, W, args):
-    """Every block format on one 4096 x 4096 matrix: the one-token matrix-vector call
-    (quantized-weight GB/s) and the 512-token matrix-core call (TFLOP/s), weights rotated
-    over > 1 GiB of copies per sample."""
+    """Every block format on one 4096 x 4096 matrix: the one-token and the 16-token (fp16)
+    matrix-vector calls (quantized-weight GB/s) and the 512-token matrix-core call
+    (TFLOP/s), weights rotated over > 1 GiB of copies per sample."""
     res = []
     for fmt in W.ALL_FORMATS:
         d = W.format_sweep_weights(fmt)
@@ -594,6 +594,15 @@ def extra_formats(torch, q, W, args):
         row["gemv_n1_us"] = us
         row["gemv_n1_weight_gbs"] = d["blob"].size / (us * 1e-6) / 1e9
         row["gemv_n1_frac_hbm"] = row["gemv_n1_weight_gbs"] / HBM_PEAK_GBS
+        # 16 fp16 tokens (qmm_gemv): the matrix cores take every format from at most 16
+        x16 = torch.from_numpy(W.format_sweep_x(16)).to("cuda").half()
+        y16 = torch.empty((16, d["M"]), device="cuda")
+        g = capture(torch, lambda: [q.qmm_gemv(h.handle, x16, 16, y16) for h in hs])
+        us = time_graph(torch, g, args.rounds) * 1e3 / len(hs)
+        del g
+        row["gemv_n16_f16_us"] = us
+        row["gemv_n16_f16_weight_gbs"] = d["blob"].size / (us * 1e-6) / 1e9
+        row["gemv_n16_f16_tflops"] = 2.0 * d["M"] * d["K"] * 16 / (us * 1e-6) / 1e12
         n = 512
         xn = torch.from_numpy(W.format_sweep_x(n)).to("cuda")
         yn = torch.empty((n, d["M"]), device="cuda")
@@ -608,8 +617,9 @@ def extra_formats(torch, q, W, args):
         res.append(row)
         del hs, rot, x1, y1, xn, yn, ws
         torch.cuda.empty_cache()
-    return {"workload": "every block format, 4096 x 4096, N(0,0.02^2) weights; 1 fp32 token (qmm_gemv) and "
-                        "512 fp16 tokens (qmm_gemm_ws, auto tile); weights rotated over >1 GiB per sample",
+    return {"workload": "every block format, 4096 x 4096, N(0,0.02^2) weights; 1 fp32 token and 16 fp16 "
+                        "tokens (qmm_gemv), 512 fp16 tokens (qmm_gemm_ws, auto tile); weights rotated over "
+                        ">1 GiB per sample",
             "results": res}
 
 
