@@ -1858,6 +1858,8 @@ constexpr int kUnitMinTokens[kNumFormats] = {
 
 bool mma_unit_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
   if (!x_f16 || N < kUnitMinTokens[fmt] || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
+  // the activations are read through a buffer of N * K fp16 values with 32-bit offsets
+  if (static_cast<int64_t>(N) * K * 2 >= (int64_t(1) << 31)) return false;
   const int64_t nU = K / 32;
   const int64_t per = (nU + kUnitMaxWaves - 1) / kUnitMaxWaves;
   const int64_t upw = (per + kUnitRing - 1) / kUnitRing * kUnitRing;
