@@ -1077,11 +1077,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_id(GemmArgs a) {
 // a wave owns 16 rows (A rows) against one 16-token block (B columns; lanes of tokens
 // past N load nothing and multiply zeros) and a run of SPW consecutive K stages,
 // its loads kept D stages ahead of its products in registers.  At a few tokens a weight
-// meets at most 16 tokens, so what bounds a call is bringing its bytes in: a stage of
-// 16 rows x 64 weights is one load per lane for the weights and one per token block for
-// the activations, and every wave of the chip has D of them in flight.  KS waves cover K;
-// their partial outputs are summed in LDS in wave order, so an output depends on K (which
-// fixes SPW and KS) and not on N, M or the token tile: both tiles give the same bits.
+// meets at most 16 tokens, so fetching each weight's bytes and decoding it into an fp16
+// operand -- which k_gemm spreads over 64 or more tokens -- set the time, not the
+// products.  KS waves cover K; their partial outputs are summed in LDS in wave order, so
+// an output depends on the call's shape and activation type (which fix SPW and KS) and
+// not on N or the token tile: both tiles give the same bits.
 // Activations of a stage through buffer loads: a lane of a token past N, or of a chunk
 // past K, gets an offset past the buffer's end, which the hardware answers with zeros
 // without touching memory -- no branch, so the loads of every stage are counted alike
