@@ -1119,32 +1119,31 @@ __global__ __launch_bounds__(1024) void k_gemvm_a4(GemvArgs a, GemvGroup grp) {
 // cores with exact operands (codes as fp16 subnormals, fp16 activations, fp32 sums):
 // a 32-deep v_mfma_f32_16x16x32_f16 step per unit, or a 16-deep v_mfma_f32_16x16x16_f16
 // step per half.  Lane group l / 16 holds the unit's weights 8 (l / 16) .. +7 (or 4 (l / 16)
-// .. +3 of each half); every lane loads and decodes its row's whole unit with the
-// format's unit decoder and takes its words by a select.  A wave runs UPW consecutive
-// units of its 16 rows with D units of loads in flight (a ring, its last turn peeled,
-// units past K multiplying zero coefficients by zero activations), one accumulator per
-// ring slot; the KS waves of a workgroup cover K and their sums are added in LDS in wave
-// order, so an output depends on its token's activations and K only.
+// .. +3 of each half).  A wave runs UPW consecutive units of its 16 rows in steps of 4:
+// lane group g loads and decodes unit g of the step with the format's unit decoder (each
+// unit once, not once per lane group) and leaves its 32 codes and (a * 2^24, b) pairs in
+// the wave's LDS slot, from which every lane group reads the words and coefficients of
+// each unit it multiplies.  D steps of loads are in flight (a ring, its last turn
+// peeled; units past K multiply zero coefficients by zero activations), with one
+// accumulator per unit of a step; the KS waves of a workgroup cover K and their sums are
+// added in LDS in wave order, so an output depends on its token's activations and K only.
 template <int F> constexpr bool unit_halves() { return F == FMT_Q6_K || F == FMT_Q2_K || F == FMT_Q3_K; }
 // at most 8 waves per workgroup (256 registers: the widest decoders' raw units, and two
 // token blocks, spill at 128), for one token block as for two, so that the split of K --
 // and with it every output's bits -- does not depend on the token count
 constexpr int kUnitMaxWaves = 8;
-constexpr int kUnitRing = 4;
+constexpr int kExWords = 12;  // LDS words per (row, unit): 8 code words, a0 * 2^24, b0, a1 * 2^24, b1
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
 // codes of bytes 0, 1 and 2, 3 of w as fp16 subnormal pairs (code * 2^-24, exact)
 __device__ __forceinline__ uint2 code_pairs(u32 w) {
   return uint2{__builtin_amdgcn_perm(0u, w, 0x0C010C00u), __builtin_amdgcn_perm(0u, w, 0x0C030C02u)};
 }
-__device__ __forceinline__ u32 pick4(int kq, u32 w0, u32 w1, u32 w2, u32 w3) {
-  return kq == 0 ? w0 : (kq == 1 ? w1 : (kq == 2 ? w2 : w3));
-}
 
 template <int F, int NTB>
 __global__ __launch_bounds__(64 * kUnitMaxWaves) void k_gemvm(GemvArgs a, GemvGroup grp) {
   using Dec = Decoder<F>;
-  constexpr int D = kUnitRing;
+  constexpr int D = 2;  // steps in flight
   constexpr bool H = unit_halves<F>();
   const u8* W;
   const void* xv;
@@ -1156,129 +1155,143 @@ __global__ __launch_bounds__(64 * kUnitMaxWaves) void k_gemvm(GemvArgs a, GemvGr
   const int w = threadIdx.x >> 6;
   const int KS = blockDim.x >> 6;
   const int K = a.K, N = a.N, nU = a.nU;
-  const int kq = lane >> 4;
-  const int upw = a.chunk_units;  // units per wave, a multiple of D
+  const int kq = lane >> 4, rr = lane & 15;
+  const int upw = a.chunk_units;  // units per wave, a multiple of 4 * D
   const int ub = w * upw;
-  const int row = min(r0 + (lane & 15), M - 1);  // rows past M repeat the last one (never stored)
+  const int row = min(r0 + rr, M - 1);  // rows past M repeat the last one (never stored)
   const u32 row_off = static_cast<u32>(row) * static_cast<u32>(a.row_bytes);
   const u32 xbytes = static_cast<u32>(N) * static_cast<u32>(K) * 2u;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(xv), 0, static_cast<int>(xbytes), 0x00020000);
+  u32* ex = reinterpret_cast<u32*>(s_dyn) + KS * NTB * 256 + w * (16 * 4 * kExWords);  // this wave's slot
+  u32* mine = ex + (rr * 4 + kq) * kExWords;  // (row rr, unit kq of the step)
 
   typename Dec::Raw rw[D];
-  uint4 xs[D][NTB];
-  // unit u into slot d: the row's unit (clamped to the last one) and, per token block,
-  // the lane's 8 activations (4 of each half): zeros for tokens past N and units past K,
-  // which the buffer loads return for an offset past the end, with no branch
-  auto fetch = [&](int u, int d) {
-    const int uc = min(u, nU - 1);
-    Dec::load(W, row_off, uc, rw[d]);
+  uint4 xs[D][4][NTB];
+  auto fetch = [&](int u0, int d) {  // step of units u0 .. u0 + 3
+    Dec::load(W, row_off, min(u0 + kq, nU - 1), rw[d]);
 #pragma unroll
-    for (int b = 0; b < NTB; ++b) {
-      const int tok = 16 * b + (lane & 15);
-      const bool in = tok < N && u < nU;
-      const u32 base = (static_cast<u32>(tok) * static_cast<u32>(K) + 32u * static_cast<u32>(uc)) * 2u;
+    for (int j = 0; j < 4; ++j) {
+      const int u = u0 + j, uc = min(u, nU - 1);
+#pragma unroll
+      for (int b = 0; b < NTB; ++b) {
+        const int tok = 16 * b + rr;
+        const bool in = tok < N && u < nU;
+        const u32 base = (static_cast<u32>(tok) * static_cast<u32>(K) + 32u * static_cast<u32>(uc)) * 2u;
+        if constexpr (H) {
+          const u32 o0 = in ? base + 8u * kq : xbytes, o1 = in ? base + 32u + 8u * kq : xbytes;
+          const uint2 v0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, 0));
+          const uint2 v1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, 0));
+          xs[d][j][b] = uint4{v0.x, v0.y, v1.x, v1.y};
+        } else {
+          xs[d][j][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, in ? base + 16u * kq : xbytes, 0, 0));
+        }
+      }
+    }
+  };
+  floatx4 acc[4][NTB];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < NTB; ++b) acc[j][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int u0, int d) {
+    {  // this lane group's unit into the wave's slot
+      Unit o;
+      Dec::unpack(rw[d], o);
+      const bool live = u0 + kq < nU;
+      const float sc = F == FMT_Q8_0 ? 1.0f : 16777216.0f;  // Q8_0: codes enter as q, not q * 2^-24
+      uint4* m4 = reinterpret_cast<uint4*>(mine);
+      m4[0] = uint4{o.c[0], o.c[1], o.c[2], o.c[3]};
+      m4[1] = uint4{o.c[4], o.c[5], o.c[6], o.c[7]};
+      m4[2] = uint4{__builtin_bit_cast(u32, live ? o.a0 * sc : 0.0f), __builtin_bit_cast(u32, live ? o.b0 : 0.0f),
+                    __builtin_bit_cast(u32, live ? o.a1 * sc : 0.0f), __builtin_bit_cast(u32, live ? o.b1 : 0.0f)};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32* e = ex + (rr * 4 + j) * kExWords;
+      const float4 cf = *reinterpret_cast<const float4*>(e + 8);  // (a0', b0, a1', b1) of row rr, unit j
       if constexpr (H) {
-        const u32 o0 = in ? base + 8u * kq : xbytes, o1 = in ? base + 32u + 8u * kq : xbytes;
-        const uint2 v0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, 0));
-        const uint2 v1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, 0));
-        xs[d][b] = uint4{v0.x, v0.y, v1.x, v1.y};
+        const half4 c0 = __builtin_bit_cast(half4, code_pairs(e[kq]));
+        const half4 c1 = __builtin_bit_cast(half4, code_pairs(e[4 + kq]));
+        const half4 ones = {1, 1, 1, 1};
+#pragma unroll
+        for (int b = 0; b < NTB; ++b) {
+          const half4 x0 = __builtin_bit_cast(half4, uint2{xs[d][j][b].x, xs[d][j][b].y});
+          const half4 x1 = __builtin_bit_cast(half4, uint2{xs[d][j][b].z, xs[d][j][b].w});
+          const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+          const floatx4 q0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, c0, z, 0, 0, 0);
+          const floatx4 s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, ones, z, 0, 0, 0);
+          const floatx4 q1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, c1, z, 0, 0, 0);
+          const floatx4 s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, ones, z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[j][b][i] = fmaf(cf.w, s1[i], fmaf(cf.z, q1[i], fmaf(cf.y, s0[i], fmaf(cf.x, q0[i], acc[j][b][i]))));
+        }
+      } else if constexpr (F == FMT_Q8_0) {
+        const uint2 cw = *reinterpret_cast<const uint2*>(e + 2 * kq);
+        const half2v off = {1152, 1152};
+        half2v h[4] = {__builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, cw.x, 0x04010400u)),
+                       __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, cw.x, 0x04030402u)),
+                       __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, cw.y, 0x04010400u)),
+                       __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, cw.y, 0x04030402u))};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = h[i] - off;
+        const half8 c = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+#pragma unroll
+        for (int b = 0; b < NTB; ++b) {
+          const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xs[d][j][b]), c,
+                                                                   floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][b][i] = fmaf(cf.x, q[i], acc[j][b][i]);
+        }
       } else {
-        xs[d][b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, in ? base + 16u * kq : xbytes, 0, 0));
+        const uint2 cw = *reinterpret_cast<const uint2*>(e + 2 * kq);
+        const uint2 p0 = code_pairs(cw.x), p1 = code_pairs(cw.y);
+        const half8 c = __builtin_bit_cast(half8, uint4{p0.x, p0.y, p1.x, p1.y});
+        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+        for (int b = 0; b < NTB; ++b) {
+          const half8 xh = __builtin_bit_cast(half8, xs[d][j][b]);
+          const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+          const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, c, z, 0, 0, 0);
+          const floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ones, z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][b][i] = fmaf(cf.y, sx[i], fmaf(cf.x, q[i], acc[j][b][i]));
+        }
       }
     }
+    // every lane group has read this step's slot before the next step writes it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  floatx4 acc[D][NTB];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-#pragma unroll
-    for (int b = 0; b < NTB; ++b) acc[d][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int u, int d) {
-    const bool live = u < nU;
-    Unit o;
-    Dec::unpack(rw[d], o);
-    const float a0 = live ? o.a0 * 16777216.0f : 0.0f, b0 = live ? o.b0 : 0.0f;  // a * 2^24, exact
-    if constexpr (H) {
-      const float a1 = live ? o.a1 * 16777216.0f : 0.0f, b1 = live ? o.b1 : 0.0f;
-      const uint2 p0 = code_pairs(pick4(kq, o.c[0], o.c[1], o.c[2], o.c[3]));
-      const uint2 p1 = code_pairs(pick4(kq, o.c[4], o.c[5], o.c[6], o.c[7]));
-      const half4 c0 = __builtin_bit_cast(half4, p0), c1 = __builtin_bit_cast(half4, p1);
-      const half4 ones = {1, 1, 1, 1};
-#pragma unroll
-      for (int b = 0; b < NTB; ++b) {
-        const half4 x0 = __builtin_bit_cast(half4, uint2{xs[d][b].x, xs[d][b].y});
-        const half4 x1 = __builtin_bit_cast(half4, uint2{xs[d][b].z, xs[d][b].w});
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        const floatx4 q0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, c0, z, 0, 0, 0);
-        const floatx4 s0 = __builtin_amdgcn_mfma_f32_16x16x16f16(x0, ones, z, 0, 0, 0);
-        const floatx4 q1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, c1, z, 0, 0, 0);
-        const floatx4 s1 = __builtin_amdgcn_mfma_f32_16x16x16f16(x1, ones, z, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[d][b][i] = fmaf(b1, s1[i], fmaf(a1, q1[i], fmaf(b0, s0[i], fmaf(a0, q0[i], acc[d][b][i]))));
-      }
-    } else if constexpr (F == FMT_Q8_0) {
-      // signed codes as exact fp16 normals (1024 + (q + 128), less 1152): y += d * sum q x
-      const float dq = live ? o.a0 : 0.0f;
-      const u32 w0 = pick4(kq, o.c[0], o.c[2], o.c[4], o.c[6]), w1 = pick4(kq, o.c[1], o.c[3], o.c[5], o.c[7]);
-      const half2v off = {1152, 1152};
-      half2v h[4] = {__builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u)),
-                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u)),
-                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u)),
-                     __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u))};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = h[i] - off;
-      const half8 c = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-#pragma unroll
-      for (int b = 0; b < NTB; ++b) {
-        const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, xs[d][b]), c,
-                                                                 floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d][b][i] = fmaf(dq, q[i], acc[d][b][i]);
-      }
-    } else {
-      const uint2 p0 = code_pairs(pick4(kq, o.c[0], o.c[2], o.c[4], o.c[6]));
-      const uint2 p1 = code_pairs(pick4(kq, o.c[1], o.c[3], o.c[5], o.c[7]));
-      const half8 c = __builtin_bit_cast(half8, uint4{p0.x, p0.y, p1.x, p1.y});
-      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-#pragma unroll
-      for (int b = 0; b < NTB; ++b) {
-        const half8 xh = __builtin_bit_cast(half8, xs[d][b]);
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        const floatx4 q = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, c, z, 0, 0, 0);
-        const floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, ones, z, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d][b][i] = fmaf(b0, sx[i], fmaf(a0, q[i], acc[d][b][i]));
-      }
-    }
-  };
-  // (scheduling barriers keep each unit's decode behind its own wait)
-#pragma unroll
-  for (int d = 0; d < D; ++d) fetch(ub + d, d);
+  for (int d = 0; d < D; ++d) fetch(ub + 4 * d, d);
   int u = ub;
-  for (int turn = D; turn < upw; turn += D, u += D) {
+  for (int turn = 4 * D; turn < upw; turn += 4 * D, u += 4 * D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      compute(u + d, d);
+      compute(u + 4 * d, d);
       __builtin_amdgcn_sched_barrier(0);
-      fetch(u + d + D, d);
+      fetch(u + 4 * d + 4 * D, d);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    compute(u + d, d);
+    compute(u + 4 * d, d);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // D[4 (l / 16) + i][l % 16] of token block b: token 16b + 4 (l / 16) + i, row r0 + l % 16;
-  // the slots' sums added in slot order, then the waves' in wave order
 #pragma unroll
   for (int b = 0; b < NTB; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = acc[0][b][i];
 #pragma unroll
-      for (int d = 1; d < D; ++d) v += acc[d][b][i];
+      for (int j = 1; j < 4; ++j) v += acc[j][b][i];
       s_dyn[((w * NTB + b) * 4 + i) * 64 + lane] = v;
     }
   __syncthreads();
@@ -1845,31 +1858,33 @@ struct MmaShape {
   size_t lds;
 };
 
-// k_gemvm's shape: KS = ceil(units / UPW) waves (at most 8), UPW a multiple of the ring
-// depth -- a function of K alone.
-// Fewest tokens at which k_gemvm takes a format's calls: from there it was the faster
-// of the two on a 4096 x 4096 matrix (fp16 tokens, weights rotated over 32 copies; us at
-// 8 / 16 / 32 tokens, vector kernel -> matrix cores: Q4_0 17.4/27.8/50.6 -> 16.0/17.4/21.4,
-// Q4_K 14.0/22.9/39.2 -> 16.4/17.7/21.3, Q6_K 19.7/31.3/55.3 -> 26.3/28.6/35.7).  Each
-// lane decodes its row's whole unit, so the kernel's fixed cost grows with the decoder's.
+// k_gemvm's shape: KS = ceil(units / UPW) waves (at most 8), UPW a multiple of 8 (two
+// steps of 4 units) -- a function of K alone.
+// Fewest tokens at which k_gemvm takes a format's calls (one token always takes the
+// one-token kernel): from there it was the faster of the two on a 4096 x 4096 matrix
+// (fp16 tokens, weights rotated over 32 copies; us at 2 / 4 / 8 / 16 tokens, vector
+// kernel -> matrix cores: Q4_0 9.7/10.2/16.7/27.3 -> 9.2/9.3/9.2/10.0, Q5_K
+// 9.3/11.0/17.4/28.1 -> 10.1/10.1/10.5/11.4, Q6_K 9.6/11.9/19.3/31.2 ->
+// 12.1/12.2/13.1/15.5).  The decode of a step's units is spread over the wave, but the
+// exchange through LDS is a fixed cost that the dearer decoders pay at 2 and 3 tokens.
 constexpr int kUnitMinTokens[kNumFormats] = {
-    /* Q4_0 */ 8, /* Q8_0 */ 12, /* Q4_K */ 12, /* Q6_K */ 16, /* A4G64 */ 33, /* Q4_1 */ 5,
-    /* Q5_0 */ 12, /* Q5_1 */ 5, /* Q2_K */ 12, /* Q3_K */ 24, /* Q5_K */ 16};
+    /* Q4_0 */ 2, /* Q8_0 */ 4, /* Q4_K */ 2, /* Q6_K */ 5, /* A4G64 */ 33, /* Q4_1 */ 2,
+    /* Q5_0 */ 4, /* Q5_1 */ 2, /* Q2_K */ 4, /* Q3_K */ 5, /* Q5_K */ 4};
 
 bool mma_unit_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
-  if (!x_f16 || N < kUnitMinTokens[fmt] || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
+  if (!x_f16 || N < 2 || N < kUnitMinTokens[fmt] || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
   // the activations are read through a buffer of N * K fp16 values with 32-bit offsets
   if (static_cast<int64_t>(N) * K * 2 >= (int64_t(1) << 31)) return false;
   const int64_t nU = K / 32;
   const int64_t per = (nU + kUnitMaxWaves - 1) / kUnitMaxWaves;
-  const int64_t upw = (per + kUnitRing - 1) / kUnitRing * kUnitRing;
+  const int64_t upw = (per + 7) / 8 * 8;  // whole steps of 4 units, 2 in flight
   if (upw > INT_MAX) return false;
   o.upw = static_cast<int>(upw);
   o.ks = static_cast<int>((nU + upw - 1) / upw);
   o.gpw = 0;
   o.ntb = N > 16 ? 2 : 1;
   o.rt = 1;
-  o.lds = static_cast<size_t>(o.ks) * o.ntb * 256 * sizeof(float);
+  o.lds = (static_cast<size_t>(o.ks) * o.ntb * 256 + static_cast<size_t>(o.ks) * 16 * 4 * kExWords) * sizeof(float);
   return true;
 }
 

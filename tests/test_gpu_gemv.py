@@ -33,8 +33,8 @@ def _run(fmt, M, K, N, xdtype, seed):
 
 # fp16 tokens take the matrix cores from a format's token count on (the library's dispatch)
 MC_FORMATS = list(FORMATS)
-MC_MIN_TOKENS = {"q4_0": 8, "q8_0": 12, "q4_k": 12, "q6_k": 16, "a4g64": 5, "q4_1": 5, "q5_0": 12, "q5_1": 5,
-                 "q2_k": 12, "q3_k": 24, "q5_k": 16}
+MC_MIN_TOKENS = {"q4_0": 2, "q8_0": 4, "q4_k": 2, "q6_k": 5, "a4g64": 5, "q4_1": 2, "q5_0": 4, "q5_1": 2,
+                 "q2_k": 4, "q3_k": 5, "q5_k": 4}
 
 
 def _ks(fmt):
@@ -116,11 +116,14 @@ def test_gemv_tokens_long_rows(fmt, xdtype):
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_gemv_tokens_match_single_token_calls(fmt):
     """Every vector path sums the same unit partials in the same order, so a call with N
-    tokens returns, bit for bit, what N one-token calls return (fp16 tokens from a few
-    on take the matrix cores instead: see below)."""
-    M, K, N = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048, 11
+    tokens returns, bit for bit, what N one-token calls return (fp16 tokens take the
+    matrix cores from a few on, by format: up to there, here; from there, below)."""
+    M, K = 300, 2560 if 2560 % oracle.block_weights(fmt) == 0 else 2048
     qm = q.QMatrix(to_dev(make_matrix(fmt, M, K, [48])), fmt, M, K)
-    for xdtype in (np.float32,) if fmt in MC_FORMATS and N >= MC_MIN_TOKENS[fmt] else (np.float32, np.float16):
+    cases = [(np.float32, 11)]
+    if MC_MIN_TOKENS[fmt] > 2:
+        cases.append((np.float16, MC_MIN_TOKENS[fmt] - 1))
+    for xdtype, N in cases:
         x = to_dev(np.random.default_rng(48).standard_normal((N, K)).astype(xdtype))
         full = to_host(qm.gemv(x))
         for t in range(N):
@@ -227,12 +230,12 @@ def test_gemv_eight_rows_per_thread(fmt, M, K):
                       f"gemv {fmt} M={M} K={K} {np.dtype(xdt).name}")
 
 
-# fp16 tokens at 5..32 take the matrix-core kernels: rows of one block up to long K (one
-# to several units or groups per wave, a last wave with fewer, one wave), for 4-bit groups
-# a K past the kernel's range (the vector path), rows that are not a multiple of 16, and one
-# or two 16-token blocks
+# fp16 tokens from a format's few (2..5) to 32 take the matrix-core kernels: rows of one
+# block up to long K (one to several units or groups per wave, a last wave with fewer, one
+# wave), for 4-bit groups a K past the kernel's range (the vector path), rows that are not
+# a multiple of 16, and one or two 16-token blocks
 @pytest.mark.parametrize("fmt", MC_FORMATS)
-@pytest.mark.parametrize("N", [5, 16, 17, 32])
+@pytest.mark.parametrize("N", [2, 4, 5, 16, 17, 32])
 def test_gemv_matrix_cores_fp16(fmt, N):
     bw = oracle.block_weights(fmt)
     shapes = ((67, 64), (67, 320), (35, 1024), (16, 2048), (130, 3072), (33, 4096), (20, 4160), (1, 1088), (9, 9728))
