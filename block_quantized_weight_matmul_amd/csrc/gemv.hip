@@ -1441,8 +1441,11 @@ __global__ __launch_bounds__(512) void k_gemvn_id(GemvArgs a) {
                                      a.tok_pass, tm, sh.npairs, s_dyn);
 }
 
-// Expert-indexed, narrow rows: Q4_0 at K = 512, the shape of p2's case (its
-// section "Additional information"), where a row is 16 one-block items.  Lane l
+constexpr int kNarrowAhead = 4;  // items in flight per lane on the narrow-row kernels
+
+// Expert-indexed, narrow rows (Q4_0 at K = 512), for up to 64 pairs (or more than
+// k_gemv_id_narrow takes): the grid is (row slice, expert rank), each workgroup
+// routing the ids for itself.  Lane l
 // of a wave takes item l % 16 of one of the wave's four rows per step, so the 16
 // lanes of a row sum their partials with the same butterfly as every other path
 // (and in the same order as reduce_rows: 0 + the unit's partial, then sum16):
@@ -1451,10 +1454,8 @@ __global__ __launch_bounds__(512) void k_gemvn_id(GemvArgs a) {
 // flight per lane, routing once; each lane holds its unit's activations of up to
 // two pairs in registers (loaded from global memory with their half sums formed
 // as everywhere else), and further pairs take another sweep of the rows.
-constexpr int kNarrowAhead = 4;
-
 template <bool XH>
-__global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
+__global__ __launch_bounds__(256) void k_gemv_id_slices(GemvArgs a) {
   using It = Item<FMT_Q4_0>;
   constexpr int D = kNarrowAhead;
   constexpr int TPM = 2;
@@ -1560,6 +1561,300 @@ __global__ __launch_bounds__(256) void k_gemv_id_narrow(GemvArgs a) {
   }
 }
 
+// Expert-indexed, narrow rows: Q4_0 at K = 512, the shape of p2's case (its
+// section "Additional information"), where a row is 16 one-block items.  Lane l
+// of a wave takes item l % 16 of one of the wave's four rows per step, so the 16
+// lanes of a row sum their partials with the same butterfly as every other path
+// (and in the same order as reduce_rows: 0 + the unit's partial, then sum16):
+// results are the bits of the dense paths.
+//
+// The grid is as many workgroups as the device holds at once.  Each routes the
+// call's ids once, into an LDS table: the distinct valid experts in ascending
+// order (their ranks), the pairs sorted by expert, and the pair chunks -- an
+// expert's pairs two at a time.  The work is then one list of steps, chunk by
+// chunk, SPC steps of four rows per chunk (the expert's rows, padded to a
+// multiple of 8 steps); wave w streams steps [w T, (w + 1) T), T a multiple of 8,
+// with kNarrowAhead items in flight per lane, the ring running on across chunk
+// boundaries.  Each lane holds its unit's activations of the chunk's pairs in
+// registers, reloaded where a chunk begins.  Against k_gemv_id_slices, each of
+// whose workgroups routes, loads its activations and fills its ring before a short
+// stream of its own, this routes once per workgroup and streams without a pause;
+// it takes calls of more than 64 pairs, below which its routing, repeated by every
+// workgroup and longer with more pairs, costs more than it saves.
+
+// LDS ints of the narrow kernel's routing: each pair's expert (P rounded up to 4),
+// presence bitmap and its word prefix counts (E / 32 words each), per rank the first
+// sorted pair and the first chunk (P + 1 each) and the expert (P), per pair its place
+// among its expert's pairs, the sorted pairs and the chunks (P each), then the
+// counts of chunks and ranks and the flag of invalid ids.  The kernel takes at most
+// kNarrowMaxPairs pairs (each thread counts the pairs before its own).
+constexpr int kNarrowMaxPairs = 512;
+inline size_t narrow_lds_ints(int E, int P) {
+  const size_t w = (static_cast<size_t>(E) + 31) / 32;
+  const size_t p4 = (static_cast<size_t>(P) + 3) / 4 * 4;
+  return p4 + 2 * w + 2 * (static_cast<size_t>(P) + 1) + 4 * static_cast<size_t>(P) + 3;
+}
+
+template <bool XH>
+__global__ __launch_bounds__(256, 2) void k_gemv_id_narrow(GemvArgs a) {
+  using It = Item<FMT_Q4_0>;
+  constexpr int D = kNarrowAhead;
+  static_assert(8 % D == 0 && D <= 8, "the ring divides a block of 8 steps");
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int P = a.N * a.S;
+  const int E = a.E;
+  const int M = a.M;
+  const int nwords = (E + 31) >> 5;
+  const int P4 = (P + 3) & ~3;
+  int* idl = reinterpret_cast<int*>(s_dyn);  // by pair: its expert, -1 for an id outside [0, E); -2 past P
+  u32* bits = reinterpret_cast<u32*>(idl + P4);
+  int* wpre = reinterpret_cast<int*>(bits + nwords);
+  int* off = wpre + nwords;  // by rank: pair count, then (after the scan) first sorted pair
+  int* coff = off + P + 1;   // by rank: first chunk
+  int* ex = coff + P + 1;    // by rank: expert
+  int* slot = ex + P;        // by pair: place among its expert's pairs
+  int* sorted = slot + P;    // pairs by expert
+  int* chunk = sorted + P;   // chunk: rank | (index among its expert's chunks) << 16
+  int* cnts = chunk + P;     // chunks, invalid ids seen, ranks
+
+  for (int w = tid; w < nwords; w += nthr) bits[w] = 0u;
+  for (int r = tid; r <= P; r += nthr) off[r] = 0;
+  for (int q = P + tid; q < P4; q += nthr) idl[q] = -2;
+  if (tid < 3) cnts[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += nthr) {
+    const int e = a.ids[p];
+    const bool valid = e >= 0 && e < E;
+    idl[p] = valid ? e : -1;
+    if (valid)
+      atomicOr(&bits[e >> 5], 1u << (e & 31));
+    else
+      cnts[1] = 1;
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  if (tid < 64) {  // word prefix counts of the bitmap (ranks): lane l takes words [l wpl, (l + 1) wpl)
+    const int wpl = (nwords + 63) >> 6;
+    const int w0 = lane * wpl, w1 = min(nwords, w0 + wpl);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - cnt;
+    for (int w = w0; w < w1; ++w) {
+      wpre[w] = run;
+      run += __popc(bits[w]);
+    }
+    if (lane == 63) cnts[2] = incl;
+  }
+  __syncthreads();
+  auto rank_of = [&](int e) { return wpre[e >> 5] + __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u)); };
+  // each pair's place among its expert's pairs, in pair order (the pairs before it with
+  // its expert): the workgroups share out one list of chunks, so every workgroup must
+  // build the same tables, which an atomic counter would not (it orders the pairs as
+  // the lanes and waves happen to arrive).  The ids are read four at a time, the same
+  // for every lane.
+  for (int p = tid; p < P; p += nthr) {
+    const int e = idl[p];
+    int lower = 0;
+#pragma unroll 8
+    for (int q = 0; q < P4; q += 4) {
+      const int4 k = *reinterpret_cast<const int4*>(idl + q);
+      lower += (q < p && k.x == e ? 1 : 0) + (q + 1 < p && k.y == e ? 1 : 0) + (q + 2 < p && k.z == e ? 1 : 0) +
+               (q + 3 < p && k.w == e ? 1 : 0);
+    }
+    if (e >= 0) {
+      const int r = rank_of(e);
+      slot[p] = lower;
+      ex[r] = e;
+      atomicAdd(&off[r], 1);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // pair and chunk offsets by rank: lane l takes ranks [l rpl, (l + 1) rpl)
+    const int nr = cnts[2];
+    const int rpl = (nr + 63) >> 6;
+    const int q0 = lane * rpl, q1 = min(nr, q0 + rpl);
+    int np = 0, nc = 0;
+    for (int r = q0; r < q1; ++r) {
+      np += off[r];
+      nc += (off[r] + 1) >> 1;
+    }
+    int ip = np, ic = nc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int vp = __shfl_up(ip, o), vc = __shfl_up(ic, o);
+      if (lane >= o) {
+        ip += vp;
+        ic += vc;
+      }
+    }
+    int rp = ip - np, rc = ic - nc;
+    for (int r = q0; r < q1; ++r) {
+      const int c = off[r];
+      off[r] = rp;
+      coff[r] = rc;
+      rp += c;
+      rc += (c + 1) >> 1;
+    }
+    if (lane == 63) {
+      off[nr] = ip;
+      coff[nr] = ic;
+      cnts[0] = ic;
+    }
+    // (the lanes see one another's stores after a wave sync)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int p = lane; p < P; p += 64) {
+      const int e = idl[p];
+      if (e >= 0) sorted[off[rank_of(e)] + slot[p]] = p;
+    }
+    for (int r = lane; r < nr; r += 64) {
+      const int n = (off[r + 1] - off[r] + 1) >> 1;
+      for (int j = 0; j < n; ++j) chunk[coff[r] + j] = r | (j << 16);
+    }
+  }
+  // ids outside [0, E) have no matrix: NaN rows, each workgroup a slice of the rows
+  if (cnts[1]) {
+    const int rpw = (M + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+    const int rlo = static_cast<int>(blockIdx.x) * rpw;
+    const float qnan = __builtin_nanf("");
+    for (int i = tid; i < P * rpw; i += nthr) {
+      const int p = i / rpw, r = rlo + (i - p * rpw);
+      if (r < M && idl[p] < 0) a.y[(u64)p * M + r] = qnan;
+    }
+  }
+  __syncthreads();
+
+  // this wave's steps: blocks of 8, each within one chunk
+  const int spc = (((M + 3) >> 2) + 7) & ~7;
+  const int total = cnts[0] * spc;  // the host keeps P * spc below 2^30
+  const int nwv = static_cast<int>(gridDim.x) * (nthr >> 6);
+  const int gw = static_cast<int>(blockIdx.x) * (nthr >> 6) + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = ((total + nwv - 1) / nwv + 7) & ~7;
+  const int s_begin = gw * T;
+  const int s_end = min(total, s_begin + T);
+  if (s_begin >= s_end) return;  // (no barrier follows)
+
+  const int gi = lane & 15;
+  const int rsub = lane >> 4;  // this lane's row within a step
+  const u32 rb = static_cast<u32>(a.row_bytes);
+  // chunk c's expert base, first pair and pair count
+  auto chunk_base = [&](int c) {
+    const int r = chunk[c] & 0xFFFF;
+    return a.W + (u64)ex[r] * a.expert_bytes;
+  };
+  auto load = [&](const u8* Wb, int rs, typename It::Raw& w) {
+    It::load(Wb, (u32)min(4 * rs + rsub, M - 1) * rb, gi, w);
+  };
+  float xv[2][32], sx[2][2];
+  int yrow[2];
+  int npair = 1;
+  auto load_x = [&](int c) {  // the chunk's pairs' activations
+    const int r = chunk[c] & 0xFFFF, j = chunk[c] >> 16;
+    const int f = off[r] + 2 * j, n = min(2, off[r + 1] - f);
+    npair = n;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t >= n) break;  // (uniform)
+      const int p = sorted[f + t];
+      yrow[t] = p;
+      const size_t xrow = static_cast<size_t>(a.x_per_slot ? p : p / a.S);
+      if constexpr (XH) {
+        typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+        const uint4* px = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(a.x) + xrow * a.K + 32 * gi);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const h8 h = __builtin_bit_cast(h8, px[k]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xv[t][8 * k + q] = static_cast<float>(h[q]);
+        }
+      } else {
+        const float4* px = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + xrow * a.K + 32 * gi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 v = px[k];
+          xv[t][4 * k] = v.x; xv[t][4 * k + 1] = v.y; xv[t][4 * k + 2] = v.z; xv[t][4 * k + 3] = v.w;
+        }
+      }
+      sx[t][0] = half_sum16(xv[t]);
+      sx[t][1] = half_sum16(xv[t] + 16);
+    }
+  };
+
+  typename It::Raw wr[D];
+  float outv[2];
+  // block at step s (chunk c, first row step rs), the next block at (Wn, nrs): step k
+  // computes slot k % D and refills it with the step D later, in this block or
+  // (RELOAD: not in a wave's last block) the next; then the block's stores -- lane
+  // gi keeps step gi % 8's sums, two lanes per output.  TP: the chunk's pairs.
+  auto block = [&](auto reload, auto tpc, const u8* Wb, int rs, const u8* Wn, int nrs) {
+    constexpr int TP = decltype(tpc)::value;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      Unit o[1][1];
+      MixPairs<FMT_Q4_0> pk[1];
+      It::unpack(wr[k % D], o[0]);
+      pk[0].make(wr[k % D], o[0]);
+      if (k + D < 8) {
+        load(Wb, rs + k + D, wr[k % D]);
+      } else {
+        if constexpr (decltype(reload)::value) load(Wn, nrs + k + D - 8, wr[k % D]);
+      }
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+        float v[1];
+        multi_run<FMT_Q4_0, 1>(pk, o, 0, xv[t], sx[t][0], sx[t][1], v);
+        const float sum = sum16(0.0f + v[0]);
+        outv[t] = (gi & 7) == k ? sum : outv[t];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int row = min(4 * (rs + (gi & 7)) + rsub, M - 1);  // rows past M repeat the last one
+#pragma unroll
+    for (int t = 0; t < TP; ++t) a.y[(u64)yrow[t] * M + row] = outv[t];
+  };
+
+  int c = s_begin / spc;
+  int rs = s_begin - c * spc;
+  const u8* Wb = chunk_base(c);
+  load_x(c);  // (issued before the ring: the first step waits for both)
+  int xc = c;
+#pragma unroll
+  for (int k = 0; k < D; ++k) load(Wb, rs + k, wr[k]);
+  for (int s = s_begin; s < s_end; s += 8) {
+    if (c != xc) {
+      load_x(c);
+      xc = c;
+    }
+    // the next block: the same chunk 8 steps on, or the next chunk's first
+    const bool same = rs + 8 < spc;
+    const int nc = same ? c : c + 1;
+    const int nrs = same ? rs + 8 : 0;
+    if (s + 8 < s_end) {
+      const u8* Wn = same ? Wb : chunk_base(nc);
+      if (npair == 2)
+        block(std::true_type{}, std::integral_constant<int, 2>{}, Wb, rs, Wn, nrs);
+      else
+        block(std::true_type{}, std::integral_constant<int, 1>{}, Wb, rs, Wn, nrs);
+      c = nc;
+      rs = nrs;
+      Wb = Wn;
+    } else if (npair == 2) {
+      block(std::false_type{}, std::integral_constant<int, 2>{}, Wb, rs, Wb, rs);
+    } else {
+      block(std::false_type{}, std::integral_constant<int, 1>{}, Wb, rs, Wb, rs);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Host side: instance tables and launch-shape choice.
 
@@ -1612,7 +1907,9 @@ struct Tables {
   GemvGroupKernel pair[2][3];             // k_gemv1_pair<Q4_K, Q6_K>: [fp16 activations][rows per thread]
   int pair_regs[2][3];
   GemvKernel multi_id[kNumFormats][2];
-  GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512
+  GemvKernel narrow_id[2];  // [fp16 activations]: Q4_0 at K = 512, more than 64 pairs
+  GemvKernel slices_id[2];  // [fp16 activations]: Q4_0 at K = 512, up to 64 pairs
+  int narrow_occ[2];        // their resident workgroups per CU
   GemvGroupKernel mma[2][3][2];  // k_gemvm_a4: [token blocks - 1][groups per wave - 2][row tiles - 1]
   GemvGroupKernel gm[kNumFormats][2];  // k_gemvm: [format][token blocks - 1] (null: not on that path)
   template <int F>
@@ -1643,6 +1940,8 @@ struct Tables {
     mma[1][2][1] = k_gemvm_a4<2, 4, 2>;
     narrow_id[0] = k_gemv_id_narrow<false>;
     narrow_id[1] = k_gemv_id_narrow<true>;
+    slices_id[0] = k_gemv_id_slices<false>;
+    slices_id[1] = k_gemv_id_slices<true>;
     fill_format<FMT_Q4_0>();
     fill_format<FMT_Q8_0>();
     fill_format<FMT_Q4_K>();
@@ -1670,6 +1969,14 @@ struct Tables {
         for (int f = 0; f < kNumFormats; ++f) one_regs[f][h][r] = regs(one[f][h][r]);
         if (r < 3) pair_regs[h][r] = regs(pair[h][r]);
       }
+    // a CU holds, per SIMD, 512 / VGPRs waves (at most 8) of each 256-thread
+    // workgroup's four: that many workgroups
+    for (int h = 0; h < 2; ++h) {
+      hipFuncAttributes at{};
+      const bool ok = hipFuncGetAttributes(&at, reinterpret_cast<const void*>(narrow_id[h])) == hipSuccess;
+      const int v = ok && at.numRegs > 0 ? (at.numRegs + 7) / 8 * 8 : 512;
+      narrow_occ[h] = std::max(1, std::min(8, 512 / v));
+    }
   }
 };
 
@@ -2071,16 +2378,8 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
   // the grid is ranks x row slices: about two workgroups per CU over all the
   // active experts
   const int M = static_cast<int>(m.M);
+  const int64_t spc = ((m.M + 3) / 4 + 7) / 8 * 8;  // the narrow kernel's steps per pair chunk
   if (m.fmt == FMT_Q4_0 && nU == 16) {
-    // narrow rows: about four 256-thread workgroups per CU over the ranks, each
-    // streaming a slice of its expert's rows (a multiple of the 16 rows of a
-    // step), at least 128 rows so that the routing stays a small part of it.
-    // Measured on 128 experts of 4096 rows at 2, 8 and 24 tokens (slices of
-    // 128-1024 rows, rings of 4-16 items).
-    const int slices = (4 * cus + ranks - 1) / ranks;
-    int RW = (M + slices - 1) / slices;
-    RW = (RW + 15) / 16 * 16;
-    if (RW < 128) RW = 128;
     GemvArgs a{};
     a.W = m.blocks;
     a.row_bytes = m.row_bytes;
@@ -2088,7 +2387,6 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
     a.M = M;
     a.nU = nU;
     a.K = static_cast<int>(m.K);
-    a.rows_per_wg = RW;
     a.x = x;
     a.x_f16 = x_f16;
     a.y = y;
@@ -2097,7 +2395,25 @@ hipError_t launch_gemv_id(const MatDesc& m, const void* x, int x_f16, int N, int
     a.S = S;
     a.x_per_slot = x_per_slot;
     a.E = static_cast<int>(m.n_experts);
-    hipLaunchKernelGGL(tables().narrow_id[x_f16 ? 1 : 0], dim3((M + RW - 1) / RW, ranks), dim3(256), 0, st, a);
+    const int h = x_f16 ? 1 : 0;
+    if (P <= 64 || P > kNarrowMaxPairs || P * spc >= (int64_t(1) << 30)) {
+      // about four 256-thread workgroups per CU over the ranks, each streaming a
+      // slice of its expert's rows (a multiple of the 16 rows of a step), at least
+      // 128 rows so that the routing stays a small part of it.  Measured on 128
+      // experts of 4096 rows at 2, 8 and 24 tokens (slices of 128-1024 rows, rings
+      // of 4-16 items).
+      const int slices = (4 * cus + ranks - 1) / ranks;
+      int RW = (M + slices - 1) / slices;
+      RW = (RW + 15) / 16 * 16;
+      if (RW < 128) RW = 128;
+      a.rows_per_wg = RW;
+      hipLaunchKernelGGL(tables().slices_id[h], dim3((M + RW - 1) / RW, ranks), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+    // a persistent grid (every workgroup resident at once), the work split evenly
+    // over its waves
+    const size_t lds = narrow_lds_ints(a.E, static_cast<int>(P)) * sizeof(int);
+    hipLaunchKernelGGL(tables().narrow_id[h], dim3(tables().narrow_occ[h] * cus), dim3(256), lds, st, a);
     return hipGetLastError();
   }
   {

@@ -168,3 +168,55 @@ def test_gemm_id_tall_experts_many_pairs_and_bad_ids():
     ref = oracle.matmul_id_ref(x, ids_ok, ws)
     sc = oracle.tolerance_scale_id(x, ids_ok, ws)
     assert_within(y[~bad], ref[~bad], sc[~bad], TOL, "slices and passes")
+
+
+@pytest.mark.parametrize("N,S,xdtype", [(1, 1, np.float32), (24, 8, np.float32), (9, 8, np.float16), (32, 24, np.float32)])
+def test_gemm_id_narrow_rows_many_chunks(N, S, xdtype):
+    """Q4_0 at K = 512 (the route-once kernel from 65 to 512 pairs, the row-slice
+    kernel at fewer or more): a row count that is no multiple of a step, experts with many pairs (several
+    chunks of two), an expert's chunks split among waves; within the bound, and some
+    outputs bit for bit the one-token dense call on their expert."""
+    fmt, E, M, K = "q4_0", 16, 4100, 512
+    blob, ws = _stack(fmt, E, M, K, 71)
+    g = np.random.default_rng([71, N, S])
+    ids = g.integers(0, E, size=(N, S)).astype(np.int32)
+    x = g.standard_normal((N, S, K)).astype(xdtype)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL, "narrow rows")
+    rb = oracle.row_bytes(fmt, K)
+    for t, s in {(0, 0), (N - 1, S - 1), (N // 2, S // 2)}:
+        e = int(ids[t, s])
+        dense = q.QMatrix(to_dev(blob[e * M * rb:(e + 1) * M * rb]), fmt, M, K)
+        yd = to_host(dense.gemv(to_dev(x[t, s][None, :].copy())))
+        assert count_differences(y[t, s][None, :], yd) == 0, (t, s, e)
+
+
+def test_gemm_id_narrow_rows_all_ids_invalid():
+    """Every id outside [0, E): every output row NaN, no expert streamed."""
+    fmt, E, M, K, N, S = "q4_0", 4, 70, 512, 3, 2
+    blob, _ = _stack(fmt, E, M, K, 72)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    ids = np.array([[4, -1], [7, 4], [-5, 100]], np.int32)
+    x = np.random.default_rng(72).standard_normal((N, S, K)).astype(np.float32)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert np.all(np.isnan(y))
+
+
+def test_gemm_id_narrow_rows_bad_ids_many_pairs():
+    """Q4_0 at K = 512 past 64 pairs (the route-once kernel) with ids outside [0, E)
+    among them: NaN rows for those, the others within the bound."""
+    fmt, E, M, K, N, S = "q4_0", 12, 1000, 512, 16, 8
+    blob, ws = _stack(fmt, E, M, K, 73)
+    g = np.random.default_rng(73)
+    ids = g.integers(0, E, size=(N, S)).astype(np.int32)
+    ids[0, 0], ids[7, 3], ids[15, 7] = -1, E, 1 << 20
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(np.isnan(y[bad]))
+    ids_ok = np.where(bad, 0, ids)
+    ref = oracle.matmul_id_ref(x, ids_ok, ws)
+    sc = oracle.tolerance_scale_id(x, ids_ok, ws)
+    assert_within(y[~bad], ref[~bad], sc[~bad], TOL, "bad ids, many pairs")
