@@ -267,8 +267,10 @@ qmm_status qmm_gemm_noalloc(const qmm_matrix *h, const void *x, qmm_dtype xt, in
  *   ids         DEVICE int32 [N, S], 4-byte aligned.  Duplicate ids are computed
  *               independently; an id outside [0, E) makes its output row all NaN.
  *   y           DEVICE fp32 [N, S, M].
- * The (token, slot) pairs are grouped by expert on the device, so each active
- * expert's blocks are streamed once per call; no host synchronisation.
+ * The (token, slot) pairs are grouped by expert on the device, and each active
+ * expert's rows are swept once per group of its pairs (two at a time on Q4_0 rows
+ * of K = 512, more on the other paths); no host synchronisation, no device memory
+ * beyond the arguments.
  */
 qmm_status qmm_gemm_id(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
                        int64_t S, int x_per_slot, const int32_t *ids, float *y,
