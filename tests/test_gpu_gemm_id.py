@@ -220,3 +220,20 @@ def test_gemm_id_narrow_rows_bad_ids_many_pairs():
     ref = oracle.matmul_id_ref(x, ids_ok, ws)
     sc = oracle.tolerance_scale_id(x, ids_ok, ws)
     assert_within(y[~bad], ref[~bad], sc[~bad], TOL, "bad ids, many pairs")
+
+
+def test_gemm_id_narrow_rows_many_experts():
+    """Q4_0 at K = 512 on 8192 experts of 5 rows with 512 pairs, the route-once kernel's
+    largest call: a presence bitmap of 256 words (several per scanning lane), several
+    ranks per lane in the offset scan, and one expert with several pairs."""
+    fmt, E, M, K, N, S = "q4_0", 8192, 5, 512, 32, 16
+    blob = make_matrix(fmt, E * M, K, [74])
+    w_all = oracle.dequantize(fmt, blob, E * M, K)
+    ws = [w_all[e * M:(e + 1) * M] for e in range(E)]
+    g = np.random.default_rng(74)
+    ids = g.integers(0, E, size=(N, S)).astype(np.int32)
+    ids[3, :4] = 17
+    x = g.standard_normal((N, S, K)).astype(np.float32)
+    qm = q.QMatrix(to_dev(blob), fmt, M, K, E)
+    y = to_host(qm.gemm_id(to_dev(x), to_dev(ids)))
+    assert_within(y, oracle.matmul_id_ref(x, ids, ws), oracle.tolerance_scale_id(x, ids, ws), TOL, "8192 experts")
