@@ -100,6 +100,8 @@ def parse():
     p.add_argument("--formats-only", action="store_true", help="only run the per-format sweep")
     p.add_argument("--small-decode-only", default=None, metavar="N[,N...]",
                    help="only time the 4-bit-group layer at these token counts (for profiling)")
+    p.add_argument("--decode-few-only", default=None, metavar="N[,N...]",
+                   help="only time the decode layer at these fp16 token counts through qmm_gemv")
     p.add_argument("--moe-only", default=None, metavar="N[,N...]",
                    help="only time the expert-indexed paths at these token counts: the matvec up to 32 "
                         "tokens, the matrix-core path above (for profiling)")
@@ -491,6 +493,61 @@ def extra_small_decode(torch, q, W, args):
                         "calls (one launch each at one token)", "layer_weight_bytes": wbytes,
             "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
             "valu_peaks_tflops": {"fma": VALU_F32_FMA_TFLOPS, "packed": VALU_F32_PACKED_TFLOPS},
+            "results": res}
+
+
+def extra_decode_few(torch, q, W, mats, args):
+    """The decode layer (the headline's seven projections) at a few fp16 tokens through
+    qmm_gemv: the same launches as the headline at one token; past one token the q+k
+    pair and gate+up share grouped calls (grouped calls mix Q4_K with Q6_K only at one
+    token), v, attn_output and ffn_down take their own.  Both formats take the matrix
+    cores from 5 tokens, the vector kernels below.  Beside it, the same
+    layer through the matrix-matrix path (qmm_gemm_ws, weights staged in fp16)."""
+    rot = Rotation(torch, [m["blob"] for m in mats])
+    hs = [[q.QMatrix(rot.slice(c, j), m["fmt"], m["M"], m["K"]) for j, m in enumerate(mats)]
+          for c in range(rot.copies)]
+    wbytes = sum(int(m["blob"].size) for m in mats)
+    groups_n = [[0, 1], [2], [3], [4, 5], [6]]
+    res = []
+    tokens = [int(t) for t in args.decode_few_only.split(",")] if args.decode_few_only else [1, 2, 4, 8, 16]
+    for n in tokens:
+        xs = [torch.from_numpy(W.prefill_x(j, n)).to("cuda") for j in range(len(mats))]
+        ys = [torch.empty((n, m["M"]), device="cuda") for m in mats]
+        layers = rot.copies
+        groups = DECODE_GROUPS if n == 1 else groups_n
+
+        def fn():
+            for c in range(layers):
+                for grp in groups:
+                    if len(grp) == 1:
+                        q.qmm_gemv(hs[c][grp[0]].handle, xs[grp[0]], n, ys[grp[0]])
+                    else:
+                        q.qmm_gemv_group([hs[c][j].handle for j in grp], [xs[j] for j in grp], n,
+                                         [ys[j] for j in grp])
+        g = capture(torch, fn)
+        us = time_graph(torch, g, args.rounds) * 1e3 / layers
+        del g
+        gbs = wbytes / (us * 1e-6) / 1e9
+        row = {"n": n, "us_per_layer": us, "weight_gbs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+               "launches": len(groups),
+               "path": "matrix cores" if n >= 5 else "vector"}
+        if n >= 2:
+            wss = []
+            for j in range(len(mats)):
+                nb = q.qmm_gemm_workspace_bytes(hs[0][j].handle, n)
+                wss.append(torch.empty((nb + 15) // 16 * 4, device="cuda") if nb else None)
+
+            def fm():
+                for c in range(layers):
+                    for j in range(len(mats)):
+                        q.qmm_gemm_ws(hs[c][j].handle, xs[j], n, ys[j], 0, wss[j])
+            g = capture(torch, fm)
+            row["gemm_us_per_layer"] = time_graph(torch, g, args.rounds) * 1e3 / layers
+            del g, wss
+        res.append(row)
+    return {"workload": "decode layer (Q4_K / Q6_K, the headline's seven projections), fp16 tokens "
+                        "(seeds of the prefill rows), weights rotated over >1 GiB per sample",
+            "layer_weight_bytes": wbytes, "copies": rot.copies, "rotation_bytes": rot.copies * rot.copy_bytes,
             "results": res}
 
 
@@ -922,6 +979,10 @@ def main():
     if args.small_decode_only:
         print(json.dumps({"small_decode_a4g64": extra_small_decode(torch, q, W, args)}), flush=True)
         return
+    if args.decode_few_only:
+        mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
+        print(json.dumps({"decode_layer_few_tokens": extra_decode_few(torch, q, W, mats, args)}), flush=True)
+        return
     if args.prefill_only:
         mats = [W.decode_weights(j) for j in range(len(W.DECODE_SHAPES))]
         print(json.dumps({"prefill_gemm": extra_prefill(torch, q, W, mats, args)}), flush=True)
@@ -986,6 +1047,7 @@ def main():
     if not args.no_extras:
         for name, fn in (("single_matvec", lambda: extra_single_matvec(torch, q, W, args)),
                          ("small_decode_a4g64", lambda: extra_small_decode(torch, q, W, args)),
+                         ("decode_layer_few_tokens", lambda: extra_decode_few(torch, q, W, mats, args)),
                          ("prefill_gemm", lambda: extra_prefill(torch, q, W, mats, args)),
                          ("prefill_batch_2x65", lambda: extra_prefill_batch(torch, q, W, args)),
                          ("formats", lambda: extra_formats(torch, q, W, args)),

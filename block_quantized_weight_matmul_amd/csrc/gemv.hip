@@ -2167,19 +2167,17 @@ struct MmaShape {
 
 // k_gemvm's shape: KS = ceil(units / UPW) waves (at most 8), UPW a multiple of 8 (two
 // steps of 4 units) -- a function of K alone.
-// Fewest tokens at which k_gemvm takes a format's calls (one token always takes the
-// one-token kernel): from there it was the faster of the two on a 4096 x 4096 matrix
-// (fp16 tokens, weights rotated over 32 copies; us at 2 / 4 / 8 / 16 tokens, vector
-// kernel -> matrix cores: Q4_0 9.7/10.2/16.7/27.3 -> 9.2/9.3/9.2/10.0, Q5_K
-// 9.3/11.0/17.4/28.1 -> 10.1/10.1/10.5/11.4, Q6_K 9.6/11.9/19.3/31.2 ->
-// 12.1/12.2/13.1/15.5).  The decode of a step's units is spread over the wave, but the
-// exchange through LDS is a fixed cost that the dearer decoders pay at 2 and 3 tokens.
-constexpr int kUnitMinTokens[kNumFormats] = {
-    /* Q4_0 */ 2, /* Q8_0 */ 4, /* Q4_K */ 2, /* Q6_K */ 5, /* A4G64 */ 33, /* Q4_1 */ 2,
-    /* Q5_0 */ 4, /* Q5_1 */ 2, /* Q2_K */ 4, /* Q3_K */ 5, /* Q5_K */ 4};
+// k_gemvm takes fp16 calls from kMmaMinTokens tokens, as k_gemvm_a4 does.  On a 4096 x
+// 4096 matrix it was the faster of the two from 2..5 tokens by format (fp16 tokens,
+// weights rotated over 32 copies; us at 2 / 4 / 8 / 16 tokens, vector kernel -> matrix
+// cores: Q4_0 9.7/10.2/16.7/27.3 -> 9.2/9.3/9.2/10.0, Q6_K 9.6/11.9/19.3/31.2 ->
+// 12.1/12.2/13.1/15.5), but on the decode layer's larger matrices the vector kernel
+// streams near its one-token rate at 2..4 tokens while this kernel stays near 1.2 TB/s
+// (layer at 2 / 3 / 4 tokens: 51.6 / 65.9 / 72.9 us from 5 tokens on, 64.3 / 73.6 /
+// 76.2 with Q4_K from 2); at 6 tokens the layer takes 75 us with it, 97 without.
 
 bool mma_unit_shape(int fmt, int64_t K, int N, int x_f16, MmaShape& o) {
-  if (!x_f16 || N < 2 || N < kUnitMinTokens[fmt] || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
+  if (!x_f16 || N < kMmaMinTokens || N > 32 || K % 32 != 0 || K < 32 || !tables().gm[fmt][0]) return false;
   // the activations are read through a buffer of N * K fp16 values with 32-bit offsets
   if (static_cast<int64_t>(N) * K * 2 >= (int64_t(1) << 31)) return false;
   const int64_t nU = K / 32;

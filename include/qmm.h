@@ -157,11 +157,11 @@ qmm_status qmm_destroy(qmm_matrix *h);
  *   y   DEVICE, [N, M] contiguous fp32, 4-byte aligned; every element is written.
  * Lanes of each 64-wide wavefront are spread over (row, 32-weight chunk) pairs so
  * none idles at narrow K, and the token count picks a kernel instance that gives
- * no register to absent tokens.  fp16 tokens from 2..5 on (by format; 4-bit affine
- * groups from 5) take the matrix cores with exact products: there a token's outputs
- * depend on its activations and K only (the same bits at any token count from that
- * threshold), and differ in summation order, not in the weights, from the vector
- * kernels, whose N-token outputs are the bits of N one-token calls.
+ * no register to absent tokens.  fp16 calls of 5 to 32 tokens take the matrix cores
+ * with exact products: there a token's outputs depend on its activations and K only
+ * (the same bits at any token count from 5), and differ in summation order, not in
+ * the weights, from the vector kernels, whose N-token outputs are the bits of N
+ * one-token calls.
  */
 qmm_status qmm_gemv(const qmm_matrix *h, const void *x, qmm_dtype xt, int64_t N,
                     float *y, qmm_stream_t stream);

@@ -33,8 +33,7 @@ def _run(fmt, M, K, N, xdtype, seed):
 
 # fp16 tokens take the matrix cores from a format's token count on (the library's dispatch)
 MC_FORMATS = list(FORMATS)
-MC_MIN_TOKENS = {"q4_0": 2, "q8_0": 4, "q4_k": 2, "q6_k": 5, "a4g64": 5, "q4_1": 2, "q5_0": 4, "q5_1": 2,
-                 "q2_k": 4, "q3_k": 5, "q5_k": 4}
+MC_MIN_TOKENS = {f: 5 for f in FORMATS}
 
 
 def _ks(fmt):
@@ -230,7 +229,7 @@ def test_gemv_eight_rows_per_thread(fmt, M, K):
                       f"gemv {fmt} M={M} K={K} {np.dtype(xdt).name}")
 
 
-# fp16 tokens from a format's few (2..5) to 32 take the matrix-core kernels: rows of one
+# fp16 tokens from 5 to 32 take the matrix-core kernels (2 and 4: the vector path): rows of one
 # block up to long K (one to several units or groups per wave, a last wave with fewer, one
 # wave), for 4-bit groups a K past the kernel's range (the vector path), rows that are not
 # a multiple of 16, and one or two 16-token blocks
